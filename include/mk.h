@@ -1,0 +1,155 @@
+/*
+ * mk.h -- C ABI of libmk.so: fused MoE dispatch + expert GEMM for MI355X (gfx950).
+ *
+ * The operation is the "MoE Dispatch+GEMM" fused kernel named in "mKernel UCCL
+ * fuses NVLink/RDMA/compute into one persistent CUDA kernel" (zubnet.ai),
+ * paragraph 2: tokens are routed to experts, their rows are dispatched into
+ * expert-contiguous buffers and every expert runs its dense GEMM, inside one
+ * persistent kernel whose workgroups take roles ("UC Berkeley presenta mKernel
+ * ..." (edge.aivizor.me), paragraph 2) and overlap at tile granularity
+ * (zubnet.ai, paragraph 2).  The pages give no formulas; the definitions below
+ * are the readings this library implements.
+ *
+ * Conventions for every entry point
+ *   - Array pointers are DEVICE pointers unless marked HOST.
+ *   - bf16 arrays hold raw bf16 bit patterns (2 bytes each), row-major.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *   - The caller allocates and owns every buffer and keeps it alive until the
+ *     stream has passed the call.  The library allocates no device memory on
+ *     the call path and keeps no mutable global state.
+ *   - Invalid arguments are reported synchronously by the return value and
+ *     nothing is launched.  No exception crosses the ABI; nothing is printed.
+ *   - Every device pointer must be 16-byte aligned.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mk_status;
+enum {
+    MK_OK = 0,
+    MK_EINVAL = 1,        /* bad shape, null pointer, misalignment, k out of range */
+    MK_EUNSUPPORTED = 2,  /* legal shape this build does not handle (see each call) */
+    MK_EWORKSPACE = 3,    /* workspace missing or smaller than required */
+    MK_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+    MK_ETIMEOUT = 5       /* a device-side wait exceeded its bound (mk_poll_error) */
+};
+
+/* Problem shape.  Local experts are [e_begin, e_begin + E_local) of the E
+ * global experts the router scores.  Requires T >= 0, d > 0, d % 64 == 0,
+ * 1 <= k <= E <= 1024, 0 <= e_begin, e_begin + E_local <= E, N > 0, N % 8 == 0. */
+typedef struct {
+    int32_t T, d, E, k, e_begin, E_local, N;
+} mk_shape;
+
+/* Where the token rows come from.  An ordinary call has S = 1, x[0] = the
+ * [T, d] bf16 token matrix and chunk_rows = 0.  For one GPU's share of an
+ * expert-parallel layer the rows arrive as S source shards (one per peer),
+ * token t = s * rows_per_src + r, each shard in its own buffer; a chunk of
+ * chunk_rows rows of a shard may be read only once its ready flag holds
+ * `epoch` (acquire), which models "a tile that has arrived feeds the GEMM
+ * while the next is still in flight" (zubnet.ai, paragraph 2). */
+typedef struct {
+    int32_t S;                   /* >= 1 */
+    int32_t rows_per_src;        /* T == S * rows_per_src */
+    const void *const *x;        /* HOST array of S device pointers, each [rows_per_src, d] bf16 */
+    int32_t chunk_rows;          /* rows per ready flag; 0 = all rows already resident */
+    uint32_t *chunk_ready;       /* [S * ceil(rows_per_src / chunk_rows)], chunk c = s * cps + j */
+    uint32_t epoch;              /* chunk c is ready iff chunk_ready[c] == epoch */
+    /* Arrival simulator (one GPU standing in for its peers).  If sim_delay_us
+     * is non-NULL, one workgroup of the fused kernel writes chunk_ready[c] =
+     * epoch (release) sim_delay_us[c] microseconds after the kernel starts.
+     * If sim_payload is also non-NULL (HOST array of S device pointers, same
+     * shape as x), that workgroup first copies the chunk from sim_payload[s]
+     * into x[s] (which must then be writable), so a read before the release
+     * sees whatever x held before the call. */
+    const uint32_t *sim_delay_us;
+    const void *const *sim_payload;
+} mk_sources;
+
+/* Role split and tile sizes.  All zeros = the per-shape table (mk_select_tuning).
+ * n_mover_wg workgroups start in the dispatch (mover) role and join the GEMM
+ * role when the dispatch work is done; n_compute_wg workgroups start in the
+ * GEMM role.  bm/bn/bk: rows, columns and depth of one GEMM tile. */
+typedef struct {
+    int32_t n_mover_wg, n_compute_wg, bm, bn, bk;
+} mk_tuning;
+
+/* Router: logits l[t,e] = sum_i x[t,i] * w_router[i,e] (+ bias[e]), fp32, in a
+ * fixed order: K split into 8 contiguous segments of d/8, a sequential fused
+ * multiply-add chain in ascending i inside each segment, the 8 partial sums
+ * added left to right, then the bias.  Top-k keeps the k experts ranked by
+ * (logit descending, expert id ascending; -0 equals +0); topk_ids[t, j] is the
+ * j-th best.  topk_w[t, j] is the softmax over all E logits at that expert
+ * (not renormalised over the k).  Token routing is named in zubnet.ai,
+ * paragraph 2, and lefilia.fr, paragraph 3; the order, tie rule and gate are
+ * this library's readings.
+ *   x         [T, d] bf16          w_router [d, E] fp32     bias [E] fp32 or NULL
+ *   topk_ids  [T, k] int32 (out)   topk_w   [T, k] fp32 (out, may be NULL)
+ *   workspace mk_route_topk_workspace_bytes(T, E) bytes, any contents.
+ * T == 0 is a no-op returning MK_OK. */
+size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E);
+mk_status mk_route_topk(const void *x, const float *w_router, const float *bias,
+                        int32_t T, int32_t d, int32_t E, int32_t k,
+                        int32_t *topk_ids, float *topk_w,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace mk_dispatch_gemm needs for this shape (0 on bad input). */
+size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src);
+
+/* Fused dispatch + expert GEMM, one persistent launch.
+ * Steps (routing per mk_route_topk unless topk_ids_in is given):
+ *   count[e']   = #{(t, j) : topk_ids[t, j] == e_begin + e'}        (histogram)
+ *   offsets     = exclusive prefix sum of count; R = offsets[E_local]
+ *   slot_of[t,j]= offsets[e'] + #{t' < t : e' chosen by t'}  or -1 if not local
+ *   row_token[slot_of[t,j]] = t
+ *   x_perm[r]   = x[row_token[r]]   (tile-chunked scatter into expert-contiguous rows)
+ *   y_perm[r,n] = bf16_rne(sum_i x_perm[r,i] * w_experts[e', n, i]), fp32 accumulation
+ * Arguments:
+ *   w_router, bias     router inputs (used iff topk_ids_in == NULL)
+ *   topk_ids_in        NULL = route inside this call; else [T, k] int32 ids routed
+ *                      by the sources (validated on device: out-of-range ids -> MK_EINVAL
+ *                      via mk_poll_error)
+ *   w_experts          [E_local, N, d] bf16, K contiguous (y = x . W^T)
+ *   y_perm             [T * min(k, E_local), N] bf16; rows >= R are not written
+ *   slot_of            [T, k] int32
+ *   expert_offsets     [E_local + 1] int32
+ *   topk_ids_out       NULL or [T, k] int32     topk_w_out NULL or [T, k] fp32
+ *   row_token          NULL or [T * min(k, E_local)] int32 (first R written)
+ *   workspace          mk_dispatch_gemm_workspace_bytes bytes, ZERO-FILLED ONCE before
+ *                      its first use; it carries state between calls (barrier and
+ *                      flag epochs), so two calls in flight must not share one.
+ *   tune               NULL or all zeros = per-shape table
+ * Device-side failures (a wait that timed out, bad topk_ids_in) are reported by
+ * mk_poll_error after the stream is synchronised; outputs are then undefined. */
+mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src,
+                           const float *w_router, const float *bias,
+                           const int32_t *topk_ids_in,
+                           const void *w_experts,
+                           void *y_perm, int32_t *slot_of, int32_t *expert_offsets,
+                           int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
+                           void *workspace, size_t workspace_bytes,
+                           const mk_tuning *tune, void *stream);
+
+/* The tuning the per-shape table picks (what a NULL/zero `tune` means). */
+mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out);
+
+/* Synchronous: reads the device error word of a dispatch workspace (the caller
+ * must have synchronised the stream).  Returns MK_OK, MK_ETIMEOUT or MK_EINVAL;
+ * *detail (if non-NULL) receives which wait or id failed.  Clears the word. */
+mk_status mk_poll_error(void *workspace, int32_t *detail);
+
+/* Static string for a status code. */
+const char *mk_status_str(mk_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

@@ -1,0 +1,300 @@
+// api.cpp -- the C ABI declared in include/mk.h: argument validation,
+// workspace layout, per-shape tuning and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mk.h"
+#include "gemm_dev.h"
+#include "layout_dev.h"
+#include "mk_args.h"
+#include "mk_launch.h"
+#include "route_dev.h"
+
+namespace {
+
+using namespace mk;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Wall-clock ticks a device-side wait may spin (MK_TIMEOUT_US, default 2 s).
+uint64_t spin_limit_ticks()
+{
+    static uint64_t ticks = 0;
+    if (ticks == 0) {
+        long us = 2000000;
+        if (const char *e = std::getenv("MK_TIMEOUT_US")) {
+            const long v = std::strtol(e, nullptr, 10);
+            if (v > 0) us = v;
+        }
+        int khz = 100000;
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            int r = 0;
+            if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) == hipSuccess && r > 0) khz = r;
+        }
+        ticks = (uint64_t)us * (uint64_t)khz / 1000u;
+    }
+    return ticks;
+}
+
+mk_status check_shape(const mk_shape *s)
+{
+    if (!s) return MK_EINVAL;
+    if (s->T < 0 || s->d <= 0 || s->E < 1 || s->k < 1 || s->k > s->E || s->e_begin < 0 || s->E_local < 1 ||
+        s->e_begin + s->E_local > s->E || s->N <= 0)
+        return MK_EINVAL;
+    if (s->d % 8 != 0 || s->N % 8 != 0) return MK_EINVAL;
+    if (s->d % 128 != 0 || s->E > 1024 || s->k > kMaxK || s->E_local > 1024) return MK_EUNSUPPORTED;
+    return MK_OK;
+}
+
+mk_status check_sources(const mk_shape *s, const mk_sources *src)
+{
+    if (!src || src->S < 1 || src->S > kMaxSources || src->rows_per_src < 0 || !src->x) return MK_EINVAL;
+    if ((long)src->S * src->rows_per_src != s->T) return MK_EINVAL;
+    for (int i = 0; i < src->S; ++i)
+        if (s->T > 0 && (!src->x[i] || !aligned16(src->x[i]))) return MK_EINVAL;
+    if (src->chunk_rows < 0) return MK_EINVAL;
+    if (src->chunk_rows > 0) return MK_EUNSUPPORTED;   // arrival flags need the fused kernel
+    return MK_OK;
+}
+
+SrcRows make_src_rows(const mk_sources *src)
+{
+    SrcRows r{};
+    for (int i = 0; i < src->S; ++i) r.p[i] = (const uint16_t *)src->x[i];
+    r.S = src->S;
+    r.rows_per_src = src->rows_per_src > 0 ? src->rows_per_src : 1;
+    return r;
+}
+
+mk_tuning table_tuning(const mk_shape *s)
+{
+    mk_tuning t{};
+    t.bm = 256;
+    t.bn = 256;
+    t.bk = 64;
+    t.n_mover_wg = 0;
+    t.n_compute_wg = 0;   // 0: every co-resident workgroup
+    (void)s;
+    return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mk_status_str(mk_status st)
+{
+    switch (st) {
+    case MK_OK: return "ok";
+    case MK_EINVAL: return "invalid argument";
+    case MK_EUNSUPPORTED: return "unsupported shape or option";
+    case MK_EWORKSPACE: return "workspace too small";
+    case MK_EHIP: return "HIP runtime error";
+    case MK_ETIMEOUT: return "device wait timed out";
+    default: return "unknown status";
+    }
+}
+
+size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E)
+{
+    if (T < 0 || E < 1) return 0;
+    return align256((size_t)T * E * 4) + 256;
+}
+
+mk_status mk_route_topk(const void *x, const float *w_router, const float *bias, int32_t T, int32_t d, int32_t E,
+                        int32_t k, int32_t *topk_ids, float *topk_w, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    if (T < 0 || d <= 0 || E < 1 || k < 1 || k > E) return MK_EINVAL;
+    if (d % 8 != 0) return MK_EINVAL;
+    if (d % 128 != 0 || E > 1024 || k > kMaxK) return MK_EUNSUPPORTED;
+    if (T == 0) return MK_OK;
+    if (!x || !w_router || !topk_ids || !workspace) return MK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(workspace) ||
+        (bias && !aligned16(bias)) || (topk_w && !aligned16(topk_w)))
+        return MK_EINVAL;
+    if (workspace_bytes < mk_route_topk_workspace_bytes(T, E)) return MK_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    RouterArgs ra{};
+    ra.src.p[0] = (const uint16_t *)x;
+    ra.src.S = 1;
+    ra.src.rows_per_src = T;
+    ra.wr = w_router;
+    ra.bias = bias;
+    ra.logits = (float *)workspace;
+    ra.T = T;
+    ra.d = d;
+    ra.E = E;
+    if (launch_router_logits(ra, st) != hipSuccess) return MK_EHIP;
+    TopkArgs ta{};
+    ta.logits = (const float *)workspace;
+    ta.ids = topk_ids;
+    ta.ids_user = nullptr;
+    ta.w_user = topk_w;
+    ta.T = T;
+    ta.E = E;
+    ta.k = k;
+    CountArgs ca{};
+    if (launch_topk(ta, ca, false, st) != hipSuccess) return MK_EHIP;
+    return MK_OK;
+}
+
+size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src)
+{
+    (void)src;
+    if (check_shape(s) != MK_OK) return 0;
+    return ws_layout(s->T, s->d, s->E, s->k, s->E_local).total;
+}
+
+mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out)
+{
+    (void)src;
+    const mk_status st = check_shape(s);
+    if (st != MK_OK) return st;
+    if (!out) return MK_EINVAL;
+    *out = table_tuning(s);
+    return MK_OK;
+}
+
+mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
+                           const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
+                           int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
+                           void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream)
+{
+    mk_status st = check_shape(s);
+    if (st != MK_OK) return st;
+    st = check_sources(s, src);
+    if (st != MK_OK) return st;
+    if (!w_experts || !expert_offsets || !workspace) return MK_EINVAL;
+    if (s->T > 0 && (!y_perm || !slot_of)) return MK_EINVAL;   // T == 0: empty outputs may be null
+    if (!topk_ids_in && !w_router) return MK_EINVAL;
+    const void *ptrs[] = {w_router, bias, topk_ids_in, w_experts, y_perm, slot_of, expert_offsets,
+                          topk_ids_out, topk_w_out, row_token, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return MK_EINVAL;
+    const WsLayout L = ws_layout(s->T, s->d, s->E, s->k, s->E_local);
+    if (workspace_bytes < L.total) return MK_EWORKSPACE;
+
+    mk_tuning tu = table_tuning(s);
+    if (tune && (tune->bm || tune->bn || tune->bk || tune->n_mover_wg || tune->n_compute_wg)) {
+        if (tune->bm != 256 || tune->bn != 256 || (tune->bk != 0 && tune->bk != 64)) return MK_EUNSUPPORTED;
+        tu.n_compute_wg = tune->n_compute_wg;
+    }
+
+    hipStream_t hs = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    WsHeader *hdr = (WsHeader *)(ws + L.hdr);
+    float *logits = (float *)(ws + L.logits);
+    int32_t *ids = (int32_t *)(ws + L.ids);
+    int32_t *lrank = (int32_t *)(ws + L.lrank);
+    int32_t *blkcnt = (int32_t *)(ws + L.blkcnt);
+    int32_t *blkbase = (int32_t *)(ws + L.blkbase);
+    int32_t *tile_off = (int32_t *)(ws + L.tile_off);
+    int32_t *row_token_ws = (int32_t *)(ws + L.row_token);
+    uint16_t *x_perm = (uint16_t *)(ws + L.x_perm);
+    const SrcRows rows = make_src_rows(src);
+
+    CountArgs ca{};
+    ca.ids = ids;
+    ca.lrank = lrank;
+    ca.blkcnt = blkcnt;
+    ca.err = &hdr->err;
+    ca.T = s->T;
+    ca.E = s->E;
+    ca.k = s->k;
+    ca.e_begin = s->e_begin;
+    ca.E_local = s->E_local;
+
+    if (s->T > 0) {
+        if (!topk_ids_in) {
+            RouterArgs ra{};
+            ra.src = rows;
+            ra.wr = w_router;
+            ra.bias = bias;
+            ra.logits = logits;
+            ra.T = s->T;
+            ra.d = s->d;
+            ra.E = s->E;
+            if (launch_router_logits(ra, hs) != hipSuccess) return MK_EHIP;
+            TopkArgs ta{};
+            ta.logits = logits;
+            ta.ids = ids;
+            ta.ids_user = topk_ids_out;
+            ta.w_user = topk_w_out;
+            ta.T = s->T;
+            ta.E = s->E;
+            ta.k = s->k;
+            if (launch_topk(ta, ca, true, hs) != hipSuccess) return MK_EHIP;
+        } else {
+            if (launch_count_given(topk_ids_in, ids, topk_ids_out, ca, hs) != hipSuccess) return MK_EHIP;
+        }
+    }
+
+    ScanArgs sa{};
+    sa.blkcnt = blkcnt;
+    sa.blkbase = blkbase;
+    sa.offsets_ws = expert_offsets;
+    sa.offsets_user = nullptr;
+    sa.tile_off = tile_off;
+    sa.hdr = hdr;
+    sa.nblk = L.nblk;
+    sa.E_local = s->E_local;
+    sa.bm = tu.bm;
+    if (launch_scan(sa, hs) != hipSuccess) return MK_EHIP;
+    if (s->T == 0) return MK_OK;
+
+    SlotArgs sl{};
+    sl.ids = ids;
+    sl.lrank = lrank;
+    sl.blkbase = blkbase;
+    sl.offsets = expert_offsets;
+    sl.slot_of = slot_of;
+    sl.row_token_ws = row_token_ws;
+    sl.row_token_user = row_token;
+    sl.T = s->T;
+    sl.k = s->k;
+    sl.e_begin = s->e_begin;
+    sl.E_local = s->E_local;
+    if (launch_slots(sl, hs) != hipSuccess) return MK_EHIP;
+    if (launch_move(rows, row_token_ws, x_perm, s->d, hdr, hs) != hipSuccess) return MK_EHIP;
+
+    GemmArgs ga{};
+    ga.x_perm = x_perm;
+    ga.w = (const uint16_t *)w_experts;
+    ga.y = (uint16_t *)y_perm;
+    ga.offsets = expert_offsets;
+    ga.tile_off = tile_off;
+    ga.tile_flag = nullptr;
+    ga.hdr = hdr;
+    ga.spin_limit = spin_limit_ticks();
+    ga.epoch = 0;
+    ga.d = s->d;
+    ga.N = s->N;
+    ga.E_local = s->E_local;
+    int grid = gemm_max_grid(tu.bm, tu.bn);
+    if (grid <= 0) return MK_EHIP;
+    if (tu.n_compute_wg > 0 && tu.n_compute_wg < grid) grid = tu.n_compute_wg;
+    grid -= grid % 8;
+    if (grid < 8) grid = 8;
+    if (launch_gemm(ga, tu.bm, tu.bn, grid, hs) != hipSuccess) return MK_EHIP;
+    return MK_OK;
+}
+
+mk_status mk_poll_error(void *workspace, int32_t *detail)
+{
+    if (!workspace) return MK_EINVAL;
+    uint32_t w[2] = {0, 0};
+    if (hipMemcpy(w, workspace, sizeof w, hipMemcpyDeviceToHost) != hipSuccess) return MK_EHIP;
+    if (detail) *detail = (int32_t)w[1];
+    if (w[0] != 0) {
+        const uint32_t zero[2] = {0, 0};
+        if (hipMemcpy(workspace, zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return MK_EHIP;
+    }
+    return (mk_status)w[0];
+}
+
+}  // extern "C"

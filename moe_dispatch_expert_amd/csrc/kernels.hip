@@ -1,0 +1,170 @@
+// kernels.hip -- __global__ entry points of libmk and their launch wrappers.
+// The stage-by-stage kernels here run the same device code as the fused
+// persistent kernel, one launch per step.
+#include <hip/hip_runtime.h>
+
+#include "gemm_dev.h"
+#include "layout_dev.h"
+#include "mk_launch.h"
+#include "route_dev.h"
+
+namespace mk {
+
+template <int TPL, int EL>
+__global__ __launch_bounds__(256) void k_router_logits(RouterArgs a)
+{
+    __shared__ float lds[kRouterSegments * (kWave / EL) * TPL * EL];
+    router_logits_block<TPL, EL>(a, blockIdx.x, blockIdx.y, lds);
+}
+
+__global__ __launch_bounds__(256) void k_topk(TopkArgs ta, CountArgs ca, int do_count)
+{
+    __shared__ int32_t ids_lds[kTokBlock * kMaxK];
+    __shared__ int32_t cnt_lds[1024];
+    topk_block(ta, blockIdx.x, ids_lds);
+    __syncthreads();
+    if (do_count) count_block(ca, blockIdx.x, ids_lds, cnt_lds);
+}
+
+__global__ __launch_bounds__(256) void k_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user,
+                                                     CountArgs ca)
+{
+    __shared__ int32_t ids_lds[kTokBlock * kMaxK];
+    __shared__ int32_t cnt_lds[1024];
+    const int base_t = blockIdx.x * kTokBlock;
+    const int n_t = min(kTokBlock, ca.T - base_t);
+    for (int i = threadIdx.x; i < n_t * ca.k; i += blockDim.x) {
+        const size_t o = (size_t)base_t * ca.k + i;
+        const int32_t id = ids_in[o];
+        ids_lds[i] = id;
+        ids_ws[o] = id;
+        if (ids_user) ids_user[o] = id;
+    }
+    __syncthreads();
+    count_block(ca, blockIdx.x, ids_lds, cnt_lds);
+}
+
+__global__ __launch_bounds__(1024) void k_scan(ScanArgs a)
+{
+    __shared__ int32_t s_cnt[1024], s_til[1024];
+    scan_block(a, s_cnt, s_til);
+}
+
+__global__ __launch_bounds__(256) void k_slots(SlotArgs a)
+{
+    const int n = a.T * a.k;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) slot_one(a, i);
+}
+
+__global__ __launch_bounds__(256) void k_move(SrcRows src, const int32_t *row_token, uint16_t *x_perm, int d,
+                                              const WsHeader *hdr)
+{
+    const int R = (int)hdr->R;
+    const int waves = gridDim.x * (blockDim.x / kWave);
+    const int wid = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    for (int r = wid; r < R; r += waves) move_row(src, row_token, x_perm, d, r, threadIdx.x % kWave);
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char s1[C::STAGE];
+    gemm_worker<C>(a, blockIdx.x, gridDim.x, s0, s1);
+}
+
+// ---------------------------------------------------------------- wrappers
+
+template <int TPL, int EL>
+static hipError_t router_go(const RouterArgs &a, hipStream_t s)
+{
+    constexpr int TB = (kWave / EL) * TPL;
+    dim3 grid((a.T + TB - 1) / TB, (a.E + EL - 1) / EL);
+    hipLaunchKernelGGL((k_router_logits<TPL, EL>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int EL>
+static hipError_t router_pick_tpl(const RouterArgs &a, hipStream_t s)
+{
+    // Most tokens per lane (reuse of each Wr load) that still gives >= 256 blocks.
+    const long eb = (a.E + EL - 1) / EL;
+    const long g = kWave / EL;
+    auto blocks = [&](long tpl) { return ((a.T + g * tpl - 1) / (g * tpl)) * eb; };
+    if (blocks(16) >= 256) return router_go<16, EL>(a, s);
+    if (blocks(8) >= 256) return router_go<8, EL>(a, s);
+    if (blocks(4) >= 256) return router_go<4, EL>(a, s);
+    if (blocks(2) >= 256) return router_go<2, EL>(a, s);
+    return router_go<1, EL>(a, s);
+}
+
+hipError_t launch_router_logits(const RouterArgs &a, hipStream_t s)
+{
+    if (a.E <= 8) return router_pick_tpl<8>(a, s);
+    if (a.E <= 16) return router_pick_tpl<16>(a, s);
+    if (a.E <= 32) return router_pick_tpl<32>(a, s);
+    return router_pick_tpl<64>(a, s);
+}
+
+hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s)
+{
+    const int nblk = (ta.T + kTokBlock - 1) / kTokBlock;
+    hipLaunchKernelGGL(k_topk, dim3(nblk), dim3(256), 0, s, ta, ca, do_count ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user, const CountArgs &ca,
+                              hipStream_t s)
+{
+    const int nblk = (ca.T + kTokBlock - 1) / kTokBlock;
+    hipLaunchKernelGGL(k_count_given, dim3(nblk), dim3(256), 0, s, ids_in, ids_ws, ids_user, ca);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_slots(const SlotArgs &a, hipStream_t s)
+{
+    const long n = (long)a.T * a.k;
+    int grid = (int)((n + 255) / 256);
+    grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);
+    hipLaunchKernelGGL(k_slots, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x_perm, int d, const WsHeader *hdr,
+                       hipStream_t s)
+{
+    hipLaunchKernelGGL(k_move, dim3(1024), dim3(256), 0, s, src, row_token, x_perm, d, hdr);
+    return hipGetLastError();
+}
+
+typedef BigTile<256, 256> Tile256;
+
+hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s)
+{
+    if (bm == 256 && bn == 256) {
+        hipLaunchKernelGGL((k_gemm<Tile256>), dim3(grid), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+int gemm_max_grid(int bm, int bn)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (bm == 256 && bn == 256) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemm<Tile256>, 256, 0) !=
+            hipSuccess)
+            return 0;
+    }
+    return cus * per_cu;
+}
+
+}  // namespace mk

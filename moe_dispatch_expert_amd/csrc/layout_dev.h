@@ -1,0 +1,109 @@
+// layout_dev.h -- expert offsets (exclusive prefix sum of the histogram),
+// GEMM row-tile table, token->slot map and its inverse, and the tile-chunked
+// row scatter into the expert-contiguous buffer.
+//
+// The dispatch half of the "MoE Dispatch+GEMM" kernel ("mKernel UCCL fuses
+// NVLink/RDMA/compute into one persistent CUDA kernel", zubnet.ai, paragraph
+// 2): rows of each token are moved to the experts that chose it, tile by tile,
+// so the GEMM can start on a tile while the next one is still moving.  Slot
+// order is the reading "ascending token id within an expert" (a stable
+// counting sort), which makes the map unique.
+#pragma once
+
+#include "mk_args.h"
+#include "mk_device.h"
+#include "route_dev.h"
+
+namespace mk {
+
+struct ScanArgs {
+    const int32_t *blkcnt;     // [nblk, E_local]
+    int32_t *blkbase;          // [nblk, E_local] exclusive prefix over blocks
+    int32_t *offsets_ws;       // [E_local + 1] expert offsets (workspace copy)
+    int32_t *offsets_user;     // [E_local + 1] or nullptr
+    int32_t *tile_off;         // [E_local + 1] exclusive prefix of ceil(count / bm)
+    WsHeader *hdr;
+    int32_t nblk, E_local, bm;
+};
+
+// One block of 1024 threads: column scan over the token blocks (thread = expert),
+// then block-wide exclusive scans of counts and tile counts.  E_local <= 1024.
+__device__ __forceinline__ void scan_block(const ScanArgs &a, int32_t *s_cnt, int32_t *s_til)
+{
+    const int e = threadIdx.x;
+    int32_t cnt = 0;
+    if (e < a.E_local) {
+        for (int b = 0; b < a.nblk; ++b) {
+            const size_t o = (size_t)b * a.E_local + e;
+            a.blkbase[o] = cnt;
+            cnt += a.blkcnt[o];
+        }
+    }
+    const int32_t til = e < a.E_local ? (cnt + a.bm - 1) / a.bm : 0;
+    s_cnt[e] = cnt;
+    s_til[e] = til;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+        const int32_t c2 = e >= off ? s_cnt[e - off] : 0;
+        const int32_t t2 = e >= off ? s_til[e - off] : 0;
+        __syncthreads();
+        s_cnt[e] += c2;
+        s_til[e] += t2;
+        __syncthreads();
+    }
+    // s_* now hold inclusive sums
+    if (e < a.E_local) {
+        a.offsets_ws[e + 1] = s_cnt[e];
+        a.tile_off[e + 1] = s_til[e];
+        if (a.offsets_user) a.offsets_user[e + 1] = s_cnt[e];
+    }
+    if (e == 0) {
+        a.offsets_ws[0] = 0;
+        a.tile_off[0] = 0;
+        if (a.offsets_user) a.offsets_user[0] = 0;
+        a.hdr->R = (uint32_t)s_cnt[a.E_local - 1];
+        a.hdr->n_tiles = (uint32_t)s_til[a.E_local - 1];
+    }
+    __syncthreads();
+}
+
+struct SlotArgs {
+    const int32_t *ids;        // [T, k]
+    const int32_t *lrank;      // [T, k]
+    const int32_t *blkbase;    // [nblk, E_local]
+    const int32_t *offsets;    // [E_local + 1]
+    int32_t *slot_of;          // [T, k] (user)
+    int32_t *row_token_ws;     // [R_cap]
+    int32_t *row_token_user;   // [R_cap] or nullptr
+    int32_t T, k, e_begin, E_local;
+};
+
+__device__ __forceinline__ void slot_one(const SlotArgs &a, int i)
+{
+    const int t = i / a.k;
+    const int le = a.ids[i] - a.e_begin;
+    int32_t slot = -1;
+    const int32_t rank = a.lrank[i];
+    if (le >= 0 && le < a.E_local && rank >= 0) {
+        slot = a.offsets[le] + a.blkbase[(size_t)(t / kTokBlock) * a.E_local + le] + rank;
+        if (slot < a.offsets[le + 1]) {
+            a.row_token_ws[slot] = t;
+            if (a.row_token_user) a.row_token_user[slot] = t;
+        } else {
+            slot = -1;   // only reachable for ids that were rejected
+        }
+    }
+    a.slot_of[i] = slot;
+}
+
+// Copy one expert-buffer row r: x_perm[r] = x[row_token[r]], 16 bytes per lane.
+__device__ __forceinline__ void move_row(const SrcRows &src, const int32_t *row_token, uint16_t *x_perm,
+                                         int d, int r, int lane)
+{
+    const uint4 *s = (const uint4 *)token_row(src, row_token[r], d);
+    uint4 *dst = (uint4 *)(x_perm + (size_t)r * d);
+    const int n16 = d / 8;
+    for (int c = lane; c < n16; c += kWave) dst[c] = s[c];
+}
+
+}  // namespace mk

@@ -1,0 +1,77 @@
+// mk_args.h -- plain structs passed by value from the host launcher to the
+// kernels, and the layout of the dispatch workspace.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kMaxSources = 64;     // source shards a call may name
+constexpr int kRouterSegments = 8;  // contiguous K segments of the router dot product
+constexpr int kMaxK = 32;           // experts per token this build handles
+constexpr int kTokBlock = 64;       // tokens per counting block (one wave, lane = token)
+constexpr int kMinBM = 16;          // smallest GEMM tile height any kernel uses
+
+// Token t lives in shard t / rows_per_src at row t % rows_per_src.
+struct SrcRows {
+    const uint16_t *p[kMaxSources];
+    int32_t S;
+    int32_t rows_per_src;
+};
+
+// Arrival flags of the source chunks (chunk_rows == 0: rows resident).
+struct SrcFlags {
+    uint32_t *ready;              // [S * chunks_per_src]
+    const uint32_t *sim_delay_us; // NULL: flags are released by someone else
+    const uint16_t *sim_payload[kMaxSources];
+    int32_t has_payload;
+    int32_t chunk_rows;
+    int32_t chunks_per_src;
+    uint32_t epoch;
+};
+
+// First 256 bytes of the dispatch workspace.
+struct WsHeader {
+    uint32_t err;          // 0 or an mk_status code
+    uint32_t err_detail;
+    uint32_t bar_count;    // grid barrier arrivals (returns to 0)
+    uint32_t bar_gen;      // grid barrier generation (grows by one per barrier)
+    uint32_t n_tiles;      // GEMM row tiles of the current call
+    uint32_t R;            // routed local rows of the current call
+    uint32_t call_epoch;   // value the current call's tile flags are released with
+    uint32_t pad[57];
+};
+static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+
+// Byte offsets of the workspace segments (all 256-byte aligned).
+struct WsLayout {
+    size_t hdr, logits, ids, lrank, blkcnt, blkbase, tile_off, tile_flag, row_token, x_perm, total;
+    int32_t nblk, max_tiles, r_cap, x_perm_rows;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_local)
+{
+    WsLayout L{};
+    L.nblk = (T + kTokBlock - 1) / kTokBlock;
+    L.r_cap = T * (k < E_local ? k : E_local);
+    L.max_tiles = L.r_cap / kMinBM + E_local + 1;
+    L.x_perm_rows = L.r_cap + 256;   // a full tile past the last row stays in bounds
+    size_t o = 0;
+    L.hdr = o;       o += align256(sizeof(WsHeader));
+    L.logits = o;    o += align256((size_t)T * E * 4);
+    L.ids = o;       o += align256((size_t)T * k * 4);
+    L.lrank = o;     o += align256((size_t)T * k * 4);
+    L.blkcnt = o;    o += align256((size_t)L.nblk * E_local * 4);
+    L.blkbase = o;   o += align256((size_t)L.nblk * E_local * 4);
+    L.tile_off = o;  o += align256((size_t)(E_local + 1) * 4);
+    L.tile_flag = o; o += align256((size_t)L.max_tiles * 4);
+    L.row_token = o; o += align256((size_t)(L.r_cap + 1) * 4);
+    L.x_perm = o;    o += align256((size_t)L.x_perm_rows * d * 2);
+    L.total = o;
+    return L;
+}
+
+}  // namespace mk

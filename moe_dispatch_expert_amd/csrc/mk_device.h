@@ -1,0 +1,168 @@
+// mk_device.h -- device-side building blocks shared by the libmk kernels
+// (gfx950 only): bf16 conversions, ordered top-k keys, wave reductions,
+// agent-scope acquire/release flags with bounded waits, and a grid barrier for
+// co-resident (cooperatively launched) grids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Error codes written into the workspace error word (match mk_status values).
+constexpr uint32_t kErrInval = 1;
+constexpr uint32_t kErrTimeout = 5;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// bf16 bits of a float, round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Order-preserving unsigned key of a float: a > b (as floats) iff key(a) > key(b);
+// -0 is mapped to +0 first so that the two compare equal, as floats do.
+__device__ __forceinline__ uint32_t float_order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k selection key: larger logit first, then lower expert id.  A key of 0
+// is below every real key and marks "already taken".
+__device__ __forceinline__ uint64_t topk_key(float logit, int e)
+{
+    return ((uint64_t)float_order_key(logit) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int topk_key_expert(uint64_t key)
+{
+    return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint64_t o = __shfl_xor(v, off, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt()
+{
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// ---------------------------------------------------------------- flags
+
+__device__ __forceinline__ uint32_t ld_acquire(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wall clock (100 MHz on MI355X), used for bounded waits and the arrival simulator.
+__device__ __forceinline__ uint64_t now_ticks() { return wall_clock64(); }
+
+// Record the first device-side error (code, detail) in the workspace error words.
+__device__ __forceinline__ void raise_error(uint32_t *err, uint32_t code, uint32_t detail)
+{
+    uint32_t expected = 0;
+    if (__hip_atomic_compare_exchange_strong(err, &expected, code, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_store(err + 1, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin (one lane per wave calls this) until *flag == want, with sleeps; gives
+// up after `limit` wall-clock ticks or as soon as another wave raised an error.
+// Returns true when the flag was seen (acquire), false on give-up.
+__device__ __forceinline__ bool wait_flag_eq(const uint32_t *flag, uint32_t want, uint32_t *err,
+                                             uint64_t limit, uint32_t detail)
+{
+    if (ld_acquire(flag) == want) return true;
+    const uint64_t t0 = now_ticks();
+    for (;;) {
+        __builtin_amdgcn_s_sleep(2);
+        if (ld_acquire(flag) == want) return true;
+        if (ld_relaxed(err) != 0) return false;
+        if (now_ticks() - t0 > limit) {
+            raise_error(err, kErrTimeout, detail);
+            return false;
+        }
+    }
+}
+
+// Same, for "value >= want" on a monotonically growing counter (wrap-safe compare).
+__device__ __forceinline__ bool wait_flag_geq(const uint32_t *flag, uint32_t want, uint32_t *err,
+                                              uint64_t limit, uint32_t detail)
+{
+    if ((int32_t)(ld_acquire(flag) - want) >= 0) return true;
+    const uint64_t t0 = now_ticks();
+    for (;;) {
+        __builtin_amdgcn_s_sleep(2);
+        if ((int32_t)(ld_acquire(flag) - want) >= 0) return true;
+        if (ld_relaxed(err) != 0) return false;
+        if (now_ticks() - t0 > limit) {
+            raise_error(err, kErrTimeout, detail);
+            return false;
+        }
+    }
+}
+
+// Grid barrier for a co-resident grid.  `count` returns to 0 after every
+// barrier and `gen` grows by one, so the words are reusable across launches
+// without a reset.  Every workgroup must call it the same number of times.
+// Returns false if the wait gave up (error raised); callers then skip work.
+__device__ __forceinline__ bool grid_barrier(uint32_t *count, uint32_t *gen, uint32_t *err,
+                                             uint64_t limit, uint32_t detail)
+{
+    __syncthreads();
+    __shared__ int ok_shared;
+    if (threadIdx.x == 0) {
+        const uint32_t g = ld_acquire(gen);
+        const uint32_t arrived =
+            __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        bool ok = true;
+        if (arrived == gridDim.x * gridDim.y * gridDim.z) {
+            __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st_release(gen, g + 1u);
+        } else {
+            ok = wait_flag_eq(gen, g + 1u, err, limit, detail);
+        }
+        ok_shared = ok ? 1 : 0;
+    }
+    __syncthreads();
+    return ok_shared != 0;
+}
+
+}  // namespace mk

@@ -1,0 +1,33 @@
+// mk_launch.h -- host-side launch wrappers for the libmk kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "mk_args.h"
+
+namespace mk {
+
+struct RouterArgs;
+struct TopkArgs;
+struct CountArgs;
+struct ScanArgs;
+struct SlotArgs;
+struct GemmArgs;
+
+// Router logits; picks the lane layout from E and the tokens per lane from T.
+hipError_t launch_router_logits(const RouterArgs &a, hipStream_t s);
+// Top-k + gate for all tokens; with do_count also the per-block histogram and ranks.
+hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s);
+// Histogram and ranks of caller-given ids (copied into the workspace id array).
+hipError_t launch_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user, const CountArgs &ca,
+                              hipStream_t s);
+hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+hipError_t launch_slots(const SlotArgs &a, hipStream_t s);
+hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x_perm, int d, const WsHeader *hdr,
+                       hipStream_t s);
+// Grouped GEMM over the tile table; bm/bn select the tile shape.
+hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s);
+// Largest co-resident grid of the GEMM kernel for this tile shape.
+int gemm_max_grid(int bm, int bn);
+
+}  // namespace mk

@@ -1,0 +1,98 @@
+"""The C ABI boundary without a GPU: libmk.so loads, exports every function
+include/mk.h declares, its struct layouts match the Python binding, and
+argument errors come back synchronously (no launch, so no device needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_dispatch_expert_amd as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mk.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib_path = mk.LIB_PATH
+    assert os.path.exists(lib_path), "build libmk.so first (moe_dispatch_expert_amd/build.py)"
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (mk_\w+)", out))
+    declared = _declared_functions()
+    assert len(declared) >= 7
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    lib = mk.load()
+    for f in declared:
+        assert hasattr(lib, f)
+
+
+def test_struct_layout_matches_binding(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "mk.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(mk_shape), sizeof(mk_sources), sizeof(mk_tuning), sizeof(mk_status));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", offsetof(mk_sources, S), offsetof(mk_sources, rows_per_src),
+         offsetof(mk_sources, x), offsetof(mk_sources, chunk_rows), offsetof(mk_sources, chunk_ready),
+         offsetof(mk_sources, epoch), offsetof(mk_sources, sim_delay_us), offsetof(mk_sources, sim_payload));
+  printf("%zu %zu\n", offsetof(mk_shape, N), offsetof(mk_tuning, bk));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    sizes = list(map(int, lines[0].split()))
+    offs = list(map(int, lines[1].split()))
+    last = list(map(int, lines[2].split()))
+    assert sizes == [ctypes.sizeof(mk.MkShape), ctypes.sizeof(mk.MkSources), ctypes.sizeof(mk.MkTuning), 4]
+    S = mk.MkSources
+    assert offs == [S.S.offset, S.rows_per_src.offset, S.x.offset, S.chunk_rows.offset, S.chunk_ready.offset,
+                    S.epoch.offset, S.sim_delay_us.offset, S.sim_payload.offset]
+    assert last == [mk.MkShape.N.offset, mk.MkTuning.bk.offset]
+
+
+def test_header_compiles_as_cxx(tmp_path):
+    src = tmp_path / "h.cpp"
+    src.write_text('#include "mk.h"\nint main() { return mk_status_str ? 0 : 1; }\n')
+    subprocess.run(["g++", "-std=c++11", "-fsyntax-only", "-I", os.path.join(ROOT, "include"), str(src)],
+                   check=True)
+
+
+def test_status_strings():
+    assert mk.mk_status_str(mk.MK_OK) == "ok"
+    assert "workspace" in mk.mk_status_str(mk.MK_EWORKSPACE)
+    assert mk.mk_status_str(99) == "unknown status"
+
+
+def test_argument_errors_are_synchronous():
+    lib = mk.load()
+    # k > E, bad d, null pointers: rejected before any HIP call
+    assert lib.mk_route_topk(None, None, None, 4, 128, 8, 9, None, None, None, 0, None) == mk.MK_EINVAL
+    assert lib.mk_route_topk(None, None, None, 4, 100, 8, 2, None, None, None, 0, None) == mk.MK_EINVAL
+    assert lib.mk_route_topk(None, None, None, 4, 136, 8, 2, None, None, None, 0, None) == mk.MK_EUNSUPPORTED
+    assert lib.mk_route_topk(None, None, None, 4, 128, 8, 2, None, None, None, 0, None) == mk.MK_EINVAL
+    assert lib.mk_route_topk(None, None, None, 0, 128, 8, 2, None, None, None, 0, None) == mk.MK_OK
+
+
+def test_workspace_bytes_and_tuning_without_gpu():
+    good = mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336)
+    assert good > 8192 * 4096 * 2          # holds the expert-contiguous row buffer
+    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 9, 0, 8, 14336) == 0   # k > E
+    assert mk.mk_dispatch_gemm_workspace_bytes(16, 128, 8, 2, 4, 8, 64) == 0         # local range past E
+    t = mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336)
+    assert t["bm"] > 0 and t["bn"] > 0
+    with pytest.raises(mk.MkError):
+        mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14335)
