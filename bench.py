@@ -1,0 +1,214 @@
+"""Benchmark of the fused MoE dispatch + expert GEMM on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--seed 0]
+
+One step = one mk_dispatch_gemm call over one batch of synthetic input
+(routing, histogram, offsets, slots, row scatter, grouped GEMM), inputs
+resident in HBM before the timed region.  Prints one JSON line:
+  value          whole-step TFLOP/s, 2*R*d*N flops per step (R = routed local rows)
+  roofline       the expert-GEMM launch alone (timed with HIP events the
+                 library records around it), against the dense bf16 MFMA peak
+  cpu_baseline   the CPU oracle timed on this host on a bounded sample
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense bf16 matrix peak: 256 CUs x 4096 flop/clk x 2.4 GHz (vendor figure 2.5 PFLOP/s).
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused MoE dispatch+GEMM TFLOP/s (% MFMA peak) + routed tokens/s, 1 GPU"
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _events(hip, n):
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e)
+    return evs
+
+
+def _elapsed_ms(hip, a, b) -> float:
+    hip.hipEventSynchronize(b)
+    ms = ctypes.c_float()
+    if hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return float(ms.value)
+
+
+def _csrc_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "moe_dispatch_expert_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str, launch_bytes_alg: float):
+    """HBM traffic per GEMM launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"gemm_{workload}_hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("csrc_sha256_16") != _csrc_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
+    import oracle
+    wl = inp["wl"]
+    t0 = time.perf_counter()
+    b = None if inp["bias"] is None else inp["bias"].numpy()
+    _, ids, _ = oracle.route(inp["x"], inp["w_router"].numpy(), wl.k, b)
+    _, offsets, _, row_token = oracle.layout(ids, wl.e_begin, wl.E_local)
+    t_route = time.perf_counter() - t0
+    R = int(offsets[-1])
+    rng = np.random.default_rng(0)
+    # one probe row, then as many rows as fit the budget
+    t1 = time.perf_counter()
+    oracle.expert_rows(inp["x"], inp["w_experts"], offsets, row_token, np.array([0], dtype=np.int32))
+    per_row = max(time.perf_counter() - t1, 1e-4)
+    n = int(max(1, min(R, (budget_s - t_route) / per_row * oracle.num_threads())))
+    rows = np.sort(rng.choice(R, size=n, replace=False)).astype(np.int32)
+    t2 = time.perf_counter()
+    oracle.expert_rows(inp["x"], inp["w_experts"], offsets, row_token, rows)
+    t_gemm = time.perf_counter() - t2
+    t_full = t_route + t_gemm * R / n          # extrapolated whole-job time
+    flops = 2.0 * R * wl.d * wl.N
+    return {"value": flops / t_full / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"routing+layout of all {wl.T} tokens ({t_route:.2f} s) + fp64 GEMM of {n} of {R} "
+                       f"expert rows ({t_gemm:.2f} s), GEMM time scaled to all rows"),
+            "routed_rows_per_s": R / t_full, "matches_gpu_R": R == R_gpu}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share only (asked for --gpus {args.gpus}); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_dispatch_expert_amd as mk
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl, args.seed)
+    dev = torch.device("cuda:0")
+    x = inp["x"]
+    xs = ([x[s * wl.rows_per_src:(s + 1) * wl.rows_per_src].contiguous().to(dev) for s in range(wl.S)]
+          if wl.S > 1 else x.to(dev))
+    wr = inp["w_router"].to(dev)
+    bias = None if inp["bias"] is None else inp["bias"].to(dev)
+    we = inp["w_experts"].to(dev)
+    ids_in = None
+    if wl.route_outside:   # the sources route their own tokens before the payload arrives (untimed)
+        parts = [mk.mk_route_topk(xs[s], wr, wl.k)[0] for s in range(wl.S)]
+        ids_in = torch.cat(parts).contiguous()
+    ws = torch.zeros(mk.mk_dispatch_gemm_workspace_bytes(wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N,
+                                                         wl.S), dtype=torch.uint8, device=dev)
+    out = mk.mk_dispatch_gemm(xs, we, wl.k, w_router=wr, bias=bias, topk_ids_in=ids_in, E=wl.E,
+                              e_begin=wl.e_begin, workspace=ws)
+    bufs = {k: out[k] for k in ("y_perm", "slot_of", "expert_offsets", "topk_ids", "topk_w", "row_token")}
+    hip = _hip()
+    evs = _events(hip, 2 * args.steps)
+
+    def step(i=None):
+        tune = None if i is None else {"ev_gemm_begin": evs[2 * i], "ev_gemm_end": evs[2 * i + 1]}
+        mk.mk_dispatch_gemm(xs, we, wl.k, w_router=wr, bias=bias, topk_ids_in=ids_in, E=wl.E,
+                            e_begin=wl.e_begin, workspace=ws, out=bufs, tune=tune)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st, detail = mk.mk_poll_error(ws)
+    if st != mk.MK_OK:
+        raise SystemExit(f"device error {mk.mk_status_str(st)} ({detail})")
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    gemm_ms = float(np.mean([_elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in range(args.steps)]))
+    for e in evs:
+        hip.hipEventDestroy(e)
+
+    R = int(bufs["expert_offsets"][-1].item())
+    flops = 2.0 * R * wl.d * wl.N
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    counts = torch.diff(bufs["expert_offsets"]).cpu()
+    hit = int((counts > 0).sum())
+    alg_bytes = (hit * wl.N * wl.d * 2 + R * wl.N * 2      # weights of hit experts, y_perm
+                 + wl.T * wl.d * 2 + (0 if ids_in is not None else wl.d * wl.E * 4))
+    traffic = _traffic(args.workload, alg_bytes)
+    # Which roof bounds the GEMM launch: flops per algorithmic byte against the ridge point.
+    if flops / max(alg_bytes, 1) >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)}
+    else:
+        gbs = alg_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel": "grouped expert GEMM", "launch_ms": round(gemm_ms, 4),
+                 "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes})
+    rec = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "N": wl.N,
+                   "E_local": wl.E_local, "e_begin": wl.e_begin, "sources": wl.S, "R": R, "seed": args.seed,
+                   "routing": "by the sources (untimed)" if ids_in is not None else "inside the step"},
+        "mfma_frac_step": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "routed_rows_per_s": R / (ms_step * 1e-3), "tokens_per_s": wl.T / (ms_step * 1e-3),
+        "hbm_GBs_step_alg": alg_bytes / (ms_step * 1e-3) / 1e9,
+        "roofline": roof,
+        "torch": torch.__version__,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, R)
+        rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -76,9 +76,14 @@ typedef struct {
 /* Role split and tile sizes.  All zeros = the per-shape table (mk_select_tuning).
  * n_mover_wg workgroups start in the dispatch (mover) role and join the GEMM
  * role when the dispatch work is done; n_compute_wg workgroups start in the
- * GEMM role.  bm/bn/bk: rows, columns and depth of one GEMM tile. */
+ * GEMM role.  bm/bn/bk: rows, columns and depth of one GEMM tile.
+ * ev_gemm_begin / ev_gemm_end: NULL, or hipEvent_t handles the library records
+ * on `stream` immediately before and after the launch that runs the expert
+ * GEMM, so a caller can time that kernel alone. */
 typedef struct {
     int32_t n_mover_wg, n_compute_wg, bm, bn, bk;
+    void *ev_gemm_begin;
+    void *ev_gemm_end;
 } mk_tuning;
 
 /* Router: logits l[t,e] = sum_i x[t,i] * w_router[i,e] (+ bias[e]), fp32, in a

@@ -39,7 +39,9 @@ class MkSources(ctypes.Structure):
 
 class MkTuning(ctypes.Structure):
     _fields_ = [("n_mover_wg", _c_i32), ("n_compute_wg", _c_i32), ("bm", _c_i32), ("bn", _c_i32),
-                ("bk", _c_i32)]
+                ("bk", _c_i32), ("ev_gemm_begin", _vp), ("ev_gemm_end", _vp)]
+
+TUNING_INTS = ("n_mover_wg", "n_compute_wg", "bm", "bn", "bk")
 
 
 class MkError(RuntimeError):
@@ -159,7 +161,7 @@ def mk_select_tuning(T, d, E, k, e_begin, E_local, N) -> dict:
     src = MkSources(1, T, None, 0, None, 0, None, None)
     out = MkTuning()
     _check(load().mk_select_tuning(ctypes.byref(shape), ctypes.byref(src), ctypes.byref(out)), "mk_select_tuning")
-    return {f: getattr(out, f) for f, _ in MkTuning._fields_}
+    return {f: getattr(out, f) for f in TUNING_INTS}
 
 
 def mk_poll_error(workspace: torch.Tensor):
@@ -211,7 +213,8 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
         workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     tu = None
     if tune:
-        tu = MkTuning(*(int(tune.get(f, 0)) for f, _ in MkTuning._fields_))
+        tu = MkTuning(*(int(tune.get(f, 0)) for f in TUNING_INTS), tune.get("ev_gemm_begin"),
+                      tune.get("ev_gemm_end"))
     st = lib.mk_dispatch_gemm(ctypes.byref(shape), ctypes.byref(srcs.c), _ptr(w_router), _ptr(bias),
                               _ptr(topk_ids_in), _ptr(w_experts), _ptr(o["y_perm"]), _ptr(o["slot_of"]),
                               _ptr(o["expert_offsets"]), _ptr(o["topk_ids"]), _ptr(o["topk_w"]),

@@ -184,6 +184,8 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         if (tune->bm != 256 || tune->bn != 256 || (tune->bk != 0 && tune->bk != 64)) return MK_EUNSUPPORTED;
         tu.n_compute_wg = tune->n_compute_wg;
     }
+    hipEvent_t ev_begin = tune ? (hipEvent_t)tune->ev_gemm_begin : nullptr;
+    hipEvent_t ev_end = tune ? (hipEvent_t)tune->ev_gemm_end : nullptr;
 
     hipStream_t hs = (hipStream_t)stream;
     char *ws = (char *)workspace;
@@ -280,7 +282,9 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     if (tu.n_compute_wg > 0 && tu.n_compute_wg < grid) grid = tu.n_compute_wg;
     grid -= grid % 8;
     if (grid < 8) grid = 8;
+    if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
     if (launch_gemm(ga, tu.bm, tu.bn, grid, hs) != hipSuccess) return MK_EHIP;
+    if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
     return MK_OK;
 }
 

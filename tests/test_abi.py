@@ -46,7 +46,7 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", offsetof(mk_sources, S), offsetof(mk_sources, rows_per_src),
          offsetof(mk_sources, x), offsetof(mk_sources, chunk_rows), offsetof(mk_sources, chunk_ready),
          offsetof(mk_sources, epoch), offsetof(mk_sources, sim_delay_us), offsetof(mk_sources, sim_payload));
-  printf("%zu %zu\n", offsetof(mk_shape, N), offsetof(mk_tuning, bk));
+  printf("%zu %zu %zu\n", offsetof(mk_shape, N), offsetof(mk_tuning, bk), offsetof(mk_tuning, ev_gemm_end));
   return 0;
 }
 ''')
@@ -61,7 +61,7 @@ int main(void) {
     S = mk.MkSources
     assert offs == [S.S.offset, S.rows_per_src.offset, S.x.offset, S.chunk_rows.offset, S.chunk_ready.offset,
                     S.epoch.offset, S.sim_delay_us.offset, S.sim_payload.offset]
-    assert last == [mk.MkShape.N.offset, mk.MkTuning.bk.offset]
+    assert last == [mk.MkShape.N.offset, mk.MkTuning.bk.offset, mk.MkTuning.ev_gemm_end.offset]
 
 
 def test_header_compiles_as_cxx(tmp_path):
