@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "../../include/mk.h"
+#include "fused_dev.h"
 #include "gemm_dev.h"
 #include "layout_dev.h"
 #include "mk_args.h"
@@ -18,25 +19,18 @@ using namespace mk;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Wall-clock ticks a device-side wait may spin (MK_TIMEOUT_US, default 2 s).
+int ticks_per_us();
+
+// Wall-clock ticks a device-side wait may spin: MK_TIMEOUT_US (read at every
+// call), default 2 s.
 uint64_t spin_limit_ticks()
 {
-    static uint64_t ticks = 0;
-    if (ticks == 0) {
-        long us = 2000000;
-        if (const char *e = std::getenv("MK_TIMEOUT_US")) {
-            const long v = std::strtol(e, nullptr, 10);
-            if (v > 0) us = v;
-        }
-        int khz = 100000;
-        int dev = 0;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            int r = 0;
-            if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) == hipSuccess && r > 0) khz = r;
-        }
-        ticks = (uint64_t)us * (uint64_t)khz / 1000u;
+    long us = 2000000;
+    if (const char *e = std::getenv("MK_TIMEOUT_US")) {
+        const long v = std::strtol(e, nullptr, 10);
+        if (v > 0) us = v;
     }
-    return ticks;
+    return (uint64_t)us * (uint64_t)ticks_per_us();
 }
 
 mk_status check_shape(const mk_shape *s)
@@ -57,7 +51,15 @@ mk_status check_sources(const mk_shape *s, const mk_sources *src)
     for (int i = 0; i < src->S; ++i)
         if (s->T > 0 && (!src->x[i] || !aligned16(src->x[i]))) return MK_EINVAL;
     if (src->chunk_rows < 0) return MK_EINVAL;
-    if (src->chunk_rows > 0) return MK_EUNSUPPORTED;   // arrival flags need the fused kernel
+    if (src->chunk_rows > 0) {
+        if (!src->chunk_ready || !aligned16(src->chunk_ready)) return MK_EINVAL;
+        if (src->sim_delay_us && !aligned16(src->sim_delay_us)) return MK_EINVAL;
+        if (src->sim_payload) {
+            if (!src->sim_delay_us) return MK_EINVAL;
+            for (int i = 0; i < src->S; ++i)
+                if (!src->sim_payload[i] || !aligned16(src->sim_payload[i])) return MK_EINVAL;
+        }
+    }
     return MK_OK;
 }
 
@@ -70,13 +72,32 @@ SrcRows make_src_rows(const mk_sources *src)
     return r;
 }
 
-mk_tuning table_tuning(const mk_shape *s)
+int ticks_per_us()
+{
+    static int v = 0;
+    if (v == 0) {
+        int dev = 0, khz = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz >= 1000)
+            v = khz / 1000;
+        else
+            v = 100;
+    }
+    return v;
+}
+
+// The per-shape table.  Every co-resident workgroup starts as a mover when
+// all source rows are resident (the copy then takes a few microseconds and
+// every workgroup turns to the GEMM as soon as its share is moved); when rows
+// arrive from peers, 64 workgroups wait for arrivals and move while the rest
+// compute on the tiles that are complete.
+mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
 {
     mk_tuning t{};
     t.bm = 256;
     t.bn = 256;
     t.bk = 64;
-    t.n_mover_wg = 0;
+    t.n_mover_wg = (src && src->chunk_rows > 0) ? 64 : 256;
     t.n_compute_wg = 0;   // 0: every co-resident workgroup
     (void)s;
     return t;
@@ -156,7 +177,7 @@ mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *
     const mk_status st = check_shape(s);
     if (st != MK_OK) return st;
     if (!out) return MK_EINVAL;
-    *out = table_tuning(s);
+    *out = table_tuning(s, src);
     return MK_OK;
 }
 
@@ -179,11 +200,18 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     const WsLayout L = ws_layout(s->T, s->d, s->E, s->k, s->E_local);
     if (workspace_bytes < L.total) return MK_EWORKSPACE;
 
-    mk_tuning tu = table_tuning(s);
+    mk_tuning tu = table_tuning(s, src);
     if (tune && (tune->bm || tune->bn || tune->bk || tune->n_mover_wg || tune->n_compute_wg)) {
-        if (tune->bm != 256 || tune->bn != 256 || (tune->bk != 0 && tune->bk != 64)) return MK_EUNSUPPORTED;
+        if ((tune->bm && tune->bm != 256) || (tune->bn && tune->bn != 256) || (tune->bk && tune->bk != 64))
+            return MK_EUNSUPPORTED;
+        if (tune->n_mover_wg) tu.n_mover_wg = tune->n_mover_wg;
         tu.n_compute_wg = tune->n_compute_wg;
     }
+    // The fused persistent kernel is the path; n_mover_wg < 0 asks for one launch per step instead
+    // (no overlap, for comparison).  Phase 3 keeps nblk * E_local block counts in LDS.
+    const bool fits_fused = (long)L.nblk * s->E_local <= kMaxScanEntries;
+    const bool staged = tu.n_mover_wg < 0 || s->T == 0 || !fits_fused;
+    if (staged && src->chunk_rows > 0) return MK_EUNSUPPORTED;
     hipEvent_t ev_begin = tune ? (hipEvent_t)tune->ev_gemm_begin : nullptr;
     hipEvent_t ev_end = tune ? (hipEvent_t)tune->ev_gemm_end : nullptr;
 
@@ -199,6 +227,94 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     int32_t *row_token_ws = (int32_t *)(ws + L.row_token);
     uint16_t *x_perm = (uint16_t *)(ws + L.x_perm);
     const SrcRows rows = make_src_rows(src);
+
+    if (!staged) {
+        const int grid = fused_max_grid();
+        if (grid <= 0) return MK_EHIP;
+        FusedArgs fa{};
+        fa.ra.src = rows;
+        fa.ra.wr = w_router;
+        fa.ra.bias = bias;
+        fa.ra.logits = logits;
+        fa.ra.T = s->T;
+        fa.ra.d = s->d;
+        fa.ra.E = s->E;
+        fa.ta.logits = logits;
+        fa.ta.ids = ids;
+        fa.ta.ids_user = topk_ids_out;
+        fa.ta.w_user = topk_w_out;
+        fa.ta.T = s->T;
+        fa.ta.E = s->E;
+        fa.ta.k = s->k;
+        fa.ca.ids = ids;
+        fa.ca.lrank = lrank;
+        fa.ca.blkcnt = blkcnt;
+        fa.ca.err = &hdr->err;
+        fa.ca.T = s->T;
+        fa.ca.E = s->E;
+        fa.ca.k = s->k;
+        fa.ca.e_begin = s->e_begin;
+        fa.ca.E_local = s->E_local;
+        fa.ga.x_perm = x_perm;
+        fa.ga.w = (const uint16_t *)w_experts;
+        fa.ga.y = (uint16_t *)y_perm;
+        fa.ga.offsets = expert_offsets;
+        fa.ga.tile_off = tile_off;
+        fa.ga.tile_flag = nullptr;
+        fa.ga.hdr = hdr;
+        fa.ga.spin_limit = spin_limit_ticks();
+        fa.ga.d = s->d;
+        fa.ga.N = s->N;
+        fa.ga.E_local = s->E_local;
+        fa.src = rows;
+        if (src->chunk_rows > 0) {
+            fa.fl.ready = src->chunk_ready;
+            fa.fl.sim_delay_us = src->sim_delay_us;
+            fa.fl.has_payload = src->sim_payload ? 1 : 0;
+            for (int i = 0; src->sim_payload && i < src->S; ++i)
+                fa.fl.sim_payload[i] = (const uint16_t *)src->sim_payload[i];
+            fa.fl.chunk_rows = src->chunk_rows;
+            fa.fl.chunks_per_src = (src->rows_per_src + src->chunk_rows - 1) / src->chunk_rows;
+            fa.fl.epoch = src->epoch;
+        }
+        fa.ids_in = topk_ids_in;
+        fa.ids_user = topk_ids_in ? topk_ids_out : nullptr;
+        fa.offsets = expert_offsets;
+        fa.slot_of = slot_of;
+        fa.row_token_ws = row_token_ws;
+        fa.row_token_user = row_token;
+        fa.x_perm = x_perm;
+        fa.blkbase = blkbase;
+        fa.tile_off = tile_off;
+        fa.tile_cnt = (uint32_t *)(ws + L.tile_flag);
+        fa.xcd_next = hdr->xcd_next;
+        fa.hdr = hdr;
+        fa.spin_limit = spin_limit_ticks();
+        fa.T = s->T;
+        fa.d = s->d;
+        fa.E = s->E;
+        fa.k = s->k;
+        fa.e_begin = s->e_begin;
+        fa.E_local = s->E_local;
+        fa.nblk = L.nblk;
+        fa.bm = tu.bm;
+        fa.has_sim = (src->chunk_rows > 0 && src->sim_delay_us) ? 1 : 0;
+        const int G = grid - fa.has_sim;
+        fa.router_el = s->E <= 8 ? 8 : 64;
+        {
+            const long g = kWave / fa.router_el;
+            const long neb = (s->E + fa.router_el - 1) / fa.router_el;
+            auto units = [&](long tpl) { return ((s->T + g * tpl - 1) / (g * tpl)) * neb; };
+            fa.router_tpl = units(16) >= 2L * G ? 16 : (units(4) >= G ? 4 : 1);
+        }
+        fa.n_mover = tu.n_mover_wg < 1 ? 1 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);
+        fa.max_tiles = L.max_tiles;
+        fa.ticks_per_us = (uint32_t)ticks_per_us();
+        if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
+        if (launch_fused(fa, grid, hs) != hipSuccess) return MK_EHIP;
+        if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
+        return MK_OK;
+    }
 
     CountArgs ca{};
     ca.ids = ids;

@@ -1,0 +1,403 @@
+// fused_dev.h -- the persistent fused dispatch + expert GEMM kernel body.
+//
+// "mKernel UCCL fuses NVLink/RDMA/compute into one persistent CUDA kernel"
+// (zubnet.ai), paragraph 2, describes one persistent kernel that pays the
+// launch cost once and overlaps at tile granularity, so a tile that has
+// arrived feeds the GEMM while the next is in flight; "UC Berkeley presenta
+// mKernel ..." (edge.aivizor.me), paragraph 2, has thread blocks take roles
+// (compute, communication) with the count per role set per tensor shape.
+// Here, on one MI355X, a co-resident grid of workgroups runs:
+//   phase 1  router logits                                  (all workgroups)
+//   -- grid barrier --
+//   phase 2  top-k, gate, per-64-token histogram + ranks    (all)
+//   -- grid barrier --
+//   phase 3  offsets / per-block bases by an LDS scan in every workgroup,
+//            slot map and row map for the workgroup's own token blocks
+//   -- grid barrier --
+//   roles    movers: copy row chunks of each tile into the expert-contiguous
+//            buffer (waiting on source-chunk arrival flags when the rows come
+//            from peers), then bump the tile's arrival count (release);
+//            compute: take GEMM tasks from per-XCD queues, wait (acquire)
+//            until the tile's count is complete, run the tile;
+//            movers join the compute role when the dispatch work is done.
+//   arrival simulator (optional, one workgroup outside the barriers): stands
+//            in for the peers and releases source-chunk flags at given delays.
+#pragma once
+
+#include "gemm_dev.h"
+#include "layout_dev.h"
+#include "mk_args.h"
+#include "mk_device.h"
+#include "route_dev.h"
+
+namespace mk {
+
+constexpr int kMoveRows = 16;          // rows per mover work unit
+constexpr int kMaxScanEntries = 16384; // nblk * E_local held in LDS by phase 3
+
+struct FusedArgs {
+    RouterArgs ra;
+    TopkArgs ta;
+    CountArgs ca;
+    GemmArgs ga;
+    SrcRows src;
+    SrcFlags fl;
+    const int32_t *ids_in;       // nullptr: route inside
+    int32_t *ids_user;           // copy of ids (given ids path) or nullptr
+    int32_t *offsets;            // [E_local + 1] user
+    int32_t *slot_of;            // [T, k] user
+    int32_t *row_token_ws;       // [R_cap]
+    int32_t *row_token_user;     // or nullptr
+    uint16_t *x_perm;            // [x_perm_rows, d] the expert-contiguous row buffer
+    int32_t *blkbase;            // [nblk, E_local]
+    int32_t *tile_off;           // [E_local + 1]
+    uint32_t *tile_cnt;          // [max_tiles] row chunks moved into each tile (reset every call)
+    uint32_t *xcd_next;          // [8] per-XCD task counters (reset every call)
+    WsHeader *hdr;
+    uint64_t spin_limit;
+    int32_t T, d, E, k, e_begin, E_local, nblk, bm;
+    int32_t router_el, router_tpl;
+    int32_t n_mover;             // workgroups that start as movers
+    int32_t has_sim;             // last workgroup is the arrival simulator
+    int32_t max_tiles;
+    uint32_t ticks_per_us;       // wall-clock ticks per microsecond
+};
+
+__device__ __forceinline__ int fused_participants(const FusedArgs &a) { return (int)gridDim.x - a.has_sim; }
+
+// Grid barrier over the participating workgroups (the simulator stays out).
+__device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detail)
+{
+    wait_vmem_all();   // every wave's stores of the phase have reached L2
+    __syncthreads();
+    __shared__ int ok_shared;
+    if (threadIdx.x == 0) {
+        const uint32_t g = ld_acquire(&a.hdr->bar_gen);
+        const uint32_t arrived =
+            __hip_atomic_fetch_add(&a.hdr->bar_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        bool ok = true;
+        if (arrived == (uint32_t)fused_participants(a)) {
+            __hip_atomic_store(&a.hdr->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st_release(&a.hdr->bar_gen, g + 1u);
+        } else {
+            ok = wait_flag_eq(&a.hdr->bar_gen, g + 1u, &a.hdr->err, a.spin_limit, detail);
+        }
+        ok_shared = ok ? 1 : 0;
+    }
+    __syncthreads();
+    return ok_shared != 0;
+}
+
+template <int TPL, int EL>
+__device__ void fused_router_phase(const FusedArgs &a, int w, int G, float *lds)
+{
+    constexpr int TB = (kWave / EL) * TPL;
+    const int ntb = (a.T + TB - 1) / TB;
+    const int neb = (a.E + EL - 1) / EL;
+    for (int u = w; u < ntb * neb; u += G) router_logits_block<TPL, EL>(a.ra, u % ntb, u / ntb, lds);
+}
+
+__device__ void fused_router_dispatch(const FusedArgs &a, int w, int G, float *lds)
+{
+    if (a.router_el == 8) {
+        if (a.router_tpl == 1) fused_router_phase<1, 8>(a, w, G, lds);
+        else if (a.router_tpl == 4) fused_router_phase<4, 8>(a, w, G, lds);
+        else fused_router_phase<16, 8>(a, w, G, lds);
+    } else {
+        if (a.router_tpl == 1) fused_router_phase<1, 64>(a, w, G, lds);
+        else if (a.router_tpl == 4) fused_router_phase<4, 64>(a, w, G, lds);
+        else fused_router_phase<16, 64>(a, w, G, lds);
+    }
+}
+
+// Phase 3 in one workgroup: per-block exclusive bases for every local expert
+// (into LDS and, for the blocks this workgroup owns, into the workspace),
+// expert offsets and tile prefix (LDS).  cnt: nblk*E_local ints; part: 256 ints;
+// off/toff: E_local+1 ints each.
+__device__ void fused_scan(const FusedArgs &a, int32_t *cnt, int32_t *part, int32_t *off, int32_t *toff)
+{
+    const int n = a.nblk * a.E_local;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = a.ca.blkcnt[i];
+    __syncthreads();
+    // thread (e, p): blocks [p*L, (p+1)*L) of expert column e
+    const int P = a.E_local >= (int)blockDim.x ? 1 : (int)blockDim.x / a.E_local;
+    const int L = (a.nblk + P - 1) / P;
+    for (int base_e = 0; base_e < a.E_local; base_e += (int)blockDim.x / P) {
+        const int e = base_e + (int)threadIdx.x % ((int)blockDim.x / P);
+        const int p = (int)threadIdx.x / ((int)blockDim.x / P);
+        int32_t s = 0;
+        if (e < a.E_local && p < P)
+            for (int b = p * L; b < min(a.nblk, (p + 1) * L); ++b) s += cnt[b * a.E_local + e];
+        __syncthreads();
+        if (e < a.E_local && p < P) part[p * ((int)blockDim.x / P) + ((int)threadIdx.x % ((int)blockDim.x / P))] = s;
+        __syncthreads();
+        if (e < a.E_local && p < P) {
+            int32_t run = 0;
+            const int col = (int)threadIdx.x % ((int)blockDim.x / P);
+            for (int q = 0; q < p; ++q) run += part[q * ((int)blockDim.x / P) + col];
+            for (int b = p * L; b < min(a.nblk, (p + 1) * L); ++b) {
+                const int32_t c = cnt[b * a.E_local + e];
+                cnt[b * a.E_local + e] = run;   // now the exclusive base of block b
+                run += c;
+            }
+            if (p == P - 1) off[e + 1] = run;   // expert total (inclusive scan below)
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        off[0] = 0;
+        toff[0] = 0;
+        for (int e = 0; e < a.E_local; ++e) {
+            const int32_t c = off[e + 1];
+            off[e + 1] = off[e] + c;
+            toff[e + 1] = toff[e] + (c + a.bm - 1) / a.bm;
+        }
+    }
+    __syncthreads();
+}
+
+// Copy one unit of up to kMoveRows consecutive rows [r0, r1) of the expert
+// buffer with all threads of the workgroup (8 loads in flight per thread),
+// first waiting for the source-chunk arrival flags of the unit's rows when
+// rows come from peers.  tok: LDS scratch of kMoveRows ints.
+__device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1, int *tok)
+{
+    const int nrows = r1 - r0;
+    __shared__ int ok_sh;
+    if (threadIdx.x < nrows) tok[threadIdx.x] = a.row_token_ws[r0 + threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int ok = 1, waited = -1;
+        if (a.fl.chunk_rows > 0) {
+            for (int i = 0; i < nrows && ok; ++i) {   // rows are in token order, so chunks ascend
+                const int t = tok[i];
+                const int sh = t / a.src.rows_per_src;
+                const int c = sh * a.fl.chunks_per_src + (t - sh * a.src.rows_per_src) / a.fl.chunk_rows;
+                if (c == waited) continue;
+                ok = wait_flag_eq(a.fl.ready + c, a.fl.epoch, &a.hdr->err, a.spin_limit,
+                                  0x20000000u | (uint32_t)c) ? 1 : 0;
+                waited = c;
+            }
+        }
+        ok_sh = ok;
+    }
+    __syncthreads();
+    if (!ok_sh) return false;
+    const int cpr = a.d / 8;   // 16-byte chunks per row
+    const int total = nrows * cpr;
+    for (int base = 0; base < total; base += 8 * (int)blockDim.x) {
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+            if (i < total) {
+                const int row = i / cpr;
+                v[j] = ((const uint4 *)token_row(a.src, tok[row], a.d))[i - row * cpr];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+            if (i < total) ((uint4 *)(a.x_perm + (size_t)r0 * a.d))[i] = v[j];
+        }
+    }
+    wait_vmem_all();   // this wave's stores have reached L2 before the release below
+    return true;
+}
+
+// The arrival simulator: releases chunk c at start + delay[c] microseconds,
+// copying the chunk's payload into the source buffer first if one is given.
+__device__ void fused_arrival_sim(const FusedArgs &a)
+{
+    const int n_chunks = a.src.S * a.fl.chunks_per_src;
+    const uint64_t per_us = a.ticks_per_us;
+    __shared__ uint64_t t0_sh;
+    __shared__ int next_sh;
+    if (threadIdx.x == 0) t0_sh = now_ticks();
+    __syncthreads();
+    const uint64_t t0 = t0_sh;
+    // release in order of due time; ties in chunk order
+    for (int released = 0; released < n_chunks; ++released) {
+        if (threadIdx.x == 0) {
+            int best = -1;
+            uint64_t best_due = ~0ull;
+            for (int c = 0; c < n_chunks; ++c) {
+                if (ld_relaxed(a.fl.ready + c) == a.fl.epoch) continue;
+                const uint64_t due = (uint64_t)a.fl.sim_delay_us[c] * per_us;
+                if (due < best_due) { best_due = due; best = c; }
+            }
+            const uint64_t lim = a.spin_limit;
+            while (best >= 0 && now_ticks() - t0 < best_due && now_ticks() - t0 < lim)
+                __builtin_amdgcn_s_sleep(8);
+            next_sh = best;
+        }
+        __syncthreads();
+        const int c = next_sh;
+        if (c < 0) break;
+        if (a.fl.has_payload) {
+            const int sh = c / a.fl.chunks_per_src;
+            const int r0 = (c % a.fl.chunks_per_src) * a.fl.chunk_rows;
+            const int r1 = min(a.src.rows_per_src, r0 + a.fl.chunk_rows);
+            const uint4 *s = (const uint4 *)(a.fl.sim_payload[sh] + (size_t)r0 * a.d);
+            uint4 *dst = (uint4 *)(a.src.p[sh] + (size_t)r0 * a.d);
+            const int n16 = (r1 - r0) * a.d / 8;
+            for (int i = threadIdx.x; i < n16; i += blockDim.x) dst[i] = s[i];
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) st_release(a.fl.ready + c, a.fl.epoch);
+        __syncthreads();
+    }
+}
+
+// off, toff: LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles in s0/s1.
+template <class C>
+__device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_t *off, int32_t *toff)
+{
+    const int w = blockIdx.x;
+    if (a.has_sim && w == (int)gridDim.x - 1) {
+        fused_arrival_sim(a);
+        return;
+    }
+    const int G = fused_participants(a);
+
+    // Every participant reads the barrier generation before its first arrival,
+    // so all of them agree on it; it does not change until all have arrived.
+    if (w == 0 && threadIdx.x < 8) a.xcd_next[threadIdx.x] = 0u;
+    for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x) a.tile_cnt[i] = 0u;
+
+    // ---- phase 1: router logits
+    if (!a.ids_in) {
+        fused_router_dispatch(a, w, G, (float *)s0);
+        if (!fused_barrier(a, 0x01000000u)) return;
+    }
+    // ---- phase 2: top-k + histogram + ranks per 64-token block
+    {
+        int32_t *ids_lds = (int32_t *)s0;
+        int32_t *cnt_lds = (int32_t *)(s0 + kTokBlock * kMaxK * 4);
+        for (int blk = w; blk < a.nblk; blk += G) {
+            if (!a.ids_in) {
+                topk_block(a.ta, blk, ids_lds);
+            } else {
+                const int base_t = blk * kTokBlock;
+                const int n_t = min(kTokBlock, a.T - base_t);
+                for (int i = threadIdx.x; i < n_t * a.k; i += blockDim.x) {
+                    const size_t o = (size_t)base_t * a.k + i;
+                    const int32_t id = a.ids_in[o];
+                    ids_lds[i] = id;
+                    a.ta.ids[o] = id;
+                    if (a.ids_user) a.ids_user[o] = id;
+                }
+            }
+            __syncthreads();
+            count_block(a.ca, blk, ids_lds, cnt_lds);
+        }
+    }
+    if (!fused_barrier(a, 0x02000000u)) return;
+
+    // ---- phase 3: scan (every workgroup), slots of own blocks
+    int32_t *cnt = (int32_t *)s0;                      // nblk * E_local (<= 64 KB)
+    int32_t *part = (int32_t *)s1;                     // 256
+    fused_scan(a, cnt, part, off, toff);
+    if (w == 0) {
+        for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
+            a.offsets[e] = off[e];
+            a.tile_off[e] = toff[e];
+        }
+        if (threadIdx.x == 0) {
+            a.hdr->R = (uint32_t)off[a.E_local];
+            a.hdr->n_tiles = (uint32_t)toff[a.E_local];
+        }
+    }
+    for (int blk = w; blk < a.nblk; blk += G) {
+        for (int i = threadIdx.x; i < kTokBlock * a.k; i += blockDim.x) {
+            const int t = blk * kTokBlock + i / a.k;
+            if (t >= a.T) break;
+            const size_t o = (size_t)t * a.k + (i % a.k);
+            const int le = a.ta.ids[o] - a.e_begin;
+            const int32_t rank = a.ca.lrank[o];
+            int32_t slot = -1;
+            if (le >= 0 && le < a.E_local && rank >= 0) {
+                slot = off[le] + cnt[blk * a.E_local + le] + rank;
+                if (slot < off[le + 1]) {
+                    a.row_token_ws[slot] = t;
+                    if (a.row_token_user) a.row_token_user[slot] = t;
+                } else {
+                    slot = -1;
+                }
+            }
+            a.slot_of[o] = slot;
+        }
+    }
+    if (!fused_barrier(a, 0x03000000u)) return;
+
+    const int n_tiles = toff[a.E_local];
+    const int R = off[a.E_local];
+    // ---- movers: unit u = (tile, row chunk), tile-major, dealt round-robin
+    __shared__ int mv_tok[kMoveRows];
+    if (w < a.n_mover) {
+        for (int e = 0, u = 0; e < a.E_local; ++e) {
+            for (int mt = 0; mt < toff[e + 1] - toff[e]; ++mt) {
+                const int tr0 = off[e] + mt * a.bm;
+                const int tr1 = min(off[e + 1], tr0 + a.bm);
+                for (int r0 = tr0; r0 < tr1; r0 += kMoveRows, ++u) {
+                    if (u % a.n_mover != w) continue;
+                    const bool ok = fused_move_unit(a, r0, min(tr1, r0 + kMoveRows), mv_tok);
+                    __syncthreads();
+                    if (!ok) return;
+                    if (threadIdx.x == 0)
+                        __hip_atomic_fetch_add(a.tile_cnt + toff[e] + mt, 1u, __ATOMIC_RELEASE,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    }
+    (void)R;
+    (void)n_tiles;
+
+    // ---- compute: per-XCD queues over chunks of CH consecutive tasks
+    const GemmArgs &g = a.ga;
+    const int NB = (g.N + C::BN - 1) / C::BN;
+    const int n_tasks = toff[a.E_local] * NB;
+    const int xcd = w % 8;
+    const int CH = (G + 7) / 8;
+    __shared__ int q_sh;
+    for (int o = 0; o < 8; ++o) {
+        const int x = (xcd + o) % 8;
+        for (;;) {
+            if (threadIdx.x == 0) {
+                const int i = (int)__hip_atomic_fetch_add(a.xcd_next + x, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                q_sh = (i / CH) * 8 * CH + x * CH + (i % CH);
+            }
+            __syncthreads();
+            const int q = q_sh;
+            __syncthreads();
+            if (q >= n_tasks) break;
+            // task q -> expert, column block, row tile (consecutive tasks share a W tile)
+            int lo = 0, hi = a.E_local;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (toff[mid] * NB <= q) lo = mid; else hi = mid;
+            }
+            const int e = lo;
+            const int nt = toff[e + 1] - toff[e];
+            const int rem = q - toff[e] * NB;
+            const int nb = rem / nt, mt = rem % nt;
+            const int cnt_e = off[e + 1] - off[e];
+            const int rows_valid = min(C::BM, cnt_e - mt * C::BM);
+            const int row0 = off[e] + mt * C::BM;
+            const uint32_t units = (uint32_t)((rows_valid + kMoveRows - 1) / kMoveRows);
+            if (threadIdx.x == 0)
+                // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
+                q_sh = wait_flag_geq(a.tile_cnt + toff[e] + mt, units, &a.hdr->err, 2 * a.spin_limit,
+                                     0x10000000u | (uint32_t)(toff[e] + mt)) ? 1 : 0;
+            __syncthreads();
+            const int ok = q_sh;
+            __syncthreads();
+            if (!ok) return;
+            gemm_tile_big<C>(g, e, row0, rows_valid, nb * C::BN, s0, s1);
+        }
+    }
+}
+
+}  // namespace mk

@@ -112,7 +112,9 @@ __device__ void gemm_tile_big(const GemmArgs &a, int e, int row0, int rows_valid
     const size_t w_first = (size_t)e * a.N + n0;
     const __amdgpu_buffer_rsrc_t wsrc =
         make_rsrc(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
-    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a.x_perm + (size_t)row0 * a.d, (size_t)C::BM * a.d * 2);
+    // Only the tile's valid rows are readable: rows past a ragged end return 0 without a memory access
+    // (they may belong to a tile that is not yet moved).
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a.x_perm + (size_t)row0 * a.d, (size_t)rows_valid * a.d * 2);
     const uint32_t row_bytes = (uint32_t)a.d * 2;
     const uint32_t lane_off = (uint32_t)(lane >> 3) * row_bytes + (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
     const int KT = a.d / C::BK;

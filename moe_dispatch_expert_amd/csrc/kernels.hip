@@ -3,6 +3,7 @@
 // persistent kernel, one launch per step.
 #include <hip/hip_runtime.h>
 
+#include "fused_dev.h"
 #include "gemm_dev.h"
 #include "layout_dev.h"
 #include "mk_launch.h"
@@ -71,6 +72,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
     __shared__ __attribute__((aligned(1024))) char s0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) char s1[C::STAGE];
     gemm_worker<C>(a, blockIdx.x, gridDim.x, s0, s1);
+}
+
+template <class C>
+__global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char s1[C::STAGE];
+    __shared__ int32_t off[1025], toff[1025];
+    fused_kernel_body<C>(a, s0, s1, off, toff);
 }
 
 // ---------------------------------------------------------------- wrappers
@@ -164,6 +174,22 @@ int gemm_max_grid(int bm, int bn)
             hipSuccess)
             return 0;
     }
+    return cus * per_cu;
+}
+
+hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s)
+{
+    void *args[] = {(void *)&a};
+    return hipLaunchCooperativeKernel((const void *)k_fused<Tile256>, dim3(grid), dim3(256), args, 0, s);
+}
+
+int fused_max_grid()
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<Tile256>, 256, 0) != hipSuccess)
+        return 0;
     return cus * per_cu;
 }
 

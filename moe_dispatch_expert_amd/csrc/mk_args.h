@@ -39,8 +39,9 @@ struct WsHeader {
     uint32_t bar_gen;      // grid barrier generation (grows by one per barrier)
     uint32_t n_tiles;      // GEMM row tiles of the current call
     uint32_t R;            // routed local rows of the current call
-    uint32_t call_epoch;   // value the current call's tile flags are released with
-    uint32_t pad[57];
+    uint32_t call_epoch;   // spare
+    uint32_t xcd_next[8];  // fused kernel: per-XCD GEMM task counters
+    uint32_t pad[49];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 

@@ -13,6 +13,7 @@ struct CountArgs;
 struct ScanArgs;
 struct SlotArgs;
 struct GemmArgs;
+struct FusedArgs;
 
 // Router logits; picks the lane layout from E and the tokens per lane from T.
 hipError_t launch_router_logits(const RouterArgs &a, hipStream_t s);
@@ -29,5 +30,8 @@ hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x
 hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s);
 // Largest co-resident grid of the GEMM kernel for this tile shape.
 int gemm_max_grid(int bm, int bn);
+// The persistent fused kernel (cooperative launch: the whole grid is co-resident).
+hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
+int fused_max_grid();
 
 }  // namespace mk
