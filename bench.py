@@ -82,6 +82,28 @@ def _traffic(workload: str, launch_bytes_alg: float):
     return t.get("bytes_per_launch")
 
 
+def trace_summary(tr: dict) -> dict:
+    """Phase boundaries of the fused kernel (max over workgroups, microseconds from the first start)."""
+    live = tr["start"] > 0
+    t0 = tr["start"][live].min()
+    us = lambda v: round(float(v - t0) / tr["ticks_per_us"], 2)
+    out = {}
+    for name in ("routed", "barrier_a", "counted", "barrier_b", "slots", "barrier_c", "moved", "done"):
+        v = tr[name][live]
+        v = v[v > 0]
+        if v.size:
+            out[name + "_max_us"] = us(v.max())
+    ft = tr["first_task"][live]
+    ft = ft[ft > 0]
+    if ft.size:
+        out["first_task_min_us"] = us(ft.min())
+        out["first_task_max_us"] = us(ft.max())
+    out["tasks_min_max"] = [int(tr["tasks"][live].min()), int(tr["tasks"][live].max())]
+    out["tile_wait_us_mean"] = round(float(tr["wait_ticks"][live].mean()) / tr["ticks_per_us"], 2)
+    out["xcc_of_wg0_to_7"] = [int(v) for v in tr["xcc"][:8]]
+    return out
+
+
 def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
     import oracle
     wl = inp["wl"]
@@ -117,6 +139,9 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace", action="store_true", help="add the fused kernel's phase timeline of the last step")
+    ap.add_argument("--staged", action="store_true", help="one launch per step instead of the fused kernel")
+    ap.add_argument("--movers", type=int, default=0, help="override the per-shape mover count")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (asked for --gpus {args.gpus}); run with --gpus 1",
@@ -148,8 +173,16 @@ def main():
     hip = _hip()
     evs = _events(hip, 2 * args.steps)
 
+    base_tune = {}
+    if args.staged:
+        base_tune["n_mover_wg"] = -1
+    elif args.movers:
+        base_tune["n_mover_wg"] = args.movers
+
     def step(i=None):
-        tune = None if i is None else {"ev_gemm_begin": evs[2 * i], "ev_gemm_end": evs[2 * i + 1]}
+        tune = dict(base_tune)
+        if i is not None:
+            tune.update({"ev_gemm_begin": evs[2 * i], "ev_gemm_end": evs[2 * i + 1]})
         mk.mk_dispatch_gemm(xs, we, wl.k, w_router=wr, bias=bias, topk_ids_in=ids_in, E=wl.E,
                             e_begin=wl.e_begin, workspace=ws, out=bufs, tune=tune)
 
@@ -204,6 +237,11 @@ def main():
         "roofline": roof,
         "torch": torch.__version__,
     }
+    if args.staged or args.movers:
+        rec["config"]["path"] = "staged" if args.staged else f"fused, {args.movers} movers"
+    if args.trace and not args.staged:
+        rec["trace"] = trace_summary(mk.mk_dispatch_gemm_trace(ws, wl.T, wl.d, wl.E, wl.k, wl.e_begin,
+                                                               wl.E_local, wl.N, wl.S))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, R)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)

@@ -145,6 +145,18 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src,
 /* The tuning the per-shape table picks (what a NULL/zero `tune` means). */
 mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out);
 
+/* Where the fused kernel's per-workgroup trace lives inside a dispatch
+ * workspace: *offset bytes from its start, *n_wg records of *words uint64
+ * each (record w = workgroup w).  Words, written by every fused call:
+ *   0 start, 1 router logits done, 2 barrier A passed, 3 histogram done,
+ *   4 barrier B passed, 5 slot map done, 6 barrier C passed, 7 mover role
+ *   done, 8 first GEMM task started, 9 workgroup done (wall-clock ticks,
+ *   *ticks_per_us per microsecond); 10 GEMM tasks run, 11 ticks spent
+ *   waiting for tiles, 12 hardware XCD id, 13 mover units copied.
+ * For profiling the overlap of the roles; the host reads it after a sync. */
+mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,
+                                  int32_t *words, int32_t *ticks_per_us);
+
 /* Synchronous: reads the device error word of a dispatch workspace (the caller
  * must have synchronised the stream).  Returns MK_OK, MK_ETIMEOUT or MK_EINVAL;
  * *detail (if non-NULL) receives which wait or id failed.  Clears the word. */

@@ -78,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.mk_select_tuning.restype = _c_i32
     lib.mk_poll_error.argtypes = [_vp, P(_c_i32)]
     lib.mk_poll_error.restype = _c_i32
+    lib.mk_dispatch_gemm_trace.argtypes = [P(MkShape), P(MkSources), P(ctypes.c_size_t), P(_c_i32), P(_c_i32),
+                                           P(_c_i32)]
+    lib.mk_dispatch_gemm_trace.restype = _c_i32
     _lib = lib
     return lib
 
@@ -162,6 +165,27 @@ def mk_select_tuning(T, d, E, k, e_begin, E_local, N) -> dict:
     out = MkTuning()
     _check(load().mk_select_tuning(ctypes.byref(shape), ctypes.byref(src), ctypes.byref(out)), "mk_select_tuning")
     return {f: getattr(out, f) for f in TUNING_INTS}
+
+
+TRACE_WORDS = ("start", "routed", "barrier_a", "counted", "barrier_b", "slots", "barrier_c", "moved",
+               "first_task", "done", "tasks", "wait_ticks", "xcc", "units")
+
+
+def mk_dispatch_gemm_trace(workspace: torch.Tensor, T, d, E, k, e_begin, E_local, N, S=1) -> dict:
+    """The fused kernel's per-workgroup trace records (mk_dispatch_gemm_trace) as int64 arrays, plus
+    ticks_per_us.  Synchronises first."""
+    shape = _shape(T, d, E, k, e_begin, E_local, N)
+    src = MkSources(S, T // max(S, 1), None, 0, None, 0, None, None)
+    off, n_wg, words, tpu = ctypes.c_size_t(), _c_i32(), _c_i32(), _c_i32()
+    _check(load().mk_dispatch_gemm_trace(ctypes.byref(shape), ctypes.byref(src), ctypes.byref(off),
+                                         ctypes.byref(n_wg), ctypes.byref(words), ctypes.byref(tpu)),
+           "mk_dispatch_gemm_trace")
+    torch.cuda.synchronize(workspace.device)
+    raw = workspace[off.value: off.value + n_wg.value * words.value * 8].view(torch.int64)
+    rec = raw.view(n_wg.value, words.value).cpu().numpy()
+    out = {name: rec[:, i] for i, name in enumerate(TRACE_WORDS)}
+    out["ticks_per_us"] = tpu.value
+    return out
 
 
 def mk_poll_error(workspace: torch.Tensor):

@@ -123,7 +123,7 @@ const char *mk_status_str(mk_status st)
 size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E)
 {
     if (T < 0 || E < 1) return 0;
-    return align256((size_t)T * E * 4) + 256;
+    return align256((size_t)kRouterSegments * T * E * 4) + 256;
 }
 
 mk_status mk_route_topk(const void *x, const float *w_router, const float *bias, int32_t T, int32_t d, int32_t E,
@@ -145,14 +145,14 @@ mk_status mk_route_topk(const void *x, const float *w_router, const float *bias,
     ra.src.S = 1;
     ra.src.rows_per_src = T;
     ra.wr = w_router;
-    ra.bias = bias;
-    ra.logits = (float *)workspace;
+    ra.part = (float *)workspace;
     ra.T = T;
     ra.d = d;
     ra.E = E;
-    if (launch_router_logits(ra, st) != hipSuccess) return MK_EHIP;
+    if (launch_router(ra, st) != hipSuccess) return MK_EHIP;
     TopkArgs ta{};
-    ta.logits = (const float *)workspace;
+    ta.part = (const float *)workspace;
+    ta.bias = bias;
     ta.ids = topk_ids;
     ta.ids_user = nullptr;
     ta.w_user = topk_w;
@@ -218,7 +218,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     hipStream_t hs = (hipStream_t)stream;
     char *ws = (char *)workspace;
     WsHeader *hdr = (WsHeader *)(ws + L.hdr);
-    float *logits = (float *)(ws + L.logits);
+    float *part = (float *)(ws + L.part);
     int32_t *ids = (int32_t *)(ws + L.ids);
     int32_t *lrank = (int32_t *)(ws + L.lrank);
     int32_t *blkcnt = (int32_t *)(ws + L.blkcnt);
@@ -234,12 +234,12 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         FusedArgs fa{};
         fa.ra.src = rows;
         fa.ra.wr = w_router;
-        fa.ra.bias = bias;
-        fa.ra.logits = logits;
+        fa.ra.part = part;
         fa.ra.T = s->T;
         fa.ra.d = s->d;
         fa.ra.E = s->E;
-        fa.ta.logits = logits;
+        fa.ta.part = part;
+        fa.ta.bias = bias;
         fa.ta.ids = ids;
         fa.ta.ids_user = topk_ids_out;
         fa.ta.w_user = topk_w_out;
@@ -300,16 +300,10 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.bm = tu.bm;
         fa.has_sim = (src->chunk_rows > 0 && src->sim_delay_us) ? 1 : 0;
         const int G = grid - fa.has_sim;
-        fa.router_el = s->E <= 8 ? 8 : 64;
-        {
-            const long g = kWave / fa.router_el;
-            const long neb = (s->E + fa.router_el - 1) / fa.router_el;
-            auto units = [&](long tpl) { return ((s->T + g * tpl - 1) / (g * tpl)) * neb; };
-            fa.router_tpl = units(16) >= 2L * G ? 16 : (units(4) >= G ? 4 : 1);
-        }
         fa.n_mover = tu.n_mover_wg < 1 ? 1 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);
         fa.max_tiles = L.max_tiles;
         fa.ticks_per_us = (uint32_t)ticks_per_us();
+        fa.trace = (uint64_t *)(ws + L.trace);
         if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
         if (launch_fused(fa, grid, hs) != hipSuccess) return MK_EHIP;
         if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
@@ -332,14 +326,14 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
             RouterArgs ra{};
             ra.src = rows;
             ra.wr = w_router;
-            ra.bias = bias;
-            ra.logits = logits;
+            ra.part = part;
             ra.T = s->T;
             ra.d = s->d;
             ra.E = s->E;
-            if (launch_router_logits(ra, hs) != hipSuccess) return MK_EHIP;
+            if (launch_router(ra, hs) != hipSuccess) return MK_EHIP;
             TopkArgs ta{};
-            ta.logits = logits;
+            ta.part = part;
+            ta.bias = bias;
             ta.ids = ids;
             ta.ids_user = topk_ids_out;
             ta.w_user = topk_w_out;
@@ -401,6 +395,20 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
     if (launch_gemm(ga, tu.bm, tu.bn, grid, hs) != hipSuccess) return MK_EHIP;
     if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
+    return MK_OK;
+}
+
+mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,
+                                  int32_t *words, int32_t *ticks_per_us_out)
+{
+    (void)src;
+    const mk_status st = check_shape(s);
+    if (st != MK_OK) return st;
+    const WsLayout L = ws_layout(s->T, s->d, s->E, s->k, s->E_local);
+    if (offset) *offset = L.trace;
+    if (n_wg) *n_wg = kTraceWGs;
+    if (words) *words = kTraceWords;
+    if (ticks_per_us_out) *ticks_per_us_out = ticks_per_us();
     return MK_OK;
 }
 

@@ -32,7 +32,7 @@
 
 namespace mk {
 
-constexpr int kMoveRows = 16;          // rows per mover work unit
+constexpr int kMoveRows = 32;          // rows per mover work unit
 constexpr int kMaxScanEntries = 16384; // nblk * E_local held in LDS by phase 3
 
 struct FusedArgs {
@@ -56,12 +56,23 @@ struct FusedArgs {
     WsHeader *hdr;
     uint64_t spin_limit;
     int32_t T, d, E, k, e_begin, E_local, nblk, bm;
-    int32_t router_el, router_tpl;
     int32_t n_mover;             // workgroups that start as movers
     int32_t has_sim;             // last workgroup is the arrival simulator
     int32_t max_tiles;
     uint32_t ticks_per_us;       // wall-clock ticks per microsecond
+    uint64_t *trace;             // [kTraceWGs][kTraceWords] per-workgroup phase stamps
 };
+
+// Trace record words (wall-clock ticks unless noted), written by thread 0.
+enum TraceWord {
+    kTrStart = 0, kTrRouted, kTrBarA, kTrCounted, kTrBarB, kTrSlots, kTrBarC, kTrMoved, kTrFirstTask,
+    kTrDone, kTrTasks /* count */, kTrWaitTicks, kTrXcc /* hardware XCC id */, kTrUnits /* count */
+};
+
+__device__ __forceinline__ void trace_put(const FusedArgs &a, int word, uint64_t v)
+{
+    if (threadIdx.x == 0 && blockIdx.x < kTraceWGs) a.trace[blockIdx.x * kTraceWords + word] = v;
+}
 
 __device__ __forceinline__ int fused_participants(const FusedArgs &a) { return (int)gridDim.x - a.has_sim; }
 
@@ -86,28 +97,6 @@ __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detai
     }
     __syncthreads();
     return ok_shared != 0;
-}
-
-template <int TPL, int EL>
-__device__ void fused_router_phase(const FusedArgs &a, int w, int G, float *lds)
-{
-    constexpr int TB = (kWave / EL) * TPL;
-    const int ntb = (a.T + TB - 1) / TB;
-    const int neb = (a.E + EL - 1) / EL;
-    for (int u = w; u < ntb * neb; u += G) router_logits_block<TPL, EL>(a.ra, u % ntb, u / ntb, lds);
-}
-
-__device__ void fused_router_dispatch(const FusedArgs &a, int w, int G, float *lds)
-{
-    if (a.router_el == 8) {
-        if (a.router_tpl == 1) fused_router_phase<1, 8>(a, w, G, lds);
-        else if (a.router_tpl == 4) fused_router_phase<4, 8>(a, w, G, lds);
-        else fused_router_phase<16, 8>(a, w, G, lds);
-    } else {
-        if (a.router_tpl == 1) fused_router_phase<1, 64>(a, w, G, lds);
-        else if (a.router_tpl == 4) fused_router_phase<4, 64>(a, w, G, lds);
-        else fused_router_phase<16, 64>(a, w, G, lds);
-    }
 }
 
 // Phase 3 in one workgroup: per-block exclusive bases for every local expert
@@ -185,10 +174,11 @@ __device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1, int *tok)
     if (!ok_sh) return false;
     const int cpr = a.d / 8;   // 16-byte chunks per row
     const int total = nrows * cpr;
-    for (int base = 0; base < total; base += 8 * (int)blockDim.x) {
-        uint4 v[8];
+    constexpr int kInFlight = 16;   // loads in flight per thread
+    for (int base = 0; base < total; base += kInFlight * (int)blockDim.x) {
+        uint4 v[kInFlight];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kInFlight; ++j) {
             const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
             if (i < total) {
                 const int row = i / cpr;
@@ -196,7 +186,7 @@ __device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1, int *tok)
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kInFlight; ++j) {
             const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
             if (i < total) ((uint4 *)(a.x_perm + (size_t)r0 * a.d))[i] = v[j];
         }
@@ -254,8 +244,11 @@ template <class C>
 __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_t *off, int32_t *toff)
 {
     const int w = blockIdx.x;
+    trace_put(a, kTrStart, now_ticks());
+    trace_put(a, kTrXcc, (uint64_t)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & 0xF));
     if (a.has_sim && w == (int)gridDim.x - 1) {
         fused_arrival_sim(a);
+        trace_put(a, kTrDone, now_ticks());
         return;
     }
     const int G = fused_participants(a);
@@ -267,16 +260,20 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
 
     // ---- phase 1: router logits
     if (!a.ids_in) {
-        fused_router_dispatch(a, w, G, (float *)s0);
+        const int units = router_units(a.T, a.E);
+        const int wave = threadIdx.x / kWave;
+        for (int u = w * 4 + wave; u < units; u += G * 4) router_unit(a.ra, u);
+        trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, 0x01000000u)) return;
+        trace_put(a, kTrBarA, now_ticks());
     }
     // ---- phase 2: top-k + histogram + ranks per 64-token block
     {
-        int32_t *ids_lds = (int32_t *)s0;
-        int32_t *cnt_lds = (int32_t *)(s0 + kTokBlock * kMaxK * 4);
+        int32_t *ids_lds = (int32_t *)s1;
+        int32_t *cnt_lds = (int32_t *)(s1 + kTokBlock * kMaxK * 4);
         for (int blk = w; blk < a.nblk; blk += G) {
             if (!a.ids_in) {
-                topk_block(a.ta, blk, ids_lds);
+                topk_block(a.ta, blk, (float *)s0, ids_lds);
             } else {
                 const int base_t = blk * kTokBlock;
                 const int n_t = min(kTokBlock, a.T - base_t);
@@ -292,7 +289,9 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
             count_block(a.ca, blk, ids_lds, cnt_lds);
         }
     }
+    trace_put(a, kTrCounted, now_ticks());
     if (!fused_barrier(a, 0x02000000u)) return;
+    trace_put(a, kTrBarB, now_ticks());
 
     // ---- phase 3: scan (every workgroup), slots of own blocks
     int32_t *cnt = (int32_t *)s0;                      // nblk * E_local (<= 64 KB)
@@ -328,12 +327,15 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
             a.slot_of[o] = slot;
         }
     }
+    trace_put(a, kTrSlots, now_ticks());
     if (!fused_barrier(a, 0x03000000u)) return;
+    trace_put(a, kTrBarC, now_ticks());
 
     const int n_tiles = toff[a.E_local];
     const int R = off[a.E_local];
     // ---- movers: unit u = (tile, row chunk), tile-major, dealt round-robin
     __shared__ int mv_tok[kMoveRows];
+    uint64_t n_units = 0;
     if (w < a.n_mover) {
         for (int e = 0, u = 0; e < a.E_local; ++e) {
             for (int mt = 0; mt < toff[e + 1] - toff[e]; ++mt) {
@@ -347,12 +349,16 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
                     if (threadIdx.x == 0)
                         __hip_atomic_fetch_add(a.tile_cnt + toff[e] + mt, 1u, __ATOMIC_RELEASE,
                                                __HIP_MEMORY_SCOPE_AGENT);
+                    ++n_units;
                 }
             }
         }
     }
     (void)R;
     (void)n_tiles;
+    trace_put(a, kTrMoved, now_ticks());
+    trace_put(a, kTrUnits, n_units);
+    uint64_t n_done = 0, wait_ticks = 0;
 
     // ---- compute: per-XCD queues over chunks of CH consecutive tasks
     const GemmArgs &g = a.ga;
@@ -387,6 +393,8 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
             const int rows_valid = min(C::BM, cnt_e - mt * C::BM);
             const int row0 = off[e] + mt * C::BM;
             const uint32_t units = (uint32_t)((rows_valid + kMoveRows - 1) / kMoveRows);
+            if (n_done == 0) trace_put(a, kTrFirstTask, now_ticks());
+            const uint64_t tw0 = now_ticks();
             if (threadIdx.x == 0)
                 // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
                 q_sh = wait_flag_geq(a.tile_cnt + toff[e] + mt, units, &a.hdr->err, 2 * a.spin_limit,
@@ -395,9 +403,14 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
             const int ok = q_sh;
             __syncthreads();
             if (!ok) return;
+            wait_ticks += now_ticks() - tw0;
             gemm_tile_big<C>(g, e, row0, rows_valid, nb * C::BN, s0, s1);
+            ++n_done;
         }
     }
+    trace_put(a, kTrDone, now_ticks());
+    trace_put(a, kTrTasks, n_done);
+    trace_put(a, kTrWaitTicks, wait_ticks);
 }
 
 }  // namespace mk

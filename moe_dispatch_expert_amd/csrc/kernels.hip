@@ -11,19 +11,19 @@
 
 namespace mk {
 
-template <int TPL, int EL>
-__global__ __launch_bounds__(256) void k_router_logits(RouterArgs a)
+// One router work unit per wave.
+__global__ __launch_bounds__(256) void k_router(RouterArgs a, int units)
 {
-    __shared__ float lds[kRouterSegments * (kWave / EL) * TPL * EL];
-    router_logits_block<TPL, EL>(a, blockIdx.x, blockIdx.y, lds);
+    const int u = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (u < units) router_unit(a, u);
 }
 
 __global__ __launch_bounds__(256) void k_topk(TopkArgs ta, CountArgs ca, int do_count)
 {
+    __shared__ float lg[16384];
     __shared__ int32_t ids_lds[kTokBlock * kMaxK];
     __shared__ int32_t cnt_lds[1024];
-    topk_block(ta, blockIdx.x, ids_lds);
-    __syncthreads();
+    topk_block(ta, blockIdx.x, lg, ids_lds);
     if (do_count) count_block(ca, blockIdx.x, ids_lds, cnt_lds);
 }
 
@@ -85,35 +85,11 @@ __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
 
 // ---------------------------------------------------------------- wrappers
 
-template <int TPL, int EL>
-static hipError_t router_go(const RouterArgs &a, hipStream_t s)
+hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 {
-    constexpr int TB = (kWave / EL) * TPL;
-    dim3 grid((a.T + TB - 1) / TB, (a.E + EL - 1) / EL);
-    hipLaunchKernelGGL((k_router_logits<TPL, EL>), grid, dim3(256), 0, s, a);
+    const int units = router_units(a.T, a.E);
+    hipLaunchKernelGGL(k_router, dim3((units + 3) / 4), dim3(256), 0, s, a, units);
     return hipGetLastError();
-}
-
-template <int EL>
-static hipError_t router_pick_tpl(const RouterArgs &a, hipStream_t s)
-{
-    // Most tokens per lane (reuse of each Wr load) that still gives >= 256 blocks.
-    const long eb = (a.E + EL - 1) / EL;
-    const long g = kWave / EL;
-    auto blocks = [&](long tpl) { return ((a.T + g * tpl - 1) / (g * tpl)) * eb; };
-    if (blocks(16) >= 256) return router_go<16, EL>(a, s);
-    if (blocks(8) >= 256) return router_go<8, EL>(a, s);
-    if (blocks(4) >= 256) return router_go<4, EL>(a, s);
-    if (blocks(2) >= 256) return router_go<2, EL>(a, s);
-    return router_go<1, EL>(a, s);
-}
-
-hipError_t launch_router_logits(const RouterArgs &a, hipStream_t s)
-{
-    if (a.E <= 8) return router_pick_tpl<8>(a, s);
-    if (a.E <= 16) return router_pick_tpl<16>(a, s);
-    if (a.E <= 32) return router_pick_tpl<32>(a, s);
-    return router_pick_tpl<64>(a, s);
 }
 
 hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s)

@@ -46,8 +46,11 @@ struct WsHeader {
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace segments (all 256-byte aligned).
+constexpr int kTraceWGs = 1024;   // workgroups the trace segment has room for
+constexpr int kTraceWords = 16;   // uint64 records per workgroup
+
 struct WsLayout {
-    size_t hdr, logits, ids, lrank, blkcnt, blkbase, tile_off, tile_flag, row_token, x_perm, total;
+    size_t hdr, part, ids, lrank, blkcnt, blkbase, tile_off, tile_flag, row_token, trace, x_perm, total;
     int32_t nblk, max_tiles, r_cap, x_perm_rows;
 };
 
@@ -62,7 +65,7 @@ inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_
     L.x_perm_rows = L.r_cap + 256;   // a full tile past the last row stays in bounds
     size_t o = 0;
     L.hdr = o;       o += align256(sizeof(WsHeader));
-    L.logits = o;    o += align256((size_t)T * E * 4);
+    L.part = o;      o += align256((size_t)kRouterSegments * T * E * 4);
     L.ids = o;       o += align256((size_t)T * k * 4);
     L.lrank = o;     o += align256((size_t)T * k * 4);
     L.blkcnt = o;    o += align256((size_t)L.nblk * E_local * 4);
@@ -70,6 +73,7 @@ inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_
     L.tile_off = o;  o += align256((size_t)(E_local + 1) * 4);
     L.tile_flag = o; o += align256((size_t)L.max_tiles * 4);
     L.row_token = o; o += align256((size_t)(L.r_cap + 1) * 4);
+    L.trace = o;     o += align256((size_t)kTraceWGs * kTraceWords * 8);
     L.x_perm = o;    o += align256((size_t)L.x_perm_rows * d * 2);
     L.total = o;
     return L;

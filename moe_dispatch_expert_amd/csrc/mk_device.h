@@ -1,7 +1,6 @@
 // mk_device.h -- device-side building blocks shared by the libmk kernels
-// (gfx950 only): bf16 conversions, ordered top-k keys, wave reductions,
-// agent-scope acquire/release flags with bounded waits, and a grid barrier for
-// co-resident (cooperatively launched) grids.
+// (gfx950 only): bf16 conversions, ordered top-k keys, wave reductions, and
+// agent-scope flags with bounded waits.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -103,66 +102,53 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t code, uint32
         __hip_atomic_store(err + 1, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void fence_acquire_agent()
+{
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 // Spin (one lane per wave calls this) until *flag == want, with sleeps; gives
 // up after `limit` wall-clock ticks or as soon as another wave raised an error.
-// Returns true when the flag was seen (acquire), false on give-up.
+// Polls with relaxed loads (no cache invalidation per poll) and orders the
+// caller's later loads after the flag with one acquire fence once it is seen.
+// Returns true when the flag was seen, false on give-up.
 __device__ __forceinline__ bool wait_flag_eq(const uint32_t *flag, uint32_t want, uint32_t *err,
                                              uint64_t limit, uint32_t detail)
 {
-    if (ld_acquire(flag) == want) return true;
-    const uint64_t t0 = now_ticks();
-    for (;;) {
-        __builtin_amdgcn_s_sleep(2);
-        if (ld_acquire(flag) == want) return true;
-        if (ld_relaxed(err) != 0) return false;
-        if (now_ticks() - t0 > limit) {
-            raise_error(err, kErrTimeout, detail);
-            return false;
+    if (ld_relaxed(flag) != want) {
+        const uint64_t t0 = now_ticks();
+        for (;;) {
+            __builtin_amdgcn_s_sleep(2);
+            if (ld_relaxed(flag) == want) break;
+            if (ld_relaxed(err) != 0) return false;
+            if (now_ticks() - t0 > limit) {
+                raise_error(err, kErrTimeout, detail);
+                return false;
+            }
         }
     }
+    fence_acquire_agent();
+    return true;
 }
 
 // Same, for "value >= want" on a monotonically growing counter (wrap-safe compare).
 __device__ __forceinline__ bool wait_flag_geq(const uint32_t *flag, uint32_t want, uint32_t *err,
                                               uint64_t limit, uint32_t detail)
 {
-    if ((int32_t)(ld_acquire(flag) - want) >= 0) return true;
-    const uint64_t t0 = now_ticks();
-    for (;;) {
-        __builtin_amdgcn_s_sleep(2);
-        if ((int32_t)(ld_acquire(flag) - want) >= 0) return true;
-        if (ld_relaxed(err) != 0) return false;
-        if (now_ticks() - t0 > limit) {
-            raise_error(err, kErrTimeout, detail);
-            return false;
+    if ((int32_t)(ld_relaxed(flag) - want) < 0) {
+        const uint64_t t0 = now_ticks();
+        for (;;) {
+            __builtin_amdgcn_s_sleep(2);
+            if ((int32_t)(ld_relaxed(flag) - want) >= 0) break;
+            if (ld_relaxed(err) != 0) return false;
+            if (now_ticks() - t0 > limit) {
+                raise_error(err, kErrTimeout, detail);
+                return false;
+            }
         }
     }
-}
-
-// Grid barrier for a co-resident grid.  `count` returns to 0 after every
-// barrier and `gen` grows by one, so the words are reusable across launches
-// without a reset.  Every workgroup must call it the same number of times.
-// Returns false if the wait gave up (error raised); callers then skip work.
-__device__ __forceinline__ bool grid_barrier(uint32_t *count, uint32_t *gen, uint32_t *err,
-                                             uint64_t limit, uint32_t detail)
-{
-    __syncthreads();
-    __shared__ int ok_shared;
-    if (threadIdx.x == 0) {
-        const uint32_t g = ld_acquire(gen);
-        const uint32_t arrived =
-            __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        bool ok = true;
-        if (arrived == gridDim.x * gridDim.y * gridDim.z) {
-            __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            st_release(gen, g + 1u);
-        } else {
-            ok = wait_flag_eq(gen, g + 1u, err, limit, detail);
-        }
-        ok_shared = ok ? 1 : 0;
-    }
-    __syncthreads();
-    return ok_shared != 0;
+    fence_acquire_agent();
+    return true;
 }
 
 }  // namespace mk

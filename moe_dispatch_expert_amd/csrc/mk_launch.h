@@ -15,8 +15,8 @@ struct SlotArgs;
 struct GemmArgs;
 struct FusedArgs;
 
-// Router logits; picks the lane layout from E and the tokens per lane from T.
-hipError_t launch_router_logits(const RouterArgs &a, hipStream_t s);
+// Router partial sums, one unit per wave (router_units).
+hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 // Top-k + gate for all tokens; with do_count also the per-block histogram and ranks.
 hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s);
 // Histogram and ranks of caller-given ids (copied into the workspace id array).

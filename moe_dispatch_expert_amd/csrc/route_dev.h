@@ -1,6 +1,7 @@
-// route_dev.h -- router device code: fp32 logits in the fixed segmented order,
-// top-k selection with ordered keys, softmax gate, and the per-block expert
-// histogram with in-block ranks from wave ballots.
+// route_dev.h -- router device code: fp32 logits in the fixed segmented order
+// (per-segment partial sums, then an ordered sum), top-k selection, softmax
+// gate, and the per-block expert histogram with in-block ranks from wave
+// ballots.
 //
 // Token routing is the first half of the "MoE Dispatch+GEMM" kernel named in
 // "mKernel UCCL fuses NVLink/RDMA/compute into one persistent CUDA kernel"
@@ -20,8 +21,7 @@ namespace mk {
 struct RouterArgs {
     SrcRows src;
     const float *wr;    // [d, E]
-    const float *bias;  // [E] or nullptr
-    float *logits;      // [T, E]
+    float *part;        // [8, E, T] per-segment partial sums
     int32_t T, d, E;
 };
 
@@ -31,142 +31,320 @@ __device__ __forceinline__ const uint16_t *token_row(const SrcRows &s, int t, in
     return s.p[sh] + (size_t)(t - sh * s.rows_per_src) * d;
 }
 
-// One block of 256 threads computes logits for TB = (64/EL)*TPL tokens x EL
-// experts.  Wave w runs the chains of segments w and w+4; lane = (token group
-// g, expert e).  Partials meet in LDS and are added in segment order.
-// lds: 8 * TB * EL floats.
-template <int TPL, int EL>
-__device__ void router_logits_block(const RouterArgs &a, int tb, int eb, float *lds)
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8])
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        f[2 * p] = __uint_as_float(w[p] << 16);
+        f[2 * p + 1] = __uint_as_float(w[p] & 0xFFFF0000u);
+    }
+}
+
+// Wave-uniform reads go through the constant address space so that they become
+// scalar loads into SGPRs (the buffers are read-only while a kernel runs).
+typedef const __attribute__((address_space(4))) float cfloat_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) u32x4_t cu32x4_t;
+
+// Work units of the partial-sum phase, one per wave.  Lane = token (E <= 64,
+// EG experts per wave with EG | E, Wr rows uniform across the wave) or lane =
+// expert (E > 64, TPL tokens per wave, token rows uniform across the wave).
+constexpr int kRouterTPL = 4;
+
+__host__ __device__ inline int router_eg(int E)
+{
+    for (int eg = 16; eg > 1; eg >>= 1)
+        if (E % eg == 0) return eg;
+    return 1;
+}
+
+__host__ __device__ inline int router_units(int T, int E)
+{
+    if (E <= 64) return ((T + 63) / 64) * kRouterSegments * (E / router_eg(E));
+    return ((T + kRouterTPL - 1) / kRouterTPL) * kRouterSegments * ((E + 63) / 64);
+}
+
+// One wave computes partial sums of one K segment s:
+//   part[s][e][t] = fma chain over i in segment s, ascending (fp32, one rounding per step).
+// Chunks of 8 elements fetched per batch; the next batch is loaded while the
+// current one is consumed, since the fused kernel runs one wave per SIMD and
+// only in-flight loads hide memory latency.
+constexpr int kRouterPF = 8;
+
+template <int EG>
+__device__ void router_unit_tok(const RouterArgs &a, int unit)
 {
 #pragma clang fp contract(off)
-    constexpr int G = kWave / EL;
-    constexpr int TB = G * TPL;
-    const int w = threadIdx.x / kWave;
-    const int l = threadIdx.x % kWave;
-    const int el = l % EL;
-    const int g = l / EL;
-    const int e = eb * EL + el;
-    const int ec = e < a.E ? e : a.E - 1;   // idle lanes compute a real column, then drop it
+    const int lane = threadIdx.x % kWave;
+    const int neg = a.E / EG;
+    const int eg = unit % neg;
+    const int s = (unit / neg) % kRouterSegments;
+    const int tg = unit / (neg * kRouterSegments);
     const int seg = a.d / kRouterSegments;
-    const int s0 = w, s1 = w + 4;
-
-    const uint16_t *xr[TPL];
+    const int nch = seg / 8;
+    const int t = tg * kWave + lane;
+    const uint4 *xr = (const uint4 *)(token_row(a.src, t < a.T ? t : a.T - 1, a.d) + s * seg);
+    cfloat_t *wb = (cfloat_t *)(a.wr + (size_t)(s * seg) * a.E + eg * EG);
+    float acc[EG];
 #pragma unroll
-    for (int j = 0; j < TPL; ++j) {
-        int t = tb * TB + g * TPL + j;
-        t = t < a.T ? t : a.T - 1;
-        xr[j] = token_row(a.src, t, a.d);
-    }
-    float acc0[TPL], acc1[TPL];
+    for (int j = 0; j < EG; ++j) acc[j] = 0.0f;
+    uint4 nxt[kRouterPF];
 #pragma unroll
-    for (int j = 0; j < TPL; ++j) { acc0[j] = 0.0f; acc1[j] = 0.0f; }
-
-    const float *w0 = a.wr + (size_t)(s0 * seg) * a.E + ec;
-    const float *w1 = a.wr + (size_t)(s1 * seg) * a.E + ec;
-    for (int c = 0; c < seg; c += 8) {
-        float wa[8], wb[8];
+    for (int p = 0; p < kRouterPF; ++p) nxt[p] = p < nch ? xr[p] : make_uint4(0, 0, 0, 0);
+    for (int cb = 0; cb < nch; cb += kRouterPF) {
+        uint4 cur[kRouterPF];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            wa[q] = w0[(size_t)(c + q) * a.E];
-            wb[q] = w1[(size_t)(c + q) * a.E];
+        for (int p = 0; p < kRouterPF; ++p) {
+            cur[p] = nxt[p];
+            nxt[p] = cb + kRouterPF + p < nch ? xr[cb + kRouterPF + p] : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < TPL; ++j) {
-            const uint4 xa = *(const uint4 *)(xr[j] + s0 * seg + c);
-            const uint4 xb = *(const uint4 *)(xr[j] + s1 * seg + c);
-            const uint32_t va[4] = {xa.x, xa.y, xa.z, xa.w};
-            const uint32_t vb[4] = {xb.x, xb.y, xb.z, xb.w};
+        for (int p = 0; p < kRouterPF; ++p) {
+            if (cb + p >= nch) break;
+            float xf[8];
+            unpack8(cur[p], xf);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                acc0[j] = __builtin_fmaf(__uint_as_float(va[p] << 16), wa[2 * p], acc0[j]);
-                acc0[j] = __builtin_fmaf(__uint_as_float(va[p] & 0xFFFF0000u), wa[2 * p + 1], acc0[j]);
-                acc1[j] = __builtin_fmaf(__uint_as_float(vb[p] << 16), wb[2 * p], acc1[j]);
-                acc1[j] = __builtin_fmaf(__uint_as_float(vb[p] & 0xFFFF0000u), wb[2 * p + 1], acc1[j]);
+            for (int q = 0; q < 8; ++q) {
+                cfloat_t *wrow = wb + (size_t)((cb + p) * 8 + q) * a.E;
+#pragma unroll
+                for (int j = 0; j < EG; ++j) acc[j] = __builtin_fmaf(xf[q], wrow[j], acc[j]);
             }
         }
     }
+    if (t < a.T) {
+#pragma unroll
+        for (int j = 0; j < EG; ++j) a.part[((size_t)s * a.E + eg * EG + j) * a.T + t] = acc[j];
+    }
+}
+
+template <int TPL>
+__device__ void router_unit_exp(const RouterArgs &a, int unit)
+{
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x % kWave;
+    const int neb = (a.E + 63) / 64;
+    const int eb = unit % neb;
+    const int s = (unit / neb) % kRouterSegments;
+    const int tb = unit / (neb * kRouterSegments);
+    const int seg = a.d / kRouterSegments;
+    const int nch = seg / 8;
+    const int e = eb * 64 + lane;
+    const float *wc = a.wr + (size_t)(s * seg) * a.E + (e < a.E ? e : a.E - 1);
+    cu32x4_t *xr[TPL];
 #pragma unroll
     for (int j = 0; j < TPL; ++j) {
-        lds[(s0 * TB + g * TPL + j) * EL + el] = acc0[j];
-        lds[(s1 * TB + g * TPL + j) * EL + el] = acc1[j];
+        const int t = tb * TPL + j;
+        xr[j] = (cu32x4_t *)(token_row(a.src, t < a.T ? t : a.T - 1, a.d) + s * seg);
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < TB * EL; idx += blockDim.x) {
-        const int tt = idx / EL, ee = idx % EL;
-        const int t = tb * TB + tt, e2 = eb * EL + ee;
-        if (t < a.T && e2 < a.E) {
-            float v = lds[tt * EL + ee];
+    float acc[TPL];
 #pragma unroll
-            for (int s = 1; s < kRouterSegments; ++s)
-                v = v + lds[(s * TB + tt) * EL + ee];
-            if (a.bias) v = v + a.bias[e2];
-            a.logits[(size_t)t * a.E + e2] = v;
+    for (int j = 0; j < TPL; ++j) acc[j] = 0.0f;
+    constexpr int PF = kRouterPF / 2;
+    float nxt[PF][8];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) nxt[p][q] = p < nch ? wc[(size_t)(p * 8 + q) * a.E] : 0.0f;
+    for (int cb = 0; cb < nch; cb += PF) {
+        float cur[PF][8];
+#pragma unroll
+        for (int p = 0; p < PF; ++p)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                cur[p][q] = nxt[p][q];
+                nxt[p][q] = cb + PF + p < nch ? wc[(size_t)((cb + PF + p) * 8 + q) * a.E] : 0.0f;
+            }
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            if (cb + p >= nch) break;
+#pragma unroll
+            for (int j = 0; j < TPL; ++j) {
+                float xf[8];
+                const u32x4_t xv = xr[j][cb + p];
+                unpack8(make_uint4(xv.x, xv.y, xv.z, xv.w), xf);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[j] = __builtin_fmaf(xf[q], cur[p][q], acc[j]);
+            }
         }
     }
-    __syncthreads();
+    if (e < a.E) {
+#pragma unroll
+        for (int j = 0; j < TPL; ++j) {
+            const int t = tb * TPL + j;
+            if (t < a.T) a.part[((size_t)s * a.E + e) * a.T + t] = acc[j];
+        }
+    }
+}
+
+__device__ __forceinline__ void router_unit(const RouterArgs &a, int unit)
+{
+    unit = __builtin_amdgcn_readfirstlane(unit);   // one unit per wave: keeps the uniform reads scalar
+    if (a.E > 64) {
+        router_unit_exp<kRouterTPL>(a, unit);
+        return;
+    }
+    switch (router_eg(a.E)) {
+    case 16: router_unit_tok<16>(a, unit); break;
+    case 8: router_unit_tok<8>(a, unit); break;
+    case 4: router_unit_tok<4>(a, unit); break;
+    case 2: router_unit_tok<2>(a, unit); break;
+    default: router_unit_tok<1>(a, unit); break;
+    }
 }
 
 struct TopkArgs {
-    const float *logits;     // [T, E]
+    const float *part;       // [8, E, T] partial sums
+    const float *bias;       // [E] or nullptr
     int32_t *ids;            // [T, k]  (workspace or user)
     int32_t *ids_user;       // [T, k] or nullptr (second copy)
     float *w_user;           // [T, k] or nullptr
     int32_t T, E, k;
 };
 
-// Top-k and gate for tokens [blk*64, blk*64 + 64): wave w handles 16 tokens,
-// lanes span the experts.  Writes ids into ids_lds[64][k] too.
-__device__ __forceinline__ void topk_block(const TopkArgs &a, int blk, int32_t *ids_lds)
+// Tokens per LDS sub-block of the top-k step: SB * (E + 1) floats fit in 64 KiB.
+__host__ __device__ inline int topk_subblock(int E)
+{
+    int sb = kTokBlock;
+    while (sb > 1 && (long)sb * (E + 1) * 4 > 65536) sb >>= 1;
+    return sb;
+}
+
+// Logits of tokens [t0, t0 + nt) into LDS: lg[tl * (E + 1) + e] = ((P0 + P1) + ... + P7) + bias.
+// Each thread keeps the 8 partial loads of 4 logits in flight.
+__device__ __forceinline__ void block_logits(const TopkArgs &a, int t0, int nt, float *lg)
+{
+#pragma clang fp contract(off)
+    const int n = nt * a.E;
+    const size_t sstride = (size_t)a.E * a.T;
+    for (int base = 0; base < n; base += 4 * (int)blockDim.x) {
+        float p[4][kRouterSegments];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = base + u * (int)blockDim.x + (int)threadIdx.x;
+            const int i2 = idx < n ? idx : n - 1;
+            const float *src = a.part + (size_t)(i2 / nt) * a.T + t0 + i2 % nt;
+#pragma unroll
+            for (int s = 0; s < kRouterSegments; ++s) p[u][s] = src[s * sstride];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = base + u * (int)blockDim.x + (int)threadIdx.x;
+            if (idx >= n) break;
+            const int tl = idx % nt, e = idx / nt;
+            float v = p[u][0];
+#pragma unroll
+            for (int s = 1; s < kRouterSegments; ++s) v = v + p[u][s];
+            if (a.bias) v = v + a.bias[e];
+            lg[tl * (a.E + 1) + e] = v;
+        }
+    }
+}
+
+// Top-k and gate for one token whose E logits are in `row` (LDS), lane = token
+// (E <= 64): a sequential selection over ascending ids, where a strict '>'
+// keeps the lower id on ties (and -0 ties with +0, as float compare does).
+// The chosen ids go to ids_row (LDS, k entries).
+__device__ __forceinline__ void topk_one_lane(const TopkArgs &a, const float *row, int t, int32_t *ids_row)
+{
+    float lv[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) lv[e] = e < a.E ? row[e] : 0.0f;
+    uint64_t taken = 0;
+    float top = 0.0f;
+    for (int j = 0; j < a.k; ++j) {
+        int best = -1;
+        float bl = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) {
+            if (e < a.E && !((taken >> e) & 1ull) && (best < 0 || lv[e] > bl)) {
+                best = e;
+                bl = lv[e];
+            }
+        }
+        taken |= 1ull << best;
+        if (j == 0) top = bl;
+        ids_row[j] = best;
+        const size_t o = (size_t)t * a.k + j;
+        a.ids[o] = best;
+        if (a.ids_user) a.ids_user[o] = best;
+    }
+    if (a.w_user) {
+        float zsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e)
+            if (e < a.E) zsum += expf(lv[e] - top);
+        for (int j = 0; j < a.k; ++j) a.w_user[(size_t)t * a.k + j] = expf(row[ids_row[j]] - top) / zsum;
+    }
+}
+
+// Top-k for one token with lanes spanning the experts (E > 64): k rounds of a
+// wave-wide max over (logit, -id) keys.
+__device__ __forceinline__ void topk_one_wave(const TopkArgs &a, const float *row, int t, int32_t *ids_row)
 {
     constexpr int kMaxV = 16;   // E <= 1024
-    const int w = threadIdx.x / kWave;
     const int l = threadIdx.x % kWave;
     const int nv = (a.E + kWave - 1) / kWave;
-    for (int tt = 0; tt < 16; ++tt) {
-        const int tl = w * 16 + tt;
-        const int t = blk * kTokBlock + tl;
-        if (t >= a.T) break;
-        const float *lrow = a.logits + (size_t)t * a.E;
-        float lv[kMaxV];
-        uint64_t key[kMaxV];
+    float lv[kMaxV];
+    uint64_t key[kMaxV];
 #pragma unroll
-        for (int v = 0; v < kMaxV; ++v) {
-            const int e = l + v * kWave;
-            const bool ok = v < nv && e < a.E;
-            lv[v] = ok ? lrow[e] : 0.0f;
-            key[v] = ok ? topk_key(lv[v], e) : 0ull;
-        }
-        float top_logit = 0.0f;
-        float zsum = 0.0f;
-        float sel_logit = 0.0f;   // lane j (< k) keeps the logit of the j-th choice
-        int sel_id = 0;
-        for (int j = 0; j < a.k; ++j) {
-            uint64_t best = 0;
+    for (int v = 0; v < kMaxV; ++v) {
+        const int e = l + v * kWave;
+        const bool ok = v < nv && e < a.E;
+        lv[v] = ok ? row[e] : 0.0f;
+        key[v] = ok ? topk_key(lv[v], e) : 0ull;
+    }
+    float top_logit = 0.0f, zsum = 0.0f, sel_logit = 0.0f;
+    int sel_id = 0;
+    for (int j = 0; j < a.k; ++j) {
+        uint64_t best = 0;
 #pragma unroll
-            for (int v = 0; v < kMaxV; ++v) best = key[v] > best ? key[v] : best;
-            best = wave_max_u64(best);
-            const int e = topk_key_expert(best);
+        for (int v = 0; v < kMaxV; ++v) best = key[v] > best ? key[v] : best;
+        best = wave_max_u64(best);
+        const int e = topk_key_expert(best);
 #pragma unroll
-            for (int v = 0; v < kMaxV; ++v)
-                if (key[v] == best) key[v] = 0ull;
-            const uint32_t ok = (uint32_t)(best >> 32);
-            const float logit = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
-            if (j == 0) top_logit = logit;
-            if (l == j) { sel_logit = logit; sel_id = e; }
-        }
+        for (int v = 0; v < kMaxV; ++v)
+            if (key[v] == best) key[v] = 0ull;
+        const uint32_t ok = (uint32_t)(best >> 32);
+        const float logit = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
+        if (j == 0) top_logit = logit;
+        if (l == j) { sel_logit = logit; sel_id = e; }
+    }
 #pragma unroll
-        for (int v = 0; v < kMaxV; ++v) {
-            const int e = l + v * kWave;
-            if (v < nv && e < a.E) zsum += expf(lv[v] - top_logit);
+    for (int v = 0; v < kMaxV; ++v) {
+        const int e = l + v * kWave;
+        if (v < nv && e < a.E) zsum += expf(lv[v] - top_logit);
+    }
+    zsum = wave_sum_f32(zsum);
+    if (l < a.k) {
+        const size_t o = (size_t)t * a.k + l;
+        a.ids[o] = sel_id;
+        if (a.ids_user) a.ids_user[o] = sel_id;
+        if (a.w_user) a.w_user[o] = expf(sel_logit - top_logit) / zsum;
+        ids_row[l] = sel_id;
+    }
+}
+
+// Top-k and gate for tokens [blk*64, blk*64 + 64), in sub-blocks whose logits
+// are first gathered into LDS (lg: 64 KiB).  ids_lds: [64][k] (LDS).
+__device__ void topk_block(const TopkArgs &a, int blk, float *lg, int32_t *ids_lds)
+{
+    const int w = threadIdx.x / kWave;
+    const int l = threadIdx.x % kWave;
+    const int sb = topk_subblock(a.E);
+    const int t_end = min(a.T, (blk + 1) * kTokBlock);
+    for (int t0 = blk * kTokBlock; t0 < t_end; t0 += sb) {
+        const int nt = min(sb, t_end - t0);
+        block_logits(a, t0, nt, lg);
+        __syncthreads();
+        if (a.E <= 64) {
+            if (w == 0 && l < nt)
+                topk_one_lane(a, lg + l * (a.E + 1), t0 + l, ids_lds + (t0 - blk * kTokBlock + l) * a.k);
+        } else {
+            for (int tl = w; tl < nt; tl += (int)blockDim.x / kWave)
+                topk_one_wave(a, lg + tl * (a.E + 1), t0 + tl, ids_lds + (t0 - blk * kTokBlock + tl) * a.k);
         }
-        zsum = wave_sum_f32(zsum);
-        if (l < a.k) {
-            const size_t o = (size_t)t * a.k + l;
-            a.ids[o] = sel_id;
-            if (a.ids_user) a.ids_user[o] = sel_id;
-            if (a.w_user) a.w_user[o] = expf(sel_logit - top_logit) / zsum;
-            if (ids_lds) ids_lds[tl * a.k + l] = sel_id;
-        }
+        __syncthreads();
     }
 }
 
