@@ -298,6 +298,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.E_local = s->E_local;
         fa.nblk = L.nblk;
         fa.bm = tu.bm;
+        static_assert(256 % kMoveRows == 0, "mover units tile the GEMM row tiles");
         fa.has_sim = (src->chunk_rows > 0 && src->sim_delay_us) ? 1 : 0;
         const int G = grid - fa.has_sim;
         fa.n_mover = tu.n_mover_wg < 1 ? 1 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);

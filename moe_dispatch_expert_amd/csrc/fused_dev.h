@@ -66,7 +66,8 @@ struct FusedArgs {
 // Trace record words (wall-clock ticks unless noted), written by thread 0.
 enum TraceWord {
     kTrStart = 0, kTrRouted, kTrBarA, kTrCounted, kTrBarB, kTrSlots, kTrBarC, kTrMoved, kTrFirstTask,
-    kTrDone, kTrTasks /* count */, kTrWaitTicks, kTrXcc /* hardware XCC id */, kTrUnits /* count */
+    kTrDone, kTrTasks /* count */, kTrWaitTicks, kTrXcc /* hardware XCC id */, kTrUnits /* count */,
+    kTrCopyTicks, kTrReleaseTicks
 };
 
 __device__ __forceinline__ void trace_put(const FusedArgs &a, int word, uint64_t v)
@@ -103,7 +104,8 @@ __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detai
 // (into LDS and, for the blocks this workgroup owns, into the workspace),
 // expert offsets and tile prefix (LDS).  cnt: nblk*E_local ints; part: 256 ints;
 // off/toff: E_local+1 ints each.
-__device__ void fused_scan(const FusedArgs &a, int32_t *cnt, int32_t *part, int32_t *off, int32_t *toff)
+__device__ void fused_scan(const FusedArgs &a, int32_t *cnt, int32_t *part, int32_t *off, int32_t *toff,
+                           int32_t *uoff)
 {
     const int n = a.nblk * a.E_local;
     for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = a.ca.blkcnt[i];
@@ -136,30 +138,29 @@ __device__ void fused_scan(const FusedArgs &a, int32_t *cnt, int32_t *part, int3
     if (threadIdx.x == 0) {
         off[0] = 0;
         toff[0] = 0;
+        uoff[0] = 0;
         for (int e = 0; e < a.E_local; ++e) {
             const int32_t c = off[e + 1];
             off[e + 1] = off[e] + c;
             toff[e + 1] = toff[e] + (c + a.bm - 1) / a.bm;
+            uoff[e + 1] = uoff[e] + (c + kMoveRows - 1) / kMoveRows;   // mover units of kMoveRows rows
         }
     }
     __syncthreads();
 }
 
 // Copy one unit of up to kMoveRows consecutive rows [r0, r1) of the expert
-// buffer with all threads of the workgroup (8 loads in flight per thread),
-// first waiting for the source-chunk arrival flags of the unit's rows when
-// rows come from peers.  tok: LDS scratch of kMoveRows ints.
-__device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1, int *tok)
+// buffer, one row per wave at a time, first waiting for the source-chunk
+// arrival flags of the unit's rows when rows come from peers.
+__device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1)
 {
     const int nrows = r1 - r0;
     __shared__ int ok_sh;
-    if (threadIdx.x < nrows) tok[threadIdx.x] = a.row_token_ws[r0 + threadIdx.x];
-    __syncthreads();
     if (threadIdx.x == 0) {
         int ok = 1, waited = -1;
         if (a.fl.chunk_rows > 0) {
             for (int i = 0; i < nrows && ok; ++i) {   // rows are in token order, so chunks ascend
-                const int t = tok[i];
+                const int t = a.row_token_ws[r0 + i];
                 const int sh = t / a.src.rows_per_src;
                 const int c = sh * a.fl.chunks_per_src + (t - sh * a.src.rows_per_src) / a.fl.chunk_rows;
                 if (c == waited) continue;
@@ -172,25 +173,9 @@ __device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1, int *tok)
     }
     __syncthreads();
     if (!ok_sh) return false;
-    const int cpr = a.d / 8;   // 16-byte chunks per row
-    const int total = nrows * cpr;
-    constexpr int kInFlight = 16;   // loads in flight per thread
-    for (int base = 0; base < total; base += kInFlight * (int)blockDim.x) {
-        uint4 v[kInFlight];
-#pragma unroll
-        for (int j = 0; j < kInFlight; ++j) {
-            const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
-            if (i < total) {
-                const int row = i / cpr;
-                v[j] = ((const uint4 *)token_row(a.src, tok[row], a.d))[i - row * cpr];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kInFlight; ++j) {
-            const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
-            if (i < total) ((uint4 *)(a.x_perm + (size_t)r0 * a.d))[i] = v[j];
-        }
-    }
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    for (int r = r0 + wave; r < r1; r += (int)blockDim.x / kWave) move_row(a.src, a.row_token_ws, a.x_perm, a.d, r, lane);
     wait_vmem_all();   // this wave's stores have reached L2 before the release below
     return true;
 }
@@ -239,9 +224,10 @@ __device__ void fused_arrival_sim(const FusedArgs &a)
     }
 }
 
-// off, toff: LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles in s0/s1.
+// off, toff, uoff: LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles in s0/s1.
 template <class C>
-__device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_t *off, int32_t *toff)
+__device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_t *off, int32_t *toff,
+                                  int32_t *uoff)
 {
     const int w = blockIdx.x;
     trace_put(a, kTrStart, now_ticks());
@@ -261,8 +247,7 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
     // ---- phase 1: router logits
     if (!a.ids_in) {
         const int units = router_units(a.T, a.E);
-        const int wave = threadIdx.x / kWave;
-        for (int u = w * 4 + wave; u < units; u += G * 4) router_unit(a.ra, u);
+        for (int u = w; u < units; u += G) router_unit(a.ra, u, s0, s1);
         trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
@@ -296,7 +281,7 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
     // ---- phase 3: scan (every workgroup), slots of own blocks
     int32_t *cnt = (int32_t *)s0;                      // nblk * E_local (<= 64 KB)
     int32_t *part = (int32_t *)s1;                     // 256
-    fused_scan(a, cnt, part, off, toff);
+    fused_scan(a, cnt, part, off, toff, uoff);
     if (w == 0) {
         for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
             a.offsets[e] = off[e];
@@ -333,31 +318,40 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
 
     const int n_tiles = toff[a.E_local];
     const int R = off[a.E_local];
-    // ---- movers: unit u = (tile, row chunk), tile-major, dealt round-robin
-    __shared__ int mv_tok[kMoveRows];
-    uint64_t n_units = 0;
+    // ---- movers: unit u = kMoveRows rows of one expert (tile-major, since bm % kMoveRows == 0),
+    // dealt round-robin over the movers
+    uint64_t n_units = 0, copy_ticks = 0, release_ticks = 0;
     if (w < a.n_mover) {
-        for (int e = 0, u = 0; e < a.E_local; ++e) {
-            for (int mt = 0; mt < toff[e + 1] - toff[e]; ++mt) {
-                const int tr0 = off[e] + mt * a.bm;
-                const int tr1 = min(off[e + 1], tr0 + a.bm);
-                for (int r0 = tr0; r0 < tr1; r0 += kMoveRows, ++u) {
-                    if (u % a.n_mover != w) continue;
-                    const bool ok = fused_move_unit(a, r0, min(tr1, r0 + kMoveRows), mv_tok);
-                    __syncthreads();
-                    if (!ok) return;
-                    if (threadIdx.x == 0)
-                        __hip_atomic_fetch_add(a.tile_cnt + toff[e] + mt, 1u, __ATOMIC_RELEASE,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                    ++n_units;
-                }
+        const int n_units_all = uoff[a.E_local];
+        for (int u = w; u < n_units_all; u += a.n_mover) {
+            int lo = 0, hi = a.E_local;   // expert e with uoff[e] <= u < uoff[e+1]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (uoff[mid] <= u) lo = mid; else hi = mid;
             }
+            const int e = lo;
+            const int q = u - uoff[e];
+            const int r0 = off[e] + q * kMoveRows;
+            const int r1 = min(off[e + 1], r0 + kMoveRows);
+            const int mt = (q * kMoveRows) / a.bm;
+            const uint64_t c0 = now_ticks();
+            const bool ok = fused_move_unit(a, r0, r1);
+            __syncthreads();
+            if (!ok) return;
+            const uint64_t c1 = now_ticks();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(a.tile_cnt + toff[e] + mt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            copy_ticks += c1 - c0;
+            release_ticks += now_ticks() - c1;
+            ++n_units;
         }
     }
     (void)R;
     (void)n_tiles;
     trace_put(a, kTrMoved, now_ticks());
     trace_put(a, kTrUnits, n_units);
+    trace_put(a, kTrCopyTicks, copy_ticks);
+    trace_put(a, kTrReleaseTicks, release_ticks);
     uint64_t n_done = 0, wait_ticks = 0;
 
     // ---- compute: per-XCD queues over chunks of CH consecutive tasks

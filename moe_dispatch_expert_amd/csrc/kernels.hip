@@ -11,11 +11,11 @@
 
 namespace mk {
 
-// One router work unit per wave.
-__global__ __launch_bounds__(256) void k_router(RouterArgs a, int units)
+// One router work unit per workgroup.
+__global__ __launch_bounds__(256) void k_router(RouterArgs a)
 {
-    const int u = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (u < units) router_unit(a, u);
+    __shared__ __attribute__((aligned(16))) char st0[40960], st1[40960];
+    router_unit(a, blockIdx.x, st0, st1);
 }
 
 __global__ __launch_bounds__(256) void k_topk(TopkArgs ta, CountArgs ca, int do_count)
@@ -79,16 +79,15 @@ __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char s0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) char s1[C::STAGE];
-    __shared__ int32_t off[1025], toff[1025];
-    fused_kernel_body<C>(a, s0, s1, off, toff);
+    __shared__ int32_t off[1025], toff[1025], uoff[1025];
+    fused_kernel_body<C>(a, s0, s1, off, toff, uoff);
 }
 
 // ---------------------------------------------------------------- wrappers
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 {
-    const int units = router_units(a.T, a.E);
-    hipLaunchKernelGGL(k_router, dim3((units + 3) / 4), dim3(256), 0, s, a, units);
+    hipLaunchKernelGGL(k_router, dim3(router_units(a.T, a.E)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -96,14 +96,44 @@ __device__ __forceinline__ void slot_one(const SlotArgs &a, int i)
     a.slot_of[i] = slot;
 }
 
-// Copy one expert-buffer row r: x_perm[r] = x[row_token[r]], 16 bytes per lane.
+typedef unsigned int cp_u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) cp_u32x4_t gcuint4_t;
+typedef __attribute__((address_space(1))) cp_u32x4_t guint4_t;
+
+// Copy one row of d bf16 (cpr = d / 8 chunks of 16 bytes) with one wave: every
+// lane first loads all of its chunks (clamped indices, so the loads are
+// unconditional and in flight together), then stores them.  CPL = chunks per
+// lane, a compile-time bound (cpr <= 64 * CPL).
+template <int CPL>
+__device__ __forceinline__ void copy_row_wave(const uint16_t *src_row, uint16_t *dst_row, int cpr, int lane)
+{
+    gcuint4_t *s = (gcuint4_t *)src_row;
+    guint4_t *d = (guint4_t *)dst_row;
+    cp_u32x4_t v[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) v[i] = s[min(lane + kWave * i, cpr - 1)];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        if (lane + kWave * i < cpr) d[lane + kWave * i] = v[i];
+}
+
+__device__ __forceinline__ void copy_row(const uint16_t *src_row, uint16_t *dst_row, int d, int lane)
+{
+    const int cpr = d / 8;
+    if (cpr <= 4 * kWave) copy_row_wave<4>(src_row, dst_row, cpr, lane);
+    else if (cpr <= 8 * kWave) copy_row_wave<8>(src_row, dst_row, cpr, lane);
+    else if (cpr <= 16 * kWave) copy_row_wave<16>(src_row, dst_row, cpr, lane);
+    else
+        for (int c0 = 0; c0 < cpr; c0 += 16 * kWave)
+            copy_row_wave<16>(src_row + (size_t)c0 * 8, dst_row + (size_t)c0 * 8, min(cpr - c0, 16 * kWave),
+                              lane);
+}
+
+// Copy one expert-buffer row r: x_perm[r] = x[row_token[r]].
 __device__ __forceinline__ void move_row(const SrcRows &src, const int32_t *row_token, uint16_t *x_perm,
                                          int d, int r, int lane)
 {
-    const uint4 *s = (const uint4 *)token_row(src, row_token[r], d);
-    uint4 *dst = (uint4 *)(x_perm + (size_t)r * d);
-    const int n16 = d / 8;
-    for (int c = lane; c < n16; c += kWave) dst[c] = s[c];
+    copy_row(token_row(src, row_token[r], d), x_perm + (size_t)r * d, d, lane);
 }
 
 }  // namespace mk

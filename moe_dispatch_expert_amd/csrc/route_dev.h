@@ -41,156 +41,150 @@ __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8])
     }
 }
 
-// Wave-uniform reads go through the constant address space so that they become
-// scalar loads into SGPRs (the buffers are read-only while a kernel runs).
-typedef const __attribute__((address_space(4))) float cfloat_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(4))) u32x4_t cu32x4_t;
+// ---------------------------------------------------------------- partial sums
+// part[s][e][t] = fma chain over i in K segment s, ascending (fp32, one rounding
+// per step).  Each of the 8 segments is an independent small SIMT GEMM
+// [T x seg] . [seg x E]; one workgroup unit = (segment, block of BT tokens,
+// block of BE experts), staged through LDS in K chunks of KC with the next
+// chunk prefetched into registers; thread (ty, tx) owns TT tokens x TE experts
+// and walks k in ascending order, so every accumulator is one chain.
+struct RouterCfg {
+    int BE, TE, TT, BT;
+};
 
-// Work units of the partial-sum phase, one per wave.  Lane = token (E <= 64,
-// EG experts per wave with EG | E, Wr rows uniform across the wave) or lane =
-// expert (E > 64, TPL tokens per wave, token rows uniform across the wave).
-constexpr int kRouterTPL = 4;
-
-__host__ __device__ inline int router_eg(int E)
+__host__ __device__ inline RouterCfg router_cfg(int E)
 {
-    for (int eg = 16; eg > 1; eg >>= 1)
-        if (E % eg == 0) return eg;
-    return 1;
+    if (E <= 8) return RouterCfg{8, 8, 1, 256};
+    if (E <= 16) return RouterCfg{16, 8, 1, 128};
+    if (E <= 32) return RouterCfg{32, 8, 2, 128};
+    if (E <= 64) return RouterCfg{64, 8, 4, 128};
+    return RouterCfg{64, 4, 1, 16};
 }
 
 __host__ __device__ inline int router_units(int T, int E)
 {
-    if (E <= 64) return ((T + 63) / 64) * kRouterSegments * (E / router_eg(E));
-    return ((T + kRouterTPL - 1) / kRouterTPL) * kRouterSegments * ((E + 63) / 64);
+    const RouterCfg c = router_cfg(E);
+    return ((T + c.BT - 1) / c.BT) * ((E + c.BE - 1) / c.BE) * kRouterSegments;
 }
 
-// One wave computes partial sums of one K segment s:
-//   part[s][e][t] = fma chain over i in segment s, ascending (fp32, one rounding per step).
-// Chunks of 8 elements fetched per batch; the next batch is loaded while the
-// current one is consumed, since the fused kernel runs one wave per SIMD and
-// only in-flight loads hide memory latency.
-constexpr int kRouterPF = 8;
+constexpr int kRouterKC = 64;   // K chunk per LDS stage (a smaller divisor of the segment if needed)
 
-template <int EG>
-__device__ void router_unit_tok(const RouterArgs &a, int unit)
+template <int BE, int TE, int TT>
+__device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, char *lds1)
 {
 #pragma clang fp contract(off)
-    const int lane = threadIdx.x % kWave;
-    const int neg = a.E / EG;
-    const int eg = unit % neg;
-    const int s = (unit / neg) % kRouterSegments;
-    const int tg = unit / (neg * kRouterSegments);
+    constexpr int NX = BE / TE;            // threads along the experts
+    constexpr int NY = 256 / NX;           // threads along the tokens
+    constexpr int BT = NY * TT;
+    constexpr int XCH = BT * kRouterKC / 8;              // 16-byte x chunks per stage (max)
+    constexpr int XPT = (XCH + 255) / 256;               // per thread
+    constexpr int WPT = (kRouterKC * BE + 255) / 256;    // W floats per thread per stage (max)
     const int seg = a.d / kRouterSegments;
-    const int nch = seg / 8;
-    const int t = tg * kWave + lane;
-    const uint4 *xr = (const uint4 *)(token_row(a.src, t < a.T ? t : a.T - 1, a.d) + s * seg);
-    cfloat_t *wb = (cfloat_t *)(a.wr + (size_t)(s * seg) * a.E + eg * EG);
-    float acc[EG];
+    const int KC = seg % kRouterKC == 0 ? kRouterKC : (seg % 32 == 0 ? 32 : 16);
+    const int ntb = (a.T + BT - 1) / BT;
+    const int neb = (a.E + BE - 1) / BE;
+    const int tb = unit % ntb;
+    const int eb = (unit / ntb) % neb;
+    const int s = unit / (ntb * neb);
+    const int tid = threadIdx.x;
+    const int tx = tid % NX, ty = tid / NX;
+    const int k_base = s * seg;
+
+    // stage layout: x tile [BT][kRouterKC] bf16, then W tile [kRouterKC][BE] fp32
+    constexpr int XBYTES = BT * kRouterKC * 2;
+    const int cpr = KC / 8;
+    uint4 xr[XPT];
+    float wrg[WPT];
+#define MK_ROUTER_FETCH(k0)                                                                       \
+    do {                                                                                          \
+        _Pragma("unroll") for (int j = 0; j < XPT; ++j) {                                         \
+            const int c = min(tid + j * 256, BT * cpr - 1);                                       \
+            const int row = c / cpr, cc = c - row * cpr;                                          \
+            const int t = min(tb * BT + row, a.T - 1);                                            \
+            xr[j] = *(const uint4 *)(token_row(a.src, t, a.d) + k_base + (k0) + cc * 8);          \
+        }                                                                                         \
+        _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                         \
+            const int c = min(tid + j * 256, KC * BE - 1);                                        \
+            const int kk = c / BE, e = c - kk * BE;                                               \
+            wrg[j] = a.wr[(size_t)(k_base + (k0) + kk) * a.E + min(eb * BE + e, a.E - 1)];        \
+        }                                                                                         \
+    } while (0)
+#define MK_ROUTER_STASH(st)                                                                       \
+    do {                                                                                          \
+        _Pragma("unroll") for (int j = 0; j < XPT; ++j) {                                         \
+            const int c = tid + j * 256;                                                          \
+            if (c < BT * cpr)                                                                     \
+                *(uint4 *)((uint16_t *)(st) + (c / cpr) * kRouterKC + (c % cpr) * 8) = xr[j];     \
+        }                                                                                         \
+        _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                         \
+            const int c = tid + j * 256;                                                          \
+            if (c < KC * BE) ((float *)((st) + XBYTES))[c] = wrg[j];                              \
+        }                                                                                         \
+    } while (0)
+
+    float acc[TT][TE];
 #pragma unroll
-    for (int j = 0; j < EG; ++j) acc[j] = 0.0f;
-    uint4 nxt[kRouterPF];
+    for (int i = 0; i < TT; ++i)
 #pragma unroll
-    for (int p = 0; p < kRouterPF; ++p) nxt[p] = p < nch ? xr[p] : make_uint4(0, 0, 0, 0);
-    for (int cb = 0; cb < nch; cb += kRouterPF) {
-        uint4 cur[kRouterPF];
+        for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
+
+    MK_ROUTER_FETCH(0);
+    MK_ROUTER_STASH(lds0);
+    __syncthreads();
+    const int nk = seg / KC;
+    for (int kc = 0; kc < nk; ++kc) {
+        char *cur = (kc & 1) ? lds1 : lds0;
+        char *nxt = (kc & 1) ? lds0 : lds1;
+        if (kc + 1 < nk) MK_ROUTER_FETCH((kc + 1) * KC);
+        const uint16_t *xt = (const uint16_t *)cur;
+        const float *wt = (const float *)(cur + XBYTES);
+        for (int k8 = 0; k8 < KC; k8 += 8) {
+            float xf[TT][8];
 #pragma unroll
-        for (int p = 0; p < kRouterPF; ++p) {
-            cur[p] = nxt[p];
-            nxt[p] = cb + kRouterPF + p < nch ? xr[cb + kRouterPF + p] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int p = 0; p < kRouterPF; ++p) {
-            if (cb + p >= nch) break;
-            float xf[8];
-            unpack8(cur[p], xf);
+            for (int i = 0; i < TT; ++i) unpack8(*(const uint4 *)(xt + (ty * TT + i) * kRouterKC + k8), xf[i]);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                cfloat_t *wrow = wb + (size_t)((cb + p) * 8 + q) * a.E;
+                float wv[TE];
 #pragma unroll
-                for (int j = 0; j < EG; ++j) acc[j] = __builtin_fmaf(xf[q], wrow[j], acc[j]);
+                for (int j = 0; j < TE; j += 4) {
+                    const float4 w4 = *(const float4 *)(wt + (k8 + q) * BE + tx * TE + j);
+                    wv[j] = w4.x;
+                    wv[j + 1] = w4.y;
+                    wv[j + 2] = w4.z;
+                    wv[j + 3] = w4.w;
+                }
+#pragma unroll
+                for (int i = 0; i < TT; ++i)
+#pragma unroll
+                    for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xf[i][q], wv[j], acc[i][j]);
             }
         }
+        if (kc + 1 < nk) MK_ROUTER_STASH(nxt);
+        __syncthreads();
     }
-    if (t < a.T) {
+#undef MK_ROUTER_FETCH
+#undef MK_ROUTER_STASH
 #pragma unroll
-        for (int j = 0; j < EG; ++j) a.part[((size_t)s * a.E + eg * EG + j) * a.T + t] = acc[j];
+    for (int i = 0; i < TT; ++i) {
+        const int t = tb * BT + ty * TT + i;
+        if (t >= a.T) continue;
+#pragma unroll
+        for (int j = 0; j < TE; ++j) {
+            const int e = eb * BE + tx * TE + j;
+            if (e < a.E) a.part[((size_t)s * a.E + e) * a.T + t] = acc[i][j];
+        }
     }
 }
 
-template <int TPL>
-__device__ void router_unit_exp(const RouterArgs &a, int unit)
+// One workgroup unit of the partial-sum phase; lds0/lds1: two stages of at
+// least 40 KiB each.
+__device__ __forceinline__ void router_unit(const RouterArgs &a, int unit, char *lds0, char *lds1)
 {
-#pragma clang fp contract(off)
-    const int lane = threadIdx.x % kWave;
-    const int neb = (a.E + 63) / 64;
-    const int eb = unit % neb;
-    const int s = (unit / neb) % kRouterSegments;
-    const int tb = unit / (neb * kRouterSegments);
-    const int seg = a.d / kRouterSegments;
-    const int nch = seg / 8;
-    const int e = eb * 64 + lane;
-    const float *wc = a.wr + (size_t)(s * seg) * a.E + (e < a.E ? e : a.E - 1);
-    cu32x4_t *xr[TPL];
-#pragma unroll
-    for (int j = 0; j < TPL; ++j) {
-        const int t = tb * TPL + j;
-        xr[j] = (cu32x4_t *)(token_row(a.src, t < a.T ? t : a.T - 1, a.d) + s * seg);
-    }
-    float acc[TPL];
-#pragma unroll
-    for (int j = 0; j < TPL; ++j) acc[j] = 0.0f;
-    constexpr int PF = kRouterPF / 2;
-    float nxt[PF][8];
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) nxt[p][q] = p < nch ? wc[(size_t)(p * 8 + q) * a.E] : 0.0f;
-    for (int cb = 0; cb < nch; cb += PF) {
-        float cur[PF][8];
-#pragma unroll
-        for (int p = 0; p < PF; ++p)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                cur[p][q] = nxt[p][q];
-                nxt[p][q] = cb + PF + p < nch ? wc[(size_t)((cb + PF + p) * 8 + q) * a.E] : 0.0f;
-            }
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            if (cb + p >= nch) break;
-#pragma unroll
-            for (int j = 0; j < TPL; ++j) {
-                float xf[8];
-                const u32x4_t xv = xr[j][cb + p];
-                unpack8(make_uint4(xv.x, xv.y, xv.z, xv.w), xf);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) acc[j] = __builtin_fmaf(xf[q], cur[p][q], acc[j]);
-            }
-        }
-    }
-    if (e < a.E) {
-#pragma unroll
-        for (int j = 0; j < TPL; ++j) {
-            const int t = tb * TPL + j;
-            if (t < a.T) a.part[((size_t)s * a.E + e) * a.T + t] = acc[j];
-        }
-    }
-}
-
-__device__ __forceinline__ void router_unit(const RouterArgs &a, int unit)
-{
-    unit = __builtin_amdgcn_readfirstlane(unit);   // one unit per wave: keeps the uniform reads scalar
-    if (a.E > 64) {
-        router_unit_exp<kRouterTPL>(a, unit);
-        return;
-    }
-    switch (router_eg(a.E)) {
-    case 16: router_unit_tok<16>(a, unit); break;
-    case 8: router_unit_tok<8>(a, unit); break;
-    case 4: router_unit_tok<4>(a, unit); break;
-    case 2: router_unit_tok<2>(a, unit); break;
-    default: router_unit_tok<1>(a, unit); break;
-    }
+    if (a.E <= 8) router_unit_tiled<8, 8, 1>(a, unit, lds0, lds1);
+    else if (a.E <= 16) router_unit_tiled<16, 8, 1>(a, unit, lds0, lds1);
+    else if (a.E <= 32) router_unit_tiled<32, 8, 2>(a, unit, lds0, lds1);
+    else if (a.E <= 64) router_unit_tiled<64, 8, 4>(a, unit, lds0, lds1);
+    else router_unit_tiled<64, 4, 1>(a, unit, lds0, lds1);
 }
 
 struct TopkArgs {
