@@ -42,7 +42,7 @@ enum {
 };
 
 /* Problem shape.  Local experts are [e_begin, e_begin + E_local) of the E
- * global experts the router scores.  Requires T >= 0, d > 0, d % 64 == 0,
+ * global experts the router scores.  Requires T >= 0, d > 0, d % 128 == 0,
  * 1 <= k <= E <= 1024, 0 <= e_begin, e_begin + E_local <= E, N > 0, N % 8 == 0. */
 typedef struct {
     int32_t T, d, E, k, e_begin, E_local, N;
