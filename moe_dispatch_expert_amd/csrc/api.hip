@@ -96,7 +96,7 @@ mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
     mk_tuning t{};
     t.bm = 256;
     t.bn = 256;
-    t.bk = 64;
+    t.bk = BigTile<256, 256>::BK;
     t.n_mover_wg = (src && src->chunk_rows > 0) ? 64 : 256;
     t.n_compute_wg = 0;   // 0: every co-resident workgroup
     (void)s;
@@ -202,7 +202,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
 
     mk_tuning tu = table_tuning(s, src);
     if (tune && (tune->bm || tune->bn || tune->bk || tune->n_mover_wg || tune->n_compute_wg)) {
-        if ((tune->bm && tune->bm != 256) || (tune->bn && tune->bn != 256) || (tune->bk && tune->bk != 64))
+        if ((tune->bm && tune->bm != 256) || (tune->bn && tune->bn != 256) || (tune->bk && tune->bk != BigTile<256, 256>::BK))
             return MK_EUNSUPPORTED;
         if (tune->n_mover_wg) tu.n_mover_wg = tune->n_mover_wg;
         tu.n_compute_wg = tune->n_compute_wg;

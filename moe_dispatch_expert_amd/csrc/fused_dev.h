@@ -33,7 +33,8 @@
 namespace mk {
 
 constexpr int kMoveRows = 32;          // rows per mover work unit
-constexpr int kMaxScanEntries = 16384; // nblk * E_local held in LDS by phase 3
+constexpr int kScanHalf = 8192;       // ints per LDS array in phase 3
+constexpr int kMaxScanEntries = 2 * kScanHalf; // nblk * E_local held in LDS by phase 3
 
 struct FusedArgs {
     RouterArgs ra;
@@ -102,9 +103,18 @@ __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detai
 
 // Phase 3 in one workgroup: per-block exclusive bases for every local expert
 // (into LDS and, for the blocks this workgroup owns, into the workspace),
-// expert offsets and tile prefix (LDS).  cnt: nblk*E_local ints; part: 256 ints;
-// off/toff: E_local+1 ints each.
-__device__ void fused_scan(const FusedArgs &a, int32_t *cnt, int32_t *part, int32_t *off, int32_t *toff,
+// expert offsets and tile prefix (LDS).  The nblk*E_local counts live in two
+// LDS arrays of kScanHalf ints (entry i in cnt0[i] or cnt1[i - kScanHalf]);
+// part: 256 ints; off/toff/uoff: E_local+1 ints each.
+struct ScanLds {
+    int32_t *cnt0, *cnt1;
+    __device__ __forceinline__ int32_t &operator[](int i) const
+    {
+        return i < kScanHalf ? cnt0[i] : cnt1[i - kScanHalf];
+    }
+};
+
+__device__ void fused_scan(const FusedArgs &a, const ScanLds &cnt, int32_t *part, int32_t *off, int32_t *toff,
                            int32_t *uoff)
 {
     const int n = a.nblk * a.E_local;
@@ -152,7 +162,7 @@ __device__ void fused_scan(const FusedArgs &a, int32_t *cnt, int32_t *part, int3
 // Copy one unit of up to kMoveRows consecutive rows [r0, r1) of the expert
 // buffer, one row per wave at a time, first waiting for the source-chunk
 // arrival flags of the unit's rows when rows come from peers.
-__device__ bool fused_move_unit(const FusedArgs &a, int r0, int r1)
+__device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, int r0, int r1)
 {
     const int nrows = r1 - r0;
     __shared__ int ok_sh;
@@ -224,10 +234,12 @@ __device__ void fused_arrival_sim(const FusedArgs &a)
     }
 }
 
-// off, toff, uoff: LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles in s0/s1.
+// st / ls: the four GEMM stage arrays (32 KiB each; ls holds their LDS-space
+// addresses for the GEMM), also used by the earlier phases; off, toff, uoff:
+// LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
 template <class C>
-__device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_t *off, int32_t *toff,
-                                  int32_t *uoff)
+__device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], const LdsStages &ls, int32_t *off,
+                                  int32_t *toff, int32_t *uoff)
 {
     const int w = blockIdx.x;
     trace_put(a, kTrStart, now_ticks());
@@ -247,18 +259,18 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
     // ---- phase 1: router logits
     if (!a.ids_in) {
         const int units = router_units(a.T, a.E);
-        for (int u = w; u < units; u += G) router_unit(a.ra, u, s0, s1);
+        for (int u = w; u < units; u += G) router_unit(a.ra, u, st[0], st[2], st[1], st[3]);
         trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
     }
     // ---- phase 2: top-k + histogram + ranks per 64-token block
     {
-        int32_t *ids_lds = (int32_t *)s1;
-        int32_t *cnt_lds = (int32_t *)(s1 + kTokBlock * kMaxK * 4);
+        int32_t *ids_lds = (int32_t *)st[1];                          // 8 KiB
+        int32_t *cnt_lds = (int32_t *)(st[1] + kTokBlock * kMaxK * 4);  // E_local ints
         for (int blk = w; blk < a.nblk; blk += G) {
             if (!a.ids_in) {
-                topk_block(a.ta, blk, (float *)s0, ids_lds);
+                topk_block(a.ta, blk, (float *)st[0], ids_lds);
             } else {
                 const int base_t = blk * kTokBlock;
                 const int n_t = min(kTokBlock, a.T - base_t);
@@ -279,8 +291,8 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
     trace_put(a, kTrBarB, now_ticks());
 
     // ---- phase 3: scan (every workgroup), slots of own blocks
-    int32_t *cnt = (int32_t *)s0;                      // nblk * E_local (<= 64 KB)
-    int32_t *part = (int32_t *)s1;                     // 256
+    const ScanLds cnt{(int32_t *)st[0], (int32_t *)st[1]};   // nblk * E_local (<= 64 KiB)
+    int32_t *part = (int32_t *)st[2];                         // 256
     fused_scan(a, cnt, part, off, toff, uoff);
     if (w == 0) {
         for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
@@ -398,7 +410,7 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *s0, char *s1, int32_
             __syncthreads();
             if (!ok) return;
             wait_ticks += now_ticks() - tw0;
-            gemm_tile_big<C>(g, e, row0, rows_valid, nb * C::BN, s0, s1);
+            gemm_tile_big<C>(g, e, row0, rows_valid, nb * C::BN, ls);
             ++n_done;
         }
     }

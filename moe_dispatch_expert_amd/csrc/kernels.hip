@@ -14,13 +14,16 @@ namespace mk {
 // One router work unit per workgroup.
 __global__ __launch_bounds__(256) void k_router(RouterArgs a)
 {
-    __shared__ __attribute__((aligned(16))) char st0[40960], st1[40960];
-    router_unit(a, blockIdx.x, st0, st1);
+    // a stage is the x tile followed by the W tile: at most 32 KiB + 2 KiB (E <= 8)
+    __shared__ __attribute__((aligned(16))) char st0[34816], st1[34816];
+    const RouterCfg c = router_cfg(a.E);
+    const int xb = c.BT * kRouterKC * 2;
+    router_unit(a, blockIdx.x, st0, st0 + xb, st1, st1 + xb);
 }
 
 __global__ __launch_bounds__(256) void k_topk(TopkArgs ta, CountArgs ca, int do_count)
 {
-    __shared__ float lg[16384];
+    __shared__ float lg[kTopkLdsBytes / 4];
     __shared__ int32_t ids_lds[kTokBlock * kMaxK];
     __shared__ int32_t cnt_lds[1024];
     topk_block(ta, blockIdx.x, lg, ids_lds);
@@ -69,18 +72,31 @@ __global__ __launch_bounds__(256) void k_move(SrcRows src, const int32_t *row_to
 template <class C>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) char s1[C::STAGE];
-    gemm_worker<C>(a, blockIdx.x, gridDim.x, s0, s1);
+    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE], s1[C::STAGE], s2[C::STAGE], s3[C::STAGE];
+    LdsStages ls;
+    ls.p[0] = (lds_char_t *)s0;
+    ls.p[1] = (lds_char_t *)s1;
+    ls.p[2] = (lds_char_t *)s2;
+    ls.p[3] = (lds_char_t *)s3;
+    gemm_worker<C>(a, blockIdx.x, gridDim.x, ls);
 }
 
 template <class C>
 __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) char s1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE], s1[C::STAGE], s2[C::STAGE], s3[C::STAGE];
     __shared__ int32_t off[1025], toff[1025], uoff[1025];
-    fused_kernel_body<C>(a, s0, s1, off, toff, uoff);
+    LdsStages ls;
+    ls.p[0] = (lds_char_t *)s0;
+    ls.p[1] = (lds_char_t *)s1;
+    ls.p[2] = (lds_char_t *)s2;
+    ls.p[3] = (lds_char_t *)s3;
+    char *st[4];   // filled one by one: a constant initializer would become a static one
+    st[0] = s0;
+    st[1] = s1;
+    st[2] = s2;
+    st[3] = s3;
+    fused_kernel_body<C>(a, st, ls, off, toff, uoff);
 }
 
 // ---------------------------------------------------------------- wrappers

@@ -70,7 +70,7 @@ __host__ __device__ inline int router_units(int T, int E)
 constexpr int kRouterKC = 64;   // K chunk per LDS stage (a smaller divisor of the segment if needed)
 
 template <int BE, int TE, int TT>
-__device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, char *lds1)
+__device__ void router_unit_tiled(const RouterArgs &a, int unit, char *x0, char *w0, char *x1, char *w1)
 {
 #pragma clang fp contract(off)
     constexpr int NX = BE / TE;            // threads along the experts
@@ -90,8 +90,9 @@ __device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, cha
     const int tx = tid % NX, ty = tid / NX;
     const int k_base = s * seg;
 
-    // stage layout: x tile [BT][kRouterKC] bf16, then W tile [kRouterKC][BE] fp32
-    constexpr int XBYTES = BT * kRouterKC * 2;
+    // a stage is an x tile [BT][kRouterKC] bf16 (<= 32 KiB) and a W tile [kRouterKC][BE] fp32 (<= 16 KiB)
+    static_assert(BT * kRouterKC * 2 <= 32768 && kRouterKC * BE * 4 <= 16384, "router stage sizes");
+    static_assert(BT * kRouterKC * 2 + kRouterKC * BE * 4 <= 34816, "router stage fits one 34 KiB array");
     const int cpr = KC / 8;
     uint4 xr[XPT];
     float wrg[WPT];
@@ -109,16 +110,16 @@ __device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, cha
             wrg[j] = a.wr[(size_t)(k_base + (k0) + kk) * a.E + min(eb * BE + e, a.E - 1)];        \
         }                                                                                         \
     } while (0)
-#define MK_ROUTER_STASH(st)                                                                       \
+#define MK_ROUTER_STASH(xs, ws)                                                                       \
     do {                                                                                          \
         _Pragma("unroll") for (int j = 0; j < XPT; ++j) {                                         \
             const int c = tid + j * 256;                                                          \
             if (c < BT * cpr)                                                                     \
-                *(uint4 *)((uint16_t *)(st) + (c / cpr) * kRouterKC + (c % cpr) * 8) = xr[j];     \
+                *(uint4 *)((uint16_t *)(xs) + (c / cpr) * kRouterKC + (c % cpr) * 8) = xr[j];     \
         }                                                                                         \
         _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                         \
             const int c = tid + j * 256;                                                          \
-            if (c < KC * BE) ((float *)((st) + XBYTES))[c] = wrg[j];                              \
+            if (c < KC * BE) ((float *)(ws))[c] = wrg[j];                                        \
         }                                                                                         \
     } while (0)
 
@@ -129,15 +130,13 @@ __device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, cha
         for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
 
     MK_ROUTER_FETCH(0);
-    MK_ROUTER_STASH(lds0);
+    MK_ROUTER_STASH(x0, w0);
     __syncthreads();
     const int nk = seg / KC;
     for (int kc = 0; kc < nk; ++kc) {
-        char *cur = (kc & 1) ? lds1 : lds0;
-        char *nxt = (kc & 1) ? lds0 : lds1;
         if (kc + 1 < nk) MK_ROUTER_FETCH((kc + 1) * KC);
-        const uint16_t *xt = (const uint16_t *)cur;
-        const float *wt = (const float *)(cur + XBYTES);
+        const uint16_t *xt = (const uint16_t *)((kc & 1) ? x1 : x0);
+        const float *wt = (const float *)((kc & 1) ? w1 : w0);
         for (int k8 = 0; k8 < KC; k8 += 8) {
             float xf[TT][8];
 #pragma unroll
@@ -159,7 +158,10 @@ __device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, cha
                     for (int j = 0; j < TE; ++j) acc[i][j] = __builtin_fmaf(xf[i][q], wv[j], acc[i][j]);
             }
         }
-        if (kc + 1 < nk) MK_ROUTER_STASH(nxt);
+        if (kc + 1 < nk) {
+            if (kc & 1) MK_ROUTER_STASH(x0, w0);
+            else MK_ROUTER_STASH(x1, w1);
+        }
         __syncthreads();
     }
 #undef MK_ROUTER_FETCH
@@ -176,15 +178,15 @@ __device__ void router_unit_tiled(const RouterArgs &a, int unit, char *lds0, cha
     }
 }
 
-// One workgroup unit of the partial-sum phase; lds0/lds1: two stages of at
-// least 40 KiB each.
-__device__ __forceinline__ void router_unit(const RouterArgs &a, int unit, char *lds0, char *lds1)
+// One workgroup unit of the partial-sum phase; two LDS stages, each an x part
+// (x0, x1: 32 KiB) and a W part (w0, w1: 16 KiB).
+__device__ __forceinline__ void router_unit(const RouterArgs &a, int unit, char *x0, char *w0, char *x1, char *w1)
 {
-    if (a.E <= 8) router_unit_tiled<8, 8, 1>(a, unit, lds0, lds1);
-    else if (a.E <= 16) router_unit_tiled<16, 8, 1>(a, unit, lds0, lds1);
-    else if (a.E <= 32) router_unit_tiled<32, 8, 2>(a, unit, lds0, lds1);
-    else if (a.E <= 64) router_unit_tiled<64, 8, 4>(a, unit, lds0, lds1);
-    else router_unit_tiled<64, 4, 1>(a, unit, lds0, lds1);
+    if (a.E <= 8) router_unit_tiled<8, 8, 1>(a, unit, x0, w0, x1, w1);
+    else if (a.E <= 16) router_unit_tiled<16, 8, 1>(a, unit, x0, w0, x1, w1);
+    else if (a.E <= 32) router_unit_tiled<32, 8, 2>(a, unit, x0, w0, x1, w1);
+    else if (a.E <= 64) router_unit_tiled<64, 8, 4>(a, unit, x0, w0, x1, w1);
+    else router_unit_tiled<64, 4, 1>(a, unit, x0, w0, x1, w1);
 }
 
 struct TopkArgs {
@@ -196,15 +198,22 @@ struct TopkArgs {
     int32_t T, E, k;
 };
 
-// Tokens per LDS sub-block of the top-k step: SB * (E + 1) floats fit in 64 KiB.
+// Row stride (floats) of one token's logits in LDS: padded by one for E <= 64,
+// where one lane reads one token's row, so that the lanes' rows fall in
+// different banks; unpadded above, where one wave reads one row.
+__host__ __device__ inline int topk_lg_stride(int E) { return E <= 64 ? E + 1 : E; }
+
+constexpr int kTopkLdsBytes = 32768;   // LDS for the logits of one top-k sub-block
+
+// Tokens per LDS sub-block of the top-k step: SB rows of logits fit in kTopkLdsBytes.
 __host__ __device__ inline int topk_subblock(int E)
 {
     int sb = kTokBlock;
-    while (sb > 1 && (long)sb * (E + 1) * 4 > 65536) sb >>= 1;
+    while (sb > 1 && (long)sb * topk_lg_stride(E) * 4 > kTopkLdsBytes) sb >>= 1;
     return sb;
 }
 
-// Logits of tokens [t0, t0 + nt) into LDS: lg[tl * (E + 1) + e] = ((P0 + P1) + ... + P7) + bias.
+// Logits of tokens [t0, t0 + nt) into LDS: lg[tl * stride + e] = ((P0 + P1) + ... + P7) + bias.
 // Each thread keeps the 8 partial loads of 4 logits in flight.
 __device__ __forceinline__ void block_logits(const TopkArgs &a, int t0, int nt, float *lg)
 {
@@ -230,7 +239,7 @@ __device__ __forceinline__ void block_logits(const TopkArgs &a, int t0, int nt, 
 #pragma unroll
             for (int s = 1; s < kRouterSegments; ++s) v = v + p[u][s];
             if (a.bias) v = v + a.bias[e];
-            lg[tl * (a.E + 1) + e] = v;
+            lg[tl * topk_lg_stride(a.E) + e] = v;
         }
     }
 }
@@ -320,7 +329,7 @@ __device__ __forceinline__ void topk_one_wave(const TopkArgs &a, const float *ro
 }
 
 // Top-k and gate for tokens [blk*64, blk*64 + 64), in sub-blocks whose logits
-// are first gathered into LDS (lg: 64 KiB).  ids_lds: [64][k] (LDS).
+// are first gathered into LDS (lg: kTopkLdsBytes).  ids_lds: [64][k] (LDS).
 __device__ void topk_block(const TopkArgs &a, int blk, float *lg, int32_t *ids_lds)
 {
     const int w = threadIdx.x / kWave;
@@ -333,10 +342,10 @@ __device__ void topk_block(const TopkArgs &a, int blk, float *lg, int32_t *ids_l
         __syncthreads();
         if (a.E <= 64) {
             if (w == 0 && l < nt)
-                topk_one_lane(a, lg + l * (a.E + 1), t0 + l, ids_lds + (t0 - blk * kTokBlock + l) * a.k);
+                topk_one_lane(a, lg + l * topk_lg_stride(a.E), t0 + l, ids_lds + (t0 - blk * kTokBlock + l) * a.k);
         } else {
             for (int tl = w; tl < nt; tl += (int)blockDim.x / kWave)
-                topk_one_wave(a, lg + tl * (a.E + 1), t0 + tl, ids_lds + (t0 - blk * kTokBlock + tl) * a.k);
+                topk_one_wave(a, lg + tl * topk_lg_stride(a.E), t0 + tl, ids_lds + (t0 - blk * kTokBlock + tl) * a.k);
         }
         __syncthreads();
     }
