@@ -382,7 +382,7 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
                 q_sh = (i / CH) * 8 * CH + x * CH + (i % CH);
             }
             __syncthreads();
-            const int q = q_sh;
+            const int q = __builtin_amdgcn_readfirstlane(q_sh);   // uniform: keeps the tile loop scalar
             __syncthreads();
             if (q >= n_tasks) break;
             // task q -> expert, column block, row tile (consecutive tasks share a W tile)
@@ -406,7 +406,7 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
                 q_sh = wait_flag_geq(a.tile_cnt + toff[e] + mt, units, &a.hdr->err, 2 * a.spin_limit,
                                      0x10000000u | (uint32_t)(toff[e] + mt)) ? 1 : 0;
             __syncthreads();
-            const int ok = q_sh;
+            const int ok = __builtin_amdgcn_readfirstlane(q_sh);
             __syncthreads();
             if (!ok) return;
             wait_ticks += now_ticks() - tw0;

@@ -8,13 +8,18 @@
 //   - a workgroup of 4 waves owns a BN x BM tile of y^T (W rows x token rows);
 //     each wave a (BN/2) x (BM/2) quadrant made of 32x32 v_mfma bf16 blocks
 //     with K = 16 per instruction;
-//   - both operands are K-contiguous in HBM, so tiles are copied straight from
-//     global memory into LDS (buffer_load ... lds, 16 bytes per lane, no
-//     register staging) through four 32-deep stages, with the 16-byte chunk
-//     index of each 64-byte LDS row XOR-swizzled by (row >> 2) & 3 so fragment
-//     reads are conflict-free on the 64-bank LDS;
-//   - fragment reads of the next K = 16 sub-step are interleaved with the
-//     MFMAs of the current one (sched_group_barrier);
+//   - both operands are K-contiguous in HBM.  K runs in slabs of 64: each
+//     wave loads its share of a slab as whole 128-byte lines (8 rows x 128 B
+//     per buffer_load_dwordx4) into registers two slabs ahead, and writes the
+//     slab into one of two LDS buffers one slab ahead.  Streaming is latency
+//     bound per CU, so what counts is the bytes in flight: registers hold two
+//     slabs (128 KiB per workgroup) on top of the two LDS buffers;
+//   - the 16-byte chunk index of each 128-byte LDS row is XOR-swizzled by
+//     (row >> 1) & 7, so both the slab writes and the fragment reads are
+//     conflict-free on the 64-bank LDS;
+//   - fragment reads of the next K = 16 step are interleaved with the MFMAs
+//     of the current one (sched_group_barrier), and the one barrier per slab
+//     sits before the last step, so the next slab's first reads overlap it;
 //   - W is the MFMA "A" operand, so each lane ends with 4 consecutive output
 //     columns of one row and the epilogue stores 8 bytes per lane;
 //   - ragged tails: tile rows past the expert's count read padding or the next
@@ -51,59 +56,67 @@ template <int BM_, int BN_>
 struct BigTile {
     static constexpr int BM = BM_;         // token rows per tile
     static constexpr int BN = BN_;         // W rows (output columns) per tile
-    static constexpr int BK = 32;          // K per stage: one 64-byte LDS row
-    static constexpr int NSTAGE = 4;       // LDS stages (distinct arrays)
+    static constexpr int BK = 64;          // K per slab: one 128-byte LDS row per tile row
     static constexpr int NI = BN / 64;     // 32-wide blocks per wave along N
     static constexpr int MI = BM / 64;     // 32-wide blocks per wave along M
-    static constexpr int W_BYTES = BN * BK * 2;
-    static constexpr int X_BYTES = BM * BK * 2;
-    static constexpr int STAGE = W_BYTES + X_BYTES;
-    static constexpr int DMA_PER_WAVE = (BN + BM) / 16 / 4;   // 1 KiB copies per wave per stage
+    static constexpr int WL = BN / 32;     // W loads per wave per slab (8 rows x 128 B each)
+    static constexpr int XL = BM / 32;     // x loads per wave per slab
+    static constexpr int STAGE = BN * BK * 2;   // bytes of one LDS array (W or x half of a slab buffer)
     static constexpr int THREADS = 256;
 };
-static_assert(BigTile<256, 256>::STAGE == 32768, "a stage is 32 KiB");
+static_assert(BigTile<256, 256>::STAGE == 32768, "an LDS array is 32 KiB");
 
-// Buffer resource words over [base, base + bytes): loads past the end return 0.
-typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, size_t bytes)
+typedef int32_t v4i_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i_t lds_v4i_t;
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+// The arguments must be wave-uniform; readfirstlane makes that visible to the
+// compiler, which otherwise wraps every load in a loop over distinct values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, size_t bytes)
 {
-    const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes;
     const uint64_t b = (uint64_t)base;
-    rsrc_t r;
-    r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
-    r.y = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(b >> 32) & 0xFFFFu));   // stride 0
-    r.z = __builtin_amdgcn_readfirstlane((int32_t)n);                                  // bytes
-    r.w = 0x00020000;
-    return r;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
 }
 
-// LDS tile rows are 64 bytes (32 bf16 of K) = 4 chunks of 16 bytes.  Position
-// p of tile row r holds global chunk p ^ swz(r), swz(r) = (r >> 2) & 3: the 16
-// lanes of one ds_read_b128 phase (rows r0..r0+15 at one chunk, r0 % 16 == 0)
-// then hit all 64 banks once, so fragment reads are conflict-free.
-__device__ __forceinline__ int lds_swz(int r) { return (r >> 2) & 3; }
+// One wave's share of a slab in registers: load i < WL is W, the rest x;
+// load i covers tile rows (4 (i % WL) + wave) * 8 + lane / 8, 16 bytes at
+// chunk lane % 8.
+template <class C>
+struct SlabRegs {
+    static constexpr int N = C::WL + C::XL;
+    v4i_t v[N];
+};
 
-// Issue the copy of ROWS rows x 32 bf16 (columns k0 .. k0+31) into an LDS tile,
-// 16 rows per wave instruction (buffer_load ... lds: 16 bytes per lane, lane l
-// lands at M0 + 16 l).  Lane l lands at row rb*16 + l/4, position l%4, so it
-// fetches the global chunk (l%4) ^ swz(l/4) (independent of rb): lane_off =
-// (l/4)*row_bytes + that*16.  Written as inline assembly so the compiler's own
-// tracking of LDS-bound loads, which cannot tell the four stage arrays apart,
-// adds no vmcnt(0) waits; every wait on these copies is explicit.
-template <int ROWS>
-__device__ __forceinline__ void issue_tile(rsrc_t src, uint32_t lane_off, uint32_t row_bytes, uint32_t k0_bytes,
-                                           lds_char_t *lds_tile, int wave)
+// Loads [I0, I1) of slab `slab`.  The row part of each offset is in the
+// per-lane offset (voff[i] = row * row_bytes + chunk * 16), which the buffer
+// range check covers, so rows past the end of a resource read 0 without a
+// memory access; the K part (slab * 128 bytes, always inside the row) is the
+// scalar offset.
+template <class C, int I0, int I1>
+__device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t wsrc, __amdgpu_buffer_rsrc_t xsrc,
+                                          const uint32_t (&voff)[C::WL], int slab, SlabRegs<C> &r)
+{
+    static_assert(C::WL == C::XL, "W and x tiles have the same height");
+    const uint32_t k0 = (uint32_t)slab * C::BK * 2;
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < C::WL ? wsrc : xsrc, voff[i % C::WL], k0, 0);
+}
+
+// Writes [I0, I1) of a slab from registers into an LDS buffer (128 B per row,
+// chunk p of row r at position p ^ ((r >> 1) & 7)).  st_off: this lane's byte
+// offset inside a block of 8 rows (the swizzle of row (4 i + wave) * 8 +
+// lane / 8 depends on the lane and the wave's parity only).
+template <class C, int I0, int I1>
+__device__ __forceinline__ void store_part(const SlabRegs<C> &r, lds_char_t *wbuf, lds_char_t *xbuf, int wave,
+                                           uint32_t st_off)
 {
 #pragma unroll
-    for (int it = 0; it < ROWS / 64; ++it) {
-        const int rb = it * 4 + wave;
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_tile + rb * 1024));
-        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)rb * 16u * row_bytes + k0_bytes);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                     :
-                     : "s"(m0), "v"(lane_off), "s"(src), "s"(soff)
-                     : "memory", "m0");
-    }
+    for (int i = I0; i < I1; ++i)
+        *(lds_v4i_t *)((i < C::WL ? wbuf : xbuf) + (4 * (i % C::WL) + wave) * 1024 + st_off) = r.v[i];
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima).
@@ -116,19 +129,19 @@ __device__ __forceinline__ void wait_vmem()
 __device__ __forceinline__ void wait_vmem_all() { wait_vmem<0>(); }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMFMA = 0x008, kSchedVMEM = 0x010, kSchedDSRead = 0x100;
+constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100, kSchedDSWrite = 0x200;
 
 template <class C>
-__device__ __forceinline__ void load_frags(const lds_char_t *stage, int wn, int wm, int off, bf16x8_t (&fa)[C::NI],
-                                           bf16x8_t (&fb)[C::MI])
+__device__ __forceinline__ void load_frags(const lds_char_t *wbuf, const lds_char_t *xbuf, int wn, int wm, int off,
+                                           bf16x8_t (&fa)[C::NI], bf16x8_t (&fb)[C::MI])
 {
     typedef __attribute__((address_space(3))) const bf16x8_t lds_frag_t;
-    const lds_char_t *wt = stage + (wn * (C::BN / 2)) * 64;
-    const lds_char_t *xt = stage + C::W_BYTES + (wm * (C::BM / 2)) * 64;
+    const lds_char_t *wt = wbuf + (wn * (C::BN / 2)) * 128;
+    const lds_char_t *xt = xbuf + (wm * (C::BM / 2)) * 128;
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i) fa[i] = *(lds_frag_t *)(wt + i * 32 * 64 + off);
+    for (int i = 0; i < C::NI; ++i) fa[i] = *(lds_frag_t *)(wt + i * 32 * 128 + off);
 #pragma unroll
-    for (int j = 0; j < C::MI; ++j) fb[j] = *(lds_frag_t *)(xt + j * 32 * 64 + off);
+    for (int j = 0; j < C::MI; ++j) fb[j] = *(lds_frag_t *)(xt + j * 32 * 128 + off);
 }
 
 template <class C>
@@ -142,60 +155,66 @@ __device__ __forceinline__ void mfma_block(const bf16x8_t (&fa)[C::NI], const bf
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
 }
 
-// Interleave the MFMAs just emitted with the fragment reads just emitted:
-// one read after each of the first NR MFMAs.
-template <class C>
-__device__ __forceinline__ void sched_mfma_with_reads(bool reads)
+// Order the K = 16 step just emitted: NR fragment reads, then NW slab writes
+// each followed by a slab load, one after each MFMA; the rest of the MFMAs
+// after them.
+template <class C, int NR, int NW>
+__device__ __forceinline__ void sched_step()
 {
-    constexpr int NR = C::NI + C::MI, NM = C::NI * C::MI;
-    if (reads) {
+    constexpr int NM = C::NI * C::MI;
+    static_assert(NR + NW <= NM, "one MFMA per read or write");
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NM - NR, 0);
-    } else {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NM, 0);
+    for (int r = 0; r < NR; ++r) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
     }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSWrite, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+    }
+    if (NM - NR - NW > 0) __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NM - NR - NW, 0);
 }
 
 // One BN x BM tile: token rows [row0, row0 + BM) of x_perm (rows_valid of
 // them readable and stored), W rows [n0, n0 + BN) of expert e.
 //
-// K runs in stages of 32 through four LDS arrays (d / 32 stages, a multiple
-// of 4 since d % 128 == 0).  Stage k lives in array k % 4 and has two
-// sub-steps of K = 16.  Per stage:
-//   sub-step 0: MFMAs on fragments fr0 while fragments fr1 (sub-step 1 of
-//               this stage) are read;
-//   wait for the copy of stage k+1, barrier (every wave is then past its
-//               reads of stage k, and stage k+1 is visible), issue the copy of
-//               stage k+4 into stage k's array;
-//   sub-step 1: MFMAs on fr1 while fr0 of stage k+1 is read.
-// The copy of stage k+4 therefore has three stages of lead time.  The loop is
-// written out four stages at a time so every LDS array and wait count is a
-// compile-time constant.
+// Slab j (K = 64 j .. 64 j + 63) is computed from LDS buffer j % 2 (W in
+// ls.p[2 (j % 2)], x in ls.p[2 (j % 2) + 1]) in four K = 16 steps, with the
+// fragments of step s + 1 read during the MFMAs of step s.  Between steps 2
+// and 3: write slab j + 1 from registers into the other buffer (its old slab
+// j - 1 was last read before the previous barrier), load slab j + 3 into the
+// registers just freed, barrier, then read step 0 of slab j + 1 during step 3.
+// Slab s lives in register set s % 2, loaded two slabs before it is written.
 template <class C>
 __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0, int rows_valid, int n0,
                                               const LdsStages &ls)
 {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps M0/soffset scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps soffsets scalar
     const int lane = threadIdx.x % kWave;
     const int wn = wave & 1, wm = wave >> 1;
     const size_t w_first = (size_t)e * a.N + n0;
-    const rsrc_t wsrc =
+    const __amdgpu_buffer_rsrc_t wsrc =
         make_rsrc(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
     // Only the tile's valid rows are readable: rows past a ragged end return 0 without a memory access
     // (they may belong to a tile that is not yet moved).
-    const rsrc_t xsrc = make_rsrc(a.x_perm + (size_t)row0 * a.d, (size_t)rows_valid * a.d * 2);
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a.x_perm + (size_t)row0 * a.d, (size_t)rows_valid * a.d * 2);
+    // Loads of slabs past the end go to empty resources: they read 0 without a memory access, and
+    // keep the number of loads in flight the same on every path.
+    const __amdgpu_buffer_rsrc_t wnone = make_rsrc(a.w, 0), xnone = make_rsrc(a.x_perm, 0);
     const uint32_t row_bytes = (uint32_t)a.d * 2;
-    const uint32_t lane_off = (uint32_t)(lane >> 2) * row_bytes + (uint32_t)(((lane & 3) ^ lds_swz(lane >> 2)) << 4);
-    const int KT = a.d / C::BK;   // a multiple of 4 (d % 128 == 0)
-
-    int frag_off[2];   // row (lane & 31) of a 32-row block, chunk 2kk + lane/32
+    uint32_t voff[C::WL];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        frag_off[kk] = (lane & 31) * 64 + (((2 * kk + (lane >> 5)) ^ lds_swz(lane & 31)) << 4);
+    for (int i = 0; i < C::WL; ++i)
+        voff[i] = (uint32_t)((4 * i + wave) * 8 + (lane >> 3)) * row_bytes + (uint32_t)(lane & 7) * 16u;
+    const uint32_t st_off = (uint32_t)(lane >> 3) * 128u + (uint32_t)(((lane & 7) ^ ((lane >> 4) + 4 * (wave & 1))) << 4);
+    const int KK = __builtin_amdgcn_readfirstlane(a.d / C::BK);   // even (d % 128 == 0); uniform
+
+    int frag_off[4];   // row (lane & 31) of a 32-row block, chunk 2 kk + lane / 32
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        frag_off[kk] = (lane & 31) * 128 + (((2 * kk + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) << 4);
 
     f32x16_t acc[C::NI][C::MI];
 #pragma unroll
@@ -205,56 +224,74 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    lds_char_t *const st[4] = {ls.p[0], ls.p[1], ls.p[2], ls.p[3]};
-    auto issue_stage = [&](int k, lds_char_t *dst) {
-        const uint32_t k0 = (uint32_t)k * C::BK * 2;
-        issue_tile<C::BN>(wsrc, lane_off, row_bytes, k0, dst, wave);
-        issue_tile<C::BM>(xsrc, lane_off, row_bytes, k0, dst + C::W_BYTES, wave);
-    };
-    // vmcnt counts loads and stores together and they may complete out of
-    // order relative to each other: the previous tile's output stores must be
-    // done before a partial vmcnt wait can stand for "these copies arrived".
-    wait_vmem_all();
-    issue_stage(0, st[0]);
-    issue_stage(1, st[1]);
-    issue_stage(2, st[2]);
-    issue_stage(3, st[3]);
-    wait_vmem<3 * C::DMA_PER_WAVE>();
+    lds_char_t *const wb[2] = {ls.p[0], ls.p[2]};
+    lds_char_t *const xb[2] = {ls.p[1], ls.p[3]};
+    constexpr int NL = SlabRegs<C>::N;
+    constexpr int P1 = (NL + 2) / 3, P2 = (2 * NL + 2) / 3;   // the slab write in three parts
+    constexpr int NR = C::NI + C::MI;
+    SlabRegs<C> r0, r1;
+    load_part<C, 0, NL>(wsrc, xsrc, voff, 0, r0);
+    load_part<C, 0, NL>(wsrc, xsrc, voff, 1, r1);
+    store_part<C, 0, NL>(r0, wb[0], xb[0], wave, st_off);
+    load_part<C, 0, NL>(KK > 2 ? wsrc : wnone, KK > 2 ? xsrc : xnone, voff, 2, r0);
     __syncthreads();
     bf16x8_t fa0[C::NI], fb0[C::MI], fa1[C::NI], fb1[C::MI];
-    load_frags<C>(st[0], wn, wm, frag_off[0], fa0, fb0);
+    load_frags<C>(wb[0], xb[0], wn, wm, frag_off[0], fa0, fb0);
 
-    // One stage; ISSUE: refill CUR with stage K + 4; WAITN: copies allowed in
-    // flight once stage K + 1 has arrived (-1: K is the last stage).
-#define MK_GEMM_STAGE(CUR, NXT, K, ISSUE, WAITN)                                                        \
+    // Slab J from buffer B; RN: the register set holding slab J + 1; NEXT
+    // (compile-time): slab J + 1 exists.  During steps 0..2, slab J + 1 is
+    // written from RN into the other buffer, a third per step, and each
+    // register is refilled with slab J + 3 right after it is written (from
+    // the empty resources if slab J + 3 does not exist).
+#define MK_GEMM_SLAB(B, RN, J, NEXT)                                                                   \
     do {                                                                                               \
-        load_frags<C>(CUR, wn, wm, frag_off[1], fa1, fb1);                                             \
+        const bool ahead_ = __builtin_amdgcn_readfirstlane((J) + 3 < KK);                              \
+        const __amdgpu_buffer_rsrc_t wl_ = ahead_ ? wsrc : wnone, xl_ = ahead_ ? xsrc : xnone;         \
+        lds_char_t *const wo_ = wb[1 - (B)];                                                           \
+        lds_char_t *const xo_ = xb[1 - (B)];                                                           \
+        load_frags<C>(wb[B], xb[B], wn, wm, frag_off[1], fa1, fb1);                                    \
         mfma_block<C>(fa0, fb0, acc);                                                                  \
-        sched_mfma_with_reads<C>(true);                                                                \
-        if ((WAITN) >= 0) {                                                                            \
-            wait_vmem<((WAITN) < 0 ? 0 : (WAITN))>();                                                  \
+        if (NEXT) {                                                                                    \
+            store_part<C, 0, P1>(RN, wo_, xo_, wave, st_off);                                          \
+            load_part<C, 0, P1>(wl_, xl_, voff, (J) + 3, RN);                                          \
+            sched_step<C, NR, P1>();                                                                   \
+        } else {                                                                                       \
+            sched_step<C, NR, 0>();                                                                    \
+        }                                                                                              \
+        load_frags<C>(wb[B], xb[B], wn, wm, frag_off[2], fa0, fb0);                                    \
+        mfma_block<C>(fa1, fb1, acc);                                                                  \
+        if (NEXT) {                                                                                    \
+            store_part<C, P1, P2>(RN, wo_, xo_, wave, st_off);                                         \
+            load_part<C, P1, P2>(wl_, xl_, voff, (J) + 3, RN);                                         \
+            sched_step<C, NR, P2 - P1>();                                                              \
+        } else {                                                                                       \
+            sched_step<C, NR, 0>();                                                                    \
+        }                                                                                              \
+        load_frags<C>(wb[B], xb[B], wn, wm, frag_off[3], fa1, fb1);                                    \
+        mfma_block<C>(fa0, fb0, acc);                                                                  \
+        if (NEXT) {                                                                                    \
+            store_part<C, P2, NL>(RN, wo_, xo_, wave, st_off);                                         \
+            load_part<C, P2, NL>(wl_, xl_, voff, (J) + 3, RN);                                         \
+            sched_step<C, NR, NL - P2>();                                                              \
+            __builtin_amdgcn_sched_barrier(0);                                                         \
             __syncthreads();                                                                           \
-            if (ISSUE) issue_stage((K) + 4, CUR);                                                      \
-            load_frags<C>(NXT, wn, wm, frag_off[0], fa0, fb0);                                         \
+            load_frags<C>(wo_, xo_, wn, wm, frag_off[0], fa0, fb0);                                    \
+        } else {                                                                                       \
+            sched_step<C, NR, 0>();                                                                    \
         }                                                                                              \
         mfma_block<C>(fa1, fb1, acc);                                                                  \
-        sched_mfma_with_reads<C>((WAITN) >= 0);                                                        \
+        if (NEXT) sched_step<C, NR, 0>();                                                              \
+        else sched_step<C, 0, 0>();                                                                    \
     } while (0)
 
-    constexpr int D2 = 2 * C::DMA_PER_WAVE;
-    int kt = 0;
-    for (; kt + 4 < KT; kt += 4) {   // every stage refills: four stages always in flight
-        MK_GEMM_STAGE(st[0], st[1], kt, true, D2);
-        MK_GEMM_STAGE(st[1], st[2], kt + 1, true, D2);
-        MK_GEMM_STAGE(st[2], st[3], kt + 2, true, D2);
-        MK_GEMM_STAGE(st[3], st[0], kt + 3, true, D2);
+    int j = 0;
+    for (; j + 2 < KK; j += 2) {
+        MK_GEMM_SLAB(0, r1, j, true);
+        MK_GEMM_SLAB(1, r0, j + 1, true);
     }
-    // last four stages: nothing left to issue, the pipeline drains
-    MK_GEMM_STAGE(st[0], st[1], kt, false, D2);
-    MK_GEMM_STAGE(st[1], st[2], kt + 1, false, C::DMA_PER_WAVE);
-    MK_GEMM_STAGE(st[2], st[3], kt + 2, false, 0);
-    MK_GEMM_STAGE(st[3], st[0], kt + 3, false, -1);
-#undef MK_GEMM_STAGE
+    MK_GEMM_SLAB(0, r1, j, true);
+    MK_GEMM_SLAB(1, r0, j + 1, false);
+#undef MK_GEMM_SLAB
     __syncthreads();   // every wave is done with the stages before the next tile refills them
 
     // epilogue: lane holds y^T[n][m] for n = base + 8*(v/4) + 4*(lane/32) + v%4, m = lane%32
