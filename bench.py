@@ -87,8 +87,8 @@ def trace_summary(tr: dict) -> dict:
     live = tr["start"] > 0
     t0 = tr["start"][live].min()
     us = lambda v: round(float(v - t0) / tr["ticks_per_us"], 2)
-    out = {}
-    for name in ("routed", "barrier_a", "counted", "barrier_b", "slots", "barrier_c", "moved", "done"):
+    out = {"start_spread_us": us(tr["start"][live].max())}
+    for name in ("routed", "barrier_a", "selected", "counted", "barrier_b", "slots", "barrier_c", "moved", "done"):
         v = tr[name][live]
         v = v[v > 0]
         if v.size:

@@ -149,11 +149,12 @@ mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *
  * workspace: *offset bytes from its start, *n_wg records of *words uint64
  * each (record w = workgroup w).  Words, written by every fused call:
  *   0 start, 1 router logits done, 2 barrier A passed, 3 histogram done,
- *   4 barrier B passed, 5 slot map done, 6 barrier C passed, 7 mover role
+ *   4 barrier B passed, 5 scan done, 6 unused (0), 7 mover role
  *   done, 8 first GEMM task started, 9 workgroup done (wall-clock ticks,
  *   *ticks_per_us per microsecond); 10 GEMM tasks run, 11 ticks spent
  *   waiting for tiles, 12 hardware XCD id, 13 mover units copied, 14 ticks
- *   copying rows, 15 ticks publishing moved units.
+ *   copying rows, 15 ticks publishing moved units, 16 token-parallel
+ *   selection done (E > 64 only); words 17.. are zero.
  * For profiling the overlap of the roles; the host reads it after a sync. */
 mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,
                                   int32_t *words, int32_t *ticks_per_us);

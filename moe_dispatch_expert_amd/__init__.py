@@ -168,7 +168,8 @@ def mk_select_tuning(T, d, E, k, e_begin, E_local, N) -> dict:
 
 
 TRACE_WORDS = ("start", "routed", "barrier_a", "counted", "barrier_b", "slots", "barrier_c", "moved",
-               "first_task", "done", "tasks", "wait_ticks", "xcc", "units", "copy_ticks", "release_ticks")
+               "first_task", "done", "tasks", "wait_ticks", "xcc", "units", "copy_ticks", "release_ticks",
+               "selected")
 
 
 def mk_dispatch_gemm_trace(workspace: torch.Tensor, T, d, E, k, e_begin, E_local, N, S=1) -> dict:

@@ -222,6 +222,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     int32_t *ids = (int32_t *)(ws + L.ids);
     int32_t *lrank = (int32_t *)(ws + L.lrank);
     int32_t *blkcnt = (int32_t *)(ws + L.blkcnt);
+    uint64_t *blkmask = (uint64_t *)(ws + L.blkmask);
     int32_t *blkbase = (int32_t *)(ws + L.blkbase);
     int32_t *tile_off = (int32_t *)(ws + L.tile_off);
     int32_t *row_token_ws = (int32_t *)(ws + L.row_token);
@@ -243,12 +244,16 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.ta.ids = ids;
         fa.ta.ids_user = topk_ids_out;
         fa.ta.w_user = topk_w_out;
+        fa.ta.blkmask = blkmask;
         fa.ta.T = s->T;
         fa.ta.E = s->E;
         fa.ta.k = s->k;
+        fa.ta.e_begin = s->e_begin;
+        fa.ta.E_local = s->E_local;
         fa.ca.ids = ids;
         fa.ca.lrank = lrank;
         fa.ca.blkcnt = blkcnt;
+        fa.ca.blkmask = blkmask;
         fa.ca.err = &hdr->err;
         fa.ca.T = s->T;
         fa.ca.E = s->E;
@@ -315,6 +320,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     ca.ids = ids;
     ca.lrank = lrank;
     ca.blkcnt = blkcnt;
+    ca.blkmask = blkmask;
     ca.err = &hdr->err;
     ca.T = s->T;
     ca.E = s->E;

@@ -68,7 +68,7 @@ struct FusedArgs {
 enum TraceWord {
     kTrStart = 0, kTrRouted, kTrBarA, kTrCounted, kTrBarB, kTrSlots, kTrBarC, kTrMoved, kTrFirstTask,
     kTrDone, kTrTasks /* count */, kTrWaitTicks, kTrXcc /* hardware XCC id */, kTrUnits /* count */,
-    kTrCopyTicks, kTrReleaseTicks
+    kTrCopyTicks, kTrReleaseTicks, kTrSelected
 };
 
 __device__ __forceinline__ void trace_put(const FusedArgs &a, int word, uint64_t v)
@@ -114,11 +114,14 @@ struct ScanLds {
     }
 };
 
-__device__ void fused_scan(const FusedArgs &a, const ScanLds &cnt, int32_t *part, int32_t *off, int32_t *toff,
-                           int32_t *uoff)
+__device__ __forceinline__ void fused_scan(const FusedArgs &a, const ScanLds &cnt, int32_t *part, int32_t *off, int32_t *toff,
+                           int32_t *uoff, bool from_masks)
 {
     const int n = a.nblk * a.E_local;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = a.ca.blkcnt[i];
+    if (from_masks)
+        for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = __popcll(a.ca.blkmask[i]);
+    else
+        for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = a.ca.blkcnt[i];
     __syncthreads();
     // thread (e, p): blocks [p*L, (p+1)*L) of expert column e
     const int P = a.E_local >= (int)blockDim.x ? 1 : (int)blockDim.x / a.E_local;
@@ -159,18 +162,80 @@ __device__ void fused_scan(const FusedArgs &a, const ScanLds &cnt, int32_t *part
     __syncthreads();
 }
 
-// Copy one unit of up to kMoveRows consecutive rows [r0, r1) of the expert
-// buffer, one row per wave at a time, first waiting for the source-chunk
-// arrival flags of the unit's rows when rows come from peers.
-__device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, int r0, int r1)
+// Rows [row0, row0 + nrows) of the expert buffer from their tokens (tok_lds,
+// -1 = skip), NR rows per wave at a time with all their loads in flight.
+template <int CPL, int NR>
+__device__ __forceinline__ void move_rows(const FusedArgs &a, const int32_t *tok_lds, int row0, int nrows, int wave,
+                                          int lane)
 {
-    const int nrows = r1 - r0;
+    const int cpr = a.d / 8;
+    for (int r0 = wave * NR; r0 < nrows; r0 += (int)(blockDim.x / kWave) * NR) {
+        const uint16_t *src[NR];
+        uint16_t *dst[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = r0 + i;
+            const int t = r < nrows ? tok_lds[r] : -1;
+            src[i] = t >= 0 ? token_row(a.src, t, a.d) : nullptr;
+            dst[i] = t >= 0 ? a.x_perm + (size_t)(row0 + r) * a.d : nullptr;
+        }
+        if (!src[0]) {   // keep a valid address in slot 0 for the clamped loads
+#pragma unroll
+            for (int i = 1; i < NR; ++i)
+                if (src[i]) src[0] = src[i];
+        }
+        if (src[0]) copy_rows_wave<CPL, NR>(src, dst, cpr, lane);
+    }
+}
+
+// One mover unit: ranks [q0, q1) (q1 - q0 <= kMoveRows) of local expert le,
+// i.e. expert-buffer rows off[le] + q0 .. off[le] + q1 - 1.  The unit finds
+// its own tokens: block b holds the expert's ranks [base_b, base_{b+1}) (bases
+// from the scan, in LDS), in the token order of the set bits of the block's
+// mask for the expert.  Then it waits for the arrival flags of the rows'
+// source chunks (when rows come from peers) and copies the rows, one per wave
+// at a time.
+__device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, const ScanLds &base, const int32_t *off, int le,
+                                                int q0, int q1, int32_t *tok_lds)
+{
+    const int n_e = off[le + 1] - off[le];
+    // blocks [b_lo, b_hi) hold ranks [q0, q1): b_lo is the last block with base <= q0,
+    // b_hi the first block with base >= q1
+    int lo = 0, hi = a.nblk;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (base[mid * a.E_local + le] <= q0) lo = mid; else hi = mid;
+    }
+    const int b_lo = lo;
+    lo = b_lo;
+    hi = a.nblk;
+    while (hi - lo > 1) {   // last block with base < q1
+        const int mid = (lo + hi) >> 1;
+        if (base[mid * a.E_local + le] < q1) lo = mid; else hi = mid;
+    }
+    const int b_hi = lo + 1;
+    if ((int)threadIdx.x < kMoveRows) tok_lds[threadIdx.x] = -1;   // a rank not found stays -1 and is skipped
+    __syncthreads();
+    for (int b = b_lo + (int)threadIdx.x; b < b_hi; b += blockDim.x) {
+        uint64_t m = a.ca.blkmask[(size_t)b * a.E_local + le];
+        int q = base[b * a.E_local + le];
+        const int q_end = b + 1 < a.nblk ? base[(b + 1) * a.E_local + le] : n_e;
+        while (m && q < q1) {
+            const int bit = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            if (q >= q0 && q < q_end) tok_lds[q - q0] = b * kTokBlock + bit;
+            ++q;
+        }
+    }
+    __syncthreads();
+    const int nrows = q1 - q0;
     __shared__ int ok_sh;
     if (threadIdx.x == 0) {
         int ok = 1, waited = -1;
         if (a.fl.chunk_rows > 0) {
             for (int i = 0; i < nrows && ok; ++i) {   // rows are in token order, so chunks ascend
-                const int t = a.row_token_ws[r0 + i];
+                const int t = tok_lds[i];
+                if (t < 0) continue;
                 const int sh = t / a.src.rows_per_src;
                 const int c = sh * a.fl.chunks_per_src + (t - sh * a.src.rows_per_src) / a.fl.chunk_rows;
                 if (c == waited) continue;
@@ -185,14 +250,22 @@ __device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, int r0, int 
     if (!ok_sh) return false;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
-    for (int r = r0 + wave; r < r1; r += (int)blockDim.x / kWave) move_row(a.src, a.row_token_ws, a.x_perm, a.d, r, lane);
+    const int cpr = a.d / 8;
+    if (cpr <= 4 * kWave) move_rows<4, 8>(a, tok_lds, off[le] + q0, nrows, wave, lane);
+    else if (cpr <= 8 * kWave) move_rows<8, 4>(a, tok_lds, off[le] + q0, nrows, wave, lane);
+    else if (cpr <= 16 * kWave) move_rows<16, 2>(a, tok_lds, off[le] + q0, nrows, wave, lane);
+    else
+        for (int r = wave; r < nrows; r += (int)blockDim.x / kWave) {
+            const int t = tok_lds[r];
+            if (t >= 0) copy_row(token_row(a.src, t, a.d), a.x_perm + (size_t)(off[le] + q0 + r) * a.d, a.d, lane);
+        }
     wait_vmem_all();   // this wave's stores have reached L2 before the release below
     return true;
 }
 
 // The arrival simulator: releases chunk c at start + delay[c] microseconds,
 // copying the chunk's payload into the source buffer first if one is given.
-__device__ void fused_arrival_sim(const FusedArgs &a)
+__device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a)
 {
     const int n_chunks = a.src.S * a.fl.chunks_per_src;
     const uint64_t per_us = a.ticks_per_us;
@@ -238,10 +311,12 @@ __device__ void fused_arrival_sim(const FusedArgs &a)
 // addresses for the GEMM), also used by the earlier phases; off, toff, uoff:
 // LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
 template <class C>
-__device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], const LdsStages &ls, int32_t *off,
+__device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], const LdsStages &ls, int32_t *off,
                                   int32_t *toff, int32_t *uoff)
 {
     const int w = blockIdx.x;
+    if (w < kTraceWGs && (int)threadIdx.x < kTraceWords) a.trace[w * kTraceWords + threadIdx.x] = 0;   // this call's record only
+    __syncthreads();
     trace_put(a, kTrStart, now_ticks());
     trace_put(a, kTrXcc, (uint64_t)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & 0xF));
     if (a.has_sim && w == (int)gridDim.x - 1) {
@@ -256,6 +331,13 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
     if (w == 0 && threadIdx.x < 8) a.xcd_next[threadIdx.x] = 0u;
     for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x) a.tile_cnt[i] = 0u;
 
+    // Token-per-wave selection (E > 64) builds the block masks with atomic ORs:
+    // clear them before barrier A.
+    const bool wave_topk = !a.ids_in && a.E > 64;
+    if (wave_topk)
+        for (int i = w * (int)blockDim.x + threadIdx.x; i < a.nblk * a.E_local; i += G * (int)blockDim.x)
+            a.ca.blkmask[i] = 0ull;
+
     // ---- phase 1: router logits
     if (!a.ids_in) {
         const int units = router_units(a.T, a.E);
@@ -264,10 +346,22 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
         if (!fused_barrier(a, 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
     }
-    // ---- phase 2: top-k + histogram + ranks per 64-token block
-    {
+    // ---- phase 2: top-k, histogram and ranks.  E > 64: the selection runs
+    // token-parallel over every workgroup (one token per wave) and ORs each
+    // token into its block's mask of every local expert it chose; after the
+    // barrier the masks give the counts and ranks.  E <= 64 or given ids: per
+    // 64-token block, selection (or copy) and histogram in one workgroup.
+    if (wave_topk) {
+        const int units = topk_wave_units(a.T);
+        for (int u = w; u < units; u += G) topk_wave_unit(a.ta, u);
+        trace_put(a, kTrSelected, now_ticks());
+        trace_put(a, kTrCounted, now_ticks());
+        if (!fused_barrier(a, 0x04000000u)) return;
+        trace_put(a, kTrBarB, now_ticks());
+    } else {
         int32_t *ids_lds = (int32_t *)st[1];                          // 8 KiB
-        int32_t *cnt_lds = (int32_t *)(st[1] + kTokBlock * kMaxK * 4);  // E_local ints
+        int32_t *cnt_lds = (int32_t *)(st[1] + kTokBlock * kMaxK * 4);  // E_local ints (<= 4 KiB)
+        uint64_t *mask_lds = (uint64_t *)(st[1] + 16384);               // E_local uint64 (<= 8 KiB)
         for (int blk = w; blk < a.nblk; blk += G) {
             if (!a.ids_in) {
                 topk_block(a.ta, blk, (float *)st[0], ids_lds);
@@ -283,17 +377,19 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
                 }
             }
             __syncthreads();
-            count_block(a.ca, blk, ids_lds, cnt_lds);
+            count_block(a.ca, blk, ids_lds, cnt_lds, mask_lds);
         }
+        trace_put(a, kTrCounted, now_ticks());
+        if (!fused_barrier(a, 0x02000000u)) return;
+        trace_put(a, kTrBarB, now_ticks());
     }
-    trace_put(a, kTrCounted, now_ticks());
-    if (!fused_barrier(a, 0x02000000u)) return;
-    trace_put(a, kTrBarB, now_ticks());
 
-    // ---- phase 3: scan (every workgroup), slots of own blocks
+    // ---- phase 3: scan (every workgroup), slot map of own blocks.  The movers
+    // need no barrier after it: they find the tokens of their rows from the
+    // block masks and the bases, which every workgroup holds in LDS.
     const ScanLds cnt{(int32_t *)st[0], (int32_t *)st[1]};   // nblk * E_local (<= 64 KiB)
     int32_t *part = (int32_t *)st[2];                         // 256
-    fused_scan(a, cnt, part, off, toff, uoff);
+    fused_scan(a, cnt, part, off, toff, uoff, wave_topk);
     if (w == 0) {
         for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
             a.offsets[e] = off[e];
@@ -310,9 +406,13 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
             if (t >= a.T) break;
             const size_t o = (size_t)t * a.k + (i % a.k);
             const int le = a.ta.ids[o] - a.e_begin;
-            const int32_t rank = a.ca.lrank[o];
+            const bool local = le >= 0 && le < a.E_local;
+            int32_t rank = -1;
+            if (!wave_topk) rank = a.ca.lrank[o];
+            else if (local)   // tokens before t in the block with the same expert
+                rank = __popcll(a.ca.blkmask[(size_t)blk * a.E_local + le] & ((1ull << (t % kTokBlock)) - 1ull));
             int32_t slot = -1;
-            if (le >= 0 && le < a.E_local && rank >= 0) {
+            if (local && rank >= 0) {
                 slot = off[le] + cnt[blk * a.E_local + le] + rank;
                 if (slot < off[le + 1]) {
                     a.row_token_ws[slot] = t;
@@ -325,15 +425,12 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
         }
     }
     trace_put(a, kTrSlots, now_ticks());
-    if (!fused_barrier(a, 0x03000000u)) return;
-    trace_put(a, kTrBarC, now_ticks());
 
-    const int n_tiles = toff[a.E_local];
-    const int R = off[a.E_local];
-    // ---- movers: unit u = kMoveRows rows of one expert (tile-major, since bm % kMoveRows == 0),
+    // ---- movers: unit u = kMoveRows ranks of one expert (tile-major, since bm % kMoveRows == 0),
     // dealt round-robin over the movers
     uint64_t n_units = 0, copy_ticks = 0, release_ticks = 0;
     if (w < a.n_mover) {
+        int32_t *tok_lds = (int32_t *)st[2] + 256;   // kMoveRows ints after the scan's partials
         const int n_units_all = uoff[a.E_local];
         for (int u = w; u < n_units_all; u += a.n_mover) {
             int lo = 0, hi = a.E_local;   // expert e with uoff[e] <= u < uoff[e+1]
@@ -343,11 +440,11 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
             }
             const int e = lo;
             const int q = u - uoff[e];
-            const int r0 = off[e] + q * kMoveRows;
-            const int r1 = min(off[e + 1], r0 + kMoveRows);
-            const int mt = (q * kMoveRows) / a.bm;
+            const int q0 = q * kMoveRows;
+            const int q1 = min(off[e + 1] - off[e], q0 + kMoveRows);
+            const int mt = q0 / a.bm;
             const uint64_t c0 = now_ticks();
-            const bool ok = fused_move_unit(a, r0, r1);
+            const bool ok = fused_move_unit(a, cnt, off, e, q0, q1, tok_lds);
             __syncthreads();
             if (!ok) return;
             const uint64_t c1 = now_ticks();
@@ -358,8 +455,6 @@ __device__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], cons
             ++n_units;
         }
     }
-    (void)R;
-    (void)n_tiles;
     trace_put(a, kTrMoved, now_ticks());
     trace_put(a, kTrUnits, n_units);
     trace_put(a, kTrCopyTicks, copy_ticks);

@@ -345,7 +345,7 @@ __device__ __forceinline__ TaskPos decode_task(const int32_t *tile_off, int E_lo
 // (w % 8 == x, dispatched round-robin over the 8 XCDs) a contiguous run of
 // tasks, so tasks sharing a W tile share that XCD's L2.
 template <class C>
-__device__ void gemm_worker(const GemmArgs &a, int w, int G, const LdsStages &ls)
+__device__ __forceinline__ void gemm_worker(const GemmArgs &a, int w, int G, const LdsStages &ls)
 {
     const int n_tiles = (int)a.hdr->n_tiles;
     const int NB = (a.N + C::BN - 1) / C::BN;

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a)
     // a stage is the x tile followed by the W tile: at most 32 KiB + 2 KiB (E <= 8)
     __shared__ __attribute__((aligned(16))) char st0[34816], st1[34816];
     const RouterCfg c = router_cfg(a.E);
-    const int xb = c.BT * kRouterKC * 2;
+    const int xb = c.BT * kRouterXS * 2;
     router_unit(a, blockIdx.x, st0, st0 + xb, st1, st1 + xb);
 }
 
@@ -26,15 +26,20 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs ta, CountArgs ca, int do_
     __shared__ float lg[kTopkLdsBytes / 4];
     __shared__ int32_t ids_lds[kTokBlock * kMaxK];
     __shared__ int32_t cnt_lds[1024];
+    __shared__ uint64_t mask_lds[1024];
     topk_block(ta, blockIdx.x, lg, ids_lds);
-    if (do_count) count_block(ca, blockIdx.x, ids_lds, cnt_lds);
+    if (do_count) count_block(ca, blockIdx.x, ids_lds, cnt_lds, mask_lds);
 }
+
+// Token-per-wave top-k (E > 64), four tokens per workgroup.
+__global__ __launch_bounds__(256) void k_topk_wave(TopkArgs ta) { topk_wave_unit(ta, blockIdx.x); }
 
 __global__ __launch_bounds__(256) void k_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user,
                                                      CountArgs ca)
 {
     __shared__ int32_t ids_lds[kTokBlock * kMaxK];
     __shared__ int32_t cnt_lds[1024];
+    __shared__ uint64_t mask_lds[1024];
     const int base_t = blockIdx.x * kTokBlock;
     const int n_t = min(kTokBlock, ca.T - base_t);
     for (int i = threadIdx.x; i < n_t * ca.k; i += blockDim.x) {
@@ -45,7 +50,7 @@ __global__ __launch_bounds__(256) void k_count_given(const int32_t *ids_in, int3
         if (ids_user) ids_user[o] = id;
     }
     __syncthreads();
-    count_block(ca, blockIdx.x, ids_lds, cnt_lds);
+    count_block(ca, blockIdx.x, ids_lds, cnt_lds, mask_lds);
 }
 
 __global__ __launch_bounds__(1024) void k_scan(ScanArgs a)
@@ -109,6 +114,14 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 
 hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s)
 {
+    if (ta.E > 64) {
+        // token-parallel selection, then the per-block histogram from the ids it wrote
+        hipLaunchKernelGGL(k_topk_wave, dim3(topk_wave_units(ta.T)), dim3(256), 0, s, ta);
+        if (!do_count) return hipGetLastError();
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_count_given(ta.ids, ta.ids, nullptr, ca, s);
+    }
     const int nblk = (ta.T + kTokBlock - 1) / kTokBlock;
     hipLaunchKernelGGL(k_topk, dim3(nblk), dim3(256), 0, s, ta, ca, do_count ? 1 : 0);
     return hipGetLastError();

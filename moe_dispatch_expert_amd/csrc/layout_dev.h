@@ -129,6 +129,30 @@ __device__ __forceinline__ void copy_row(const uint16_t *src_row, uint16_t *dst_
                               lane);
 }
 
+// Copy NR rows of d bf16 with one wave, all NR * CPL loads of a lane in
+// flight before the first store (cpr = d / 8 <= 64 * CPL chunks per row).
+// src[i] / dst[i] may be null for a row that is skipped.
+template <int CPL, int NR>
+__device__ __forceinline__ void copy_rows_wave(const uint16_t *const (&src)[NR], uint16_t *const (&dst)[NR],
+                                               int cpr, int lane)
+{
+    cp_u32x4_t v[NR][CPL];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        gcuint4_t *s = (gcuint4_t *)(src[r] ? src[r] : src[0]);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) v[r][i] = s[min(lane + kWave * i, cpr - 1)];
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        if (!dst[r]) continue;
+        guint4_t *d = (guint4_t *)dst[r];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            if (lane + kWave * i < cpr) d[lane + kWave * i] = v[r][i];
+    }
+}
+
 // Copy one expert-buffer row r: x_perm[r] = x[row_token[r]].
 __device__ __forceinline__ void move_row(const SrcRows &src, const int32_t *row_token, uint16_t *x_perm,
                                          int d, int r, int lane)

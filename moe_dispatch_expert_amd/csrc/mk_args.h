@@ -47,10 +47,10 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 // Byte offsets of the workspace segments (all 256-byte aligned).
 constexpr int kTraceWGs = 1024;   // workgroups the trace segment has room for
-constexpr int kTraceWords = 16;   // uint64 records per workgroup
+constexpr int kTraceWords = 32;   // uint64 records per workgroup
 
 struct WsLayout {
-    size_t hdr, part, ids, lrank, blkcnt, blkbase, tile_off, tile_flag, row_token, trace, x_perm, total;
+    size_t hdr, part, ids, lrank, blkcnt, blkbase, blkmask, tile_off, tile_flag, row_token, trace, x_perm, total;
     int32_t nblk, max_tiles, r_cap, x_perm_rows;
 };
 
@@ -70,6 +70,7 @@ inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_
     L.lrank = o;     o += align256((size_t)T * k * 4);
     L.blkcnt = o;    o += align256((size_t)L.nblk * E_local * 4);
     L.blkbase = o;   o += align256((size_t)L.nblk * E_local * 4);
+    L.blkmask = o;   o += align256((size_t)L.nblk * E_local * 8);
     L.tile_off = o;  o += align256((size_t)(E_local + 1) * 4);
     L.tile_flag = o; o += align256((size_t)L.max_tiles * 4);
     L.row_token = o; o += align256((size_t)(L.r_cap + 1) * 4);
