@@ -6,8 +6,12 @@ One step = one mk_dispatch_gemm call over one batch of synthetic input
 (routing, histogram, offsets, slots, row scatter, grouped GEMM), inputs
 resident in HBM before the timed region.  Prints one JSON line:
   value          whole-step TFLOP/s, 2*R*d*N flops per step (R = routed local rows)
-  roofline       the expert-GEMM launch alone (timed with HIP events the
-                 library records around it), against the dense bf16 MFMA peak
+  roofline       the dominant kernel's launch (the fused kernel, or with
+                 --staged the grouped GEMM), timed with HIP events the library
+                 records around it on its stream, against the dense bf16 MFMA
+                 peak (or HBM when the flops per byte sit below the ridge);
+                 traffic = counter-measured HBM bytes per launch when the
+                 committed summary matches the kernel sources
   cpu_baseline   the CPU oracle timed on this host on a bounded sample
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -69,10 +73,14 @@ def _csrc_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str, launch_bytes_alg: float):
-    """HBM traffic per GEMM launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", f"gemm_{workload}_hbm_traffic.json")
+def _traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` (fused or gemm) from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
+    p = _traffic_path(kernel, workload)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -80,6 +88,55 @@ def _traffic(workload: str, launch_bytes_alg: float):
     if t.get("csrc_sha256_16") != _csrc_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def _pmc_per_dispatch(d: str, kernel_substr: str, counter: str) -> float:
+    """Mean value of `counter` over the dispatches of kernels whose name contains kernel_substr, from a
+    rocprofv3 --pmc -f csv output directory."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} samples for '{kernel_substr}' under {d}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic(out_dir: str, workload: str, kernel: str, copy_mib: int) -> dict:
+    """HBM bytes per launch from four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, KiB per
+    dispatch) of the kernel and of a plain copy of copy_mib MiB: each counter is scaled by
+    (bytes the copy moves) / (what the counter reads for the copy)."""
+    substr = {"fused": "k_fused", "gemm": "k_gemm"}[kernel]
+    copy_bytes = copy_mib * 1024 * 1024
+    f_k = _pmc_per_dispatch(os.path.join(out_dir, f"pmc_fetch_{kernel}_{workload}"), substr, "FETCH_SIZE")
+    w_k = _pmc_per_dispatch(os.path.join(out_dir, f"pmc_write_{kernel}_{workload}"), substr, "WRITE_SIZE")
+    f_c = _pmc_per_dispatch(os.path.join(out_dir, "pmc_fetch_copy"), "MulFunctor", "FETCH_SIZE")
+    w_c = _pmc_per_dispatch(os.path.join(out_dir, "pmc_write_copy"), "MulFunctor", "WRITE_SIZE")
+    fetch_scale, write_scale = copy_bytes / f_c, copy_bytes / w_c
+    rec = {"kernel": substr, "workload": workload, "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
+           "copy_bytes": copy_bytes, "copy_fetch_kib": f_c, "copy_write_kib": w_c,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "bytes_per_launch": f_k * fetch_scale + w_k * write_scale, "csrc_sha256_16": _csrc_hash()}
+    with open(_traffic_path(kernel, workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def copy_calibration(mib: int, reps: int = 3):
+    """A plain device copy of a known size, for counter calibration: an elementwise kernel that reads
+    and writes every byte once (torch's multiply by one; a same-dtype copy_ may go to a DMA engine)."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.mul(src, 1, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
 def trace_summary(tr: dict) -> dict:
@@ -142,7 +199,18 @@ def main():
     ap.add_argument("--trace", action="store_true", help="add the fused kernel's phase timeline of the last step")
     ap.add_argument("--staged", action="store_true", help="one launch per step instead of the fused kernel")
     ap.add_argument("--movers", type=int, default=0, help="override the per-shape mover count")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain MIB-MiB device copy (counter calibration) and exit")
+    ap.add_argument("--write-traffic", default="", metavar="DIR",
+                    help="only turn the rocprofv3 --pmc outputs under DIR into profiles/<kernel>_<workload>_hbm_traffic.json")
+    ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"), help="kernel for --write-traffic")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.write_traffic:
+        print(json.dumps(write_traffic(args.write_traffic, args.workload, args.kernel, 1024)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (asked for --gpus {args.gpus}); run with --gpus 1",
               file=sys.stderr)
@@ -213,7 +281,8 @@ def main():
     hit = int((counts > 0).sum())
     alg_bytes = (hit * wl.N * wl.d * 2 + R * wl.N * 2      # weights of hit experts, y_perm
                  + wl.T * wl.d * 2 + (0 if ids_in is not None else wl.d * wl.E * 4))
-    traffic = _traffic(args.workload, alg_bytes)
+    kernel = "gemm" if args.staged else "fused"
+    traffic = _traffic(kernel, args.workload) if not args.movers else None
     # Which roof bounds the GEMM launch: flops per algorithmic byte against the ridge point.
     if flops / max(alg_bytes, 1) >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
@@ -222,7 +291,9 @@ def main():
         gbs = alg_bytes / (gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": traffic, "kernel": "grouped expert GEMM", "launch_ms": round(gemm_ms, 4),
+    roof.update({"traffic": traffic,
+                 "kernel": "grouped expert GEMM (k_gemm)" if args.staged else "fused dispatch+GEMM (k_fused)",
+                 "launch_ms": round(gemm_ms, 4),
                  "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes})
     rec = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -505,7 +505,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
             __syncthreads();
             if (!ok) return;
             wait_ticks += now_ticks() - tw0;
-            gemm_tile_big<C>(g, e, row0, rows_valid, nb * C::BN, ls);
+            gemm_tile_any(g, e, row0, rows_valid, nb * C::BN, ls);
             ++n_done;
         }
     }

@@ -52,17 +52,20 @@ struct GemmArgs {
     int32_t d, N, E_local;
 };
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WN_ = 2>
 struct BigTile {
     static constexpr int BM = BM_;         // token rows per tile
     static constexpr int BN = BN_;         // W rows (output columns) per tile
+    static constexpr int WN = WN_;         // waves along N (the other 4 / WN along M)
+    static constexpr int WM = 4 / WN_;
     static constexpr int BK = 64;          // K per slab: one 128-byte LDS row per tile row
-    static constexpr int NI = BN / 64;     // 32-wide blocks per wave along N
-    static constexpr int MI = BM / 64;     // 32-wide blocks per wave along M
+    static constexpr int NI = BN / WN / 32;   // 32-wide blocks per wave along N
+    static constexpr int MI = BM / WM / 32;   // 32-wide blocks per wave along M
     static constexpr int WL = BN / 32;     // W loads per wave per slab (8 rows x 128 B each)
     static constexpr int XL = BM / 32;     // x loads per wave per slab
     static constexpr int STAGE = BN * BK * 2;   // bytes of one LDS array (W or x half of a slab buffer)
     static constexpr int THREADS = 256;
+    static_assert(NI >= 1 && MI >= 1 && XL <= WL, "tile shape");
 };
 static_assert(BigTile<256, 256>::STAGE == 32768, "an LDS array is 32 KiB");
 
@@ -99,11 +102,10 @@ template <class C, int I0, int I1>
 __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t wsrc, __amdgpu_buffer_rsrc_t xsrc,
                                           const uint32_t (&voff)[C::WL], int slab, SlabRegs<C> &r)
 {
-    static_assert(C::WL == C::XL, "W and x tiles have the same height");
     const uint32_t k0 = (uint32_t)slab * C::BK * 2;
 #pragma unroll
     for (int i = I0; i < I1; ++i)
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < C::WL ? wsrc : xsrc, voff[i % C::WL], k0, 0);
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < C::WL ? wsrc : xsrc, voff[i < C::WL ? i : i - C::WL], k0, 0);
 }
 
 // Writes [I0, I1) of a slab from registers into an LDS buffer (128 B per row,
@@ -116,7 +118,7 @@ __device__ __forceinline__ void store_part(const SlabRegs<C> &r, lds_char_t *wbu
 {
 #pragma unroll
     for (int i = I0; i < I1; ++i)
-        *(lds_v4i_t *)((i < C::WL ? wbuf : xbuf) + (4 * (i % C::WL) + wave) * 1024 + st_off) = r.v[i];
+        *(lds_v4i_t *)((i < C::WL ? wbuf : xbuf) + (4 * (i < C::WL ? i : i - C::WL) + wave) * 1024 + st_off) = r.v[i];
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima).
@@ -136,8 +138,8 @@ __device__ __forceinline__ void load_frags(const lds_char_t *wbuf, const lds_cha
                                            bf16x8_t (&fa)[C::NI], bf16x8_t (&fb)[C::MI])
 {
     typedef __attribute__((address_space(3))) const bf16x8_t lds_frag_t;
-    const lds_char_t *wt = wbuf + (wn * (C::BN / 2)) * 128;
-    const lds_char_t *xt = xbuf + (wm * (C::BM / 2)) * 128;
+    const lds_char_t *wt = wbuf + (wn * (C::BN / C::WN)) * 128;
+    const lds_char_t *xt = xbuf + (wm * (C::BM / C::WM)) * 128;
 #pragma unroll
     for (int i = 0; i < C::NI; ++i) fa[i] = *(lds_frag_t *)(wt + i * 32 * 128 + off);
 #pragma unroll
@@ -162,7 +164,7 @@ template <class C, int NR, int NW>
 __device__ __forceinline__ void sched_step()
 {
     constexpr int NM = C::NI * C::MI;
-    static_assert(NR + NW <= NM, "one MFMA per read or write");
+    if (NR + NW > NM) return;   // too few MFMAs to pair with: the compiler's own order
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
@@ -193,7 +195,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps soffsets scalar
     const int lane = threadIdx.x % kWave;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % C::WN, wm = wave / C::WN;
     const size_t w_first = (size_t)e * a.N + n0;
     const __amdgpu_buffer_rsrc_t wsrc =
         make_rsrc(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
@@ -298,14 +300,14 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
     const int n_limit = a.N - n0;
 #pragma unroll
     for (int j = 0; j < C::MI; ++j) {
-        const int m = wm * (C::BM / 2) + j * 32 + (lane & 31);
+        const int m = wm * (C::BM / C::WM) + j * 32 + (lane & 31);
         if (m >= rows_valid) continue;
         uint16_t *yrow = a.y + (size_t)(row0 + m) * a.N + n0;
 #pragma unroll
         for (int i = 0; i < C::NI; ++i) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = wn * (C::BN / 2) + i * 32 + 8 * g + 4 * (lane >> 5);
+                const int n = wn * (C::BN / C::WN) + i * 32 + 8 * g + 4 * (lane >> 5);
                 if (n < n_limit) {
                     const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][4 * g + 0]) |
                                         ((uint32_t)f32_to_bf16(acc[i][j][4 * g + 1]) << 16);
@@ -316,6 +318,24 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
             }
         }
     }
+}
+
+// The tile heights in use: full row tiles are 256 rows; the last (ragged)
+// row tile of an expert takes the smallest height that covers its rows, so a
+// tail of a few rows (and every tile of a decode-sized batch) costs a fraction
+// of a full tile's matrix work.
+typedef BigTile<256, 256, 2> TileM256;
+typedef BigTile<128, 256, 2> TileM128;
+typedef BigTile<64, 256, 4> TileM64;
+typedef BigTile<32, 256, 4> TileM32;
+
+__device__ __forceinline__ void gemm_tile_any(const GemmArgs &a, int e, int row0, int rows_valid, int n0,
+                                              const LdsStages &ls)
+{
+    if (rows_valid > 128) gemm_tile_big<TileM256>(a, e, row0, rows_valid, n0, ls);
+    else if (rows_valid > 64) gemm_tile_big<TileM128>(a, e, row0, rows_valid, n0, ls);
+    else if (rows_valid > 32) gemm_tile_big<TileM64>(a, e, row0, rows_valid, n0, ls);
+    else gemm_tile_big<TileM32>(a, e, row0, rows_valid, n0, ls);
 }
 
 // Task q -> (expert, row tile, column block), tasks ordered expert-major, then
@@ -366,7 +386,7 @@ __device__ __forceinline__ void gemm_worker(const GemmArgs &a, int w, int G, con
             __syncthreads();
             if (!ok_sh) return;
         }
-        gemm_tile_big<C>(a, p.e, row0, rows_valid, p.nb * C::BN, ls);
+        gemm_tile_any(a, p.e, row0, rows_valid, p.nb * C::BN, ls);
     }
 }
 

@@ -55,7 +55,7 @@ struct RouterCfg {
 };
 
 // The configurations, by index; router_cfg_index picks one from E.
-__host__ __device__ constexpr RouterCfg router_cfg_at(int ci)
+__host__ __device__ __forceinline__ constexpr RouterCfg router_cfg_at(int ci)
 {
     return ci == 0 ? RouterCfg{8, 4, 1, 128}
          : ci == 1 ? RouterCfg{16, 8, 1, 128}
@@ -63,11 +63,11 @@ __host__ __device__ constexpr RouterCfg router_cfg_at(int ci)
          : ci == 3 ? RouterCfg{64, 8, 4, 128}
                    : RouterCfg{64, 4, 1, 16};
 }
-__host__ __device__ constexpr int router_cfg_index(int E)
+__host__ __device__ __forceinline__ constexpr int router_cfg_index(int E)
 {
     return E <= 8 ? 0 : E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 3 : 4;
 }
-__host__ __device__ constexpr RouterCfg router_cfg(int E) { return router_cfg_at(router_cfg_index(E)); }
+__host__ __device__ __forceinline__ constexpr RouterCfg router_cfg(int E) { return router_cfg_at(router_cfg_index(E)); }
 
 __host__ __device__ inline int router_units(int T, int E)
 {
@@ -81,7 +81,7 @@ constexpr int kRouterKC = 64;   // K chunk per LDS stage (a smaller divisor of t
 constexpr int kRouterXS = kRouterKC + 8;
 
 template <int CI>
-__device__ void router_unit_tiled(const RouterArgs &a, int unit, char *x0, char *w0, char *x1, char *w1)
+__device__ __forceinline__ void router_unit_tiled(const RouterArgs &a, int unit, char *x0, char *w0, char *x1, char *w1)
 {
 #pragma clang fp contract(off)
     constexpr int BE = router_cfg_at(CI).BE, TE = router_cfg_at(CI).TE, TT = router_cfg_at(CI).TT;
