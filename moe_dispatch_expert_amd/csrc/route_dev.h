@@ -61,7 +61,7 @@ __host__ __device__ __forceinline__ constexpr RouterCfg router_cfg_at(int ci)
          : ci == 1 ? RouterCfg{16, 8, 1, 128}
          : ci == 2 ? RouterCfg{32, 8, 2, 128}
          : ci == 3 ? RouterCfg{64, 8, 4, 128}
-                   : RouterCfg{64, 4, 1, 16};
+                   : RouterCfg{32, 4, 1, 32};
 }
 __host__ __device__ __forceinline__ constexpr int router_cfg_index(int E)
 {
