@@ -116,7 +116,15 @@ def write_traffic(out_dir: str, workload: str, kernel: str, copy_mib: int) -> di
     f_c = _pmc_per_dispatch(os.path.join(out_dir, "pmc_fetch_copy"), "MulFunctor", "FETCH_SIZE")
     w_c = _pmc_per_dispatch(os.path.join(out_dir, "pmc_write_copy"), "MulFunctor", "WRITE_SIZE")
     fetch_scale, write_scale = copy_bytes / f_c, copy_bytes / w_c
-    rec = {"kernel": substr, "workload": workload, "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
+    run = ("python3 bench.py --staged --steps 3 --warmup 1 --no-cpu-baseline" if kernel == "gemm" else
+           f"python3 bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline")
+    commands = [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} -f csv -d {out_dir}/pmc_{c.split('_')[0].lower()}_{kernel}_{workload} "
+                f"-o run -- {run}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    commands += [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} -f csv -d {out_dir}/pmc_{c.split('_')[0].lower()}_copy -o run "
+                 f"-- python3 bench.py --copy-calibration {copy_mib}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    commands.append(f"python3 bench.py --write-traffic {out_dir} --workload {workload} --kernel {kernel}")
+    rec = {"kernel": substr, "workload": workload, "commands": commands,
+           "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
            "copy_bytes": copy_bytes, "copy_fetch_kib": f_c, "copy_write_kib": w_c,
            "fetch_scale": fetch_scale, "write_scale": write_scale,
            "bytes_per_launch": f_k * fetch_scale + w_k * write_scale, "csrc_sha256_16": _csrc_hash()}
