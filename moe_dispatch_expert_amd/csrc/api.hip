@@ -265,9 +265,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.ga.y = (uint16_t *)y_perm;
         fa.ga.offsets = expert_offsets;
         fa.ga.tile_off = tile_off;
-        fa.ga.tile_flag = nullptr;
         fa.ga.hdr = hdr;
-        fa.ga.spin_limit = spin_limit_ticks();
         fa.ga.d = s->d;
         fa.ga.N = s->N;
         fa.ga.E_local = s->E_local;
@@ -387,10 +385,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     ga.y = (uint16_t *)y_perm;
     ga.offsets = expert_offsets;
     ga.tile_off = tile_off;
-    ga.tile_flag = nullptr;
     ga.hdr = hdr;
-    ga.spin_limit = spin_limit_ticks();
-    ga.epoch = 0;
     ga.d = s->d;
     ga.N = s->N;
     ga.E_local = s->E_local;

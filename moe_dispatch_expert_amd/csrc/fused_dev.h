@@ -468,9 +468,11 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     const int xcd = w % 8;
     const int CH = (G + 7) / 8;
     __shared__ int q_sh;
-    for (int o = 0; o < 8; ++o) {
-        const int x = (xcd + o) % 8;
-        for (;;) {
+    // The next task index, walking this XCD's queue, then the others' (-1: none left).
+    int o = 0;
+    auto claim = [&]() -> int {
+        for (; o < 8; ++o) {
+            const int x = (xcd + o) % 8;
             if (threadIdx.x == 0) {
                 const int i = (int)__hip_atomic_fetch_add(a.xcd_next + x, 1u, __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT);
@@ -479,36 +481,49 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
             __syncthreads();
             const int q = __builtin_amdgcn_readfirstlane(q_sh);   // uniform: keeps the tile loop scalar
             __syncthreads();
-            if (q >= n_tasks) break;
-            // task q -> expert, column block, row tile (consecutive tasks share a W tile)
-            int lo = 0, hi = a.E_local;
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (toff[mid] * NB <= q) lo = mid; else hi = mid;
-            }
-            const int e = lo;
-            const int nt = toff[e + 1] - toff[e];
-            const int rem = q - toff[e] * NB;
-            const int nb = rem / nt, mt = rem % nt;
-            const int cnt_e = off[e + 1] - off[e];
-            const int rows_valid = min(C::BM, cnt_e - mt * C::BM);
-            const int row0 = off[e] + mt * C::BM;
-            const uint32_t units = (uint32_t)((rows_valid + kMoveRows - 1) / kMoveRows);
-            if (n_done == 0) trace_put(a, kTrFirstTask, now_ticks());
-            const uint64_t tw0 = now_ticks();
-            if (threadIdx.x == 0)
-                // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
-                q_sh = wait_flag_geq(a.tile_cnt + toff[e] + mt, units, &a.hdr->err, 2 * a.spin_limit,
-                                     0x10000000u | (uint32_t)(toff[e] + mt)) ? 1 : 0;
-            __syncthreads();
-            const int ok = __builtin_amdgcn_readfirstlane(q_sh);
-            __syncthreads();
-            if (!ok) return;
-            wait_ticks += now_ticks() - tw0;
-            gemm_tile_any(g, e, row0, rows_valid, nb * C::BN, ls);
-            ++n_done;
+            if (q < n_tasks) return q;
         }
-    }
+        return -1;
+    };
+    // Task q -> expert, column block, row tile (consecutive tasks share a W tile).
+    auto job_of = [&](int q) -> TileJob {
+        TileJob t{0, 0, 0, 0};
+        if (q < 0) return t;
+        int lo = 0, hi = a.E_local;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (toff[mid] * NB <= q) lo = mid; else hi = mid;
+        }
+        const int nt = toff[lo + 1] - toff[lo];
+        const int rem = q - toff[lo] * NB;
+        const int mt = rem % nt;
+        t.e = __builtin_amdgcn_readfirstlane(lo);
+        t.row0 = __builtin_amdgcn_readfirstlane(off[lo] + mt * C::BM);
+        t.rows_valid = __builtin_amdgcn_readfirstlane(min(C::BM, off[lo + 1] - off[lo] - mt * C::BM));
+        t.n0 = __builtin_amdgcn_readfirstlane((rem / nt) * C::BN);
+        return t;
+    };
+    // Row tile t's arrival counter and the count of moved units that completes it.
+    auto tile_counter = [&](const TileJob &t) { return a.tile_cnt + toff[t.e] + (t.row0 - off[t.e]) / C::BM; };
+    auto tile_units = [&](const TileJob &t) { return (uint32_t)((t.rows_valid + kMoveRows - 1) / kMoveRows); };
+    // Blocking: wait until all rows of t are moved (false: give up, the error word is set).
+    auto wait = [&](const TileJob &t) -> bool {
+        if (n_done == 0) trace_put(a, kTrFirstTask, now_ticks());
+        const uint64_t tw0 = now_ticks();
+        if (threadIdx.x == 0)
+            // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
+            q_sh = wait_flag_geq(tile_counter(t), tile_units(t), &a.hdr->err, 2 * a.spin_limit,
+                                 0x10000000u | (uint32_t)(tile_counter(t) - a.tile_cnt)) ? 1 : 0;
+        __syncthreads();
+        const int ok = __builtin_amdgcn_readfirstlane(q_sh);
+        __syncthreads();
+        wait_ticks += now_ticks() - tw0;
+        return ok != 0;
+    };
+    auto claim_job = [&]() { return job_of(claim()); };
+    auto done = [&]() { ++n_done; };
+    LambdaSched<decltype(claim_job), decltype(wait), decltype(done)> sc{claim_job, wait, done};
+    gemm_run(g, sc, ls);
     trace_put(a, kTrDone, now_ticks());
     trace_put(a, kTrTasks, n_done);
     trace_put(a, kTrWaitTicks, wait_ticks);

@@ -21,7 +21,8 @@
 //     of the current one (sched_group_barrier), and the one barrier per slab
 //     sits before the last step, so the next slab's first reads overlap it;
 //   - W is the MFMA "A" operand, so each lane ends with 4 consecutive output
-//     columns of one row and the epilogue stores 8 bytes per lane;
+//     columns of one row; the epilogue stages the bf16 tile in LDS and stores
+//     whole 512-byte row segments (16 bytes per lane);
 //   - ragged tails: tile rows past the expert's count read padding or the next
 //     expert's rows and are never stored; W rows past N are clamped.
 #pragma once
@@ -35,9 +36,17 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 
 // The four LDS stage arrays of a GEMM workgroup, as LDS-space pointers (their
 // 32-bit LDS addresses are compile-time constants once the arrays are placed).
+// The arrays are consecutive, 32 KiB each: p[k] == p[0] + k * 32768.
 struct LdsStages {
     lds_char_t *p[4];
 };
+
+// Stage array k (0..3) for a runtime k (address arithmetic: an indexed load of
+// p[] would put the pointer array in scratch memory).
+__device__ __forceinline__ lds_char_t *stage_at(const LdsStages &ls, int k)
+{
+    return ls.p[0] + k * 32768;
+}
 
 struct GemmArgs {
     const uint16_t *x_perm;      // [x_perm_rows, d]
@@ -45,10 +54,7 @@ struct GemmArgs {
     uint16_t *y;                 // [R_cap, N]
     const int32_t *offsets;      // [E_local + 1]
     const int32_t *tile_off;     // [E_local + 1] exclusive prefix of row tiles
-    const uint32_t *tile_flag;   // [max_tiles]: tile ready iff == epoch; nullptr = no waits
     WsHeader *hdr;
-    uint64_t spin_limit;         // wall-clock ticks a wait may take
-    uint32_t epoch;
     int32_t d, N, E_local;
 };
 
@@ -121,6 +127,17 @@ __device__ __forceinline__ void store_part(const SlabRegs<C> &r, lds_char_t *wbu
         *(lds_v4i_t *)((i < C::WL ? wbuf : xbuf) + (4 * (i < C::WL ? i : i - C::WL) + wave) * 1024 + st_off) = r.v[i];
 }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats as two round-to-nearest-even bf16 in one word (lo = a), one
+// conversion instruction for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmem()
@@ -179,8 +196,135 @@ __device__ __forceinline__ void sched_step()
     if (NM - NR - NW > 0) __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NM - NR - NW, 0);
 }
 
-// One BN x BM tile: token rows [row0, row0 + BM) of x_perm (rows_valid of
-// them readable and stored), W rows [n0, n0 + BN) of expert e.
+// Epilogue, first half: the tile's bf16 outputs go into LDS, so that the
+// global stores (second half) are whole 512-byte output row segments (16 bytes
+// per lane, two rows per wave store) instead of 8-byte pieces scattered over
+// 32 rows per store.
+//   - Lane (wave, lane) holds y^T[n][m] for n = nw + i*32 + 8*(v/4) + 4*(lane/32)
+//     + v%4, m = mw + j*32 + lane%32 (32x32 MFMA accumulator layout).  Each
+//     group of 4 consecutive n is one 8-byte write into LDS row m.
+//   - LDS row m of the tile lives in stage array m / 64 at (m % 64) * 512 bytes;
+//     its 16-byte chunk c sits at position c ^ (m % 32), so the 32 rows one
+//     write touches spread over all banks and a row read back is contiguous.
+//   - The caller's stage arrays are free: the main loop ends with a barrier.
+template <class C>
+__device__ __forceinline__ void stage_tile(const f32x16_t (&acc)[C::NI][C::MI], const LdsStages &ls, int wave,
+                                           int lane)
+{
+    static_assert(C::BN == 256 && C::BM <= 256, "an output row segment is 512 bytes; at most 4 x 64 rows");
+    const int wn = wave % C::WN, wm = wave / C::WN;
+    // The swizzled offsets depend only on the lane; computed from an opaque copy of it here, so that the
+    // compiler does not hoist dozens of them out of the tile loop and keep them live (spilled) throughout.
+    int lo_ = lane;
+    asm volatile("" : "+v"(lo_));
+    lane = lo_;
+#pragma unroll
+    for (int j = 0; j < C::MI; ++j) {
+        const int mb = wm * (C::BM / C::WM) + j * 32;   // uniform, a multiple of 32
+        const int m = mb + (lane & 31);
+        lds_char_t *row = stage_at(ls, __builtin_amdgcn_readfirstlane(mb >> 6)) + ((mb & 63) + (lane & 31)) * 512;
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = (wn * (C::BN / C::WN) + i * 32 + 8 * g) >> 3;
+                typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+                *(lds_u32x2_t *)(row + ((c ^ (m & 31)) << 4) + ((lane >> 5) << 3)) =
+                    u32x2_t{pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
+                            pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+            }
+        }
+    }
+}
+
+// Second half of the epilogue: after a barrier that follows stage_tile, wave
+// w stores rows [w * BM / 4, (w + 1) * BM / 4) of the staged tile.
+template <class C>
+__device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, int rows_valid, int n0,
+                                                  const LdsStages &ls, int wave, int lane)
+{
+    // Two rows per instruction; rows are read back in batches of up to 16, then stored, so the LDS
+    // latency is paid once per batch.  (Opaque lane: see stage_tile.)
+    int lo_ = lane;
+    asm volatile("" : "+v"(lo_));
+    lane = lo_;
+    constexpr int RPW = C::BM / 4;
+    constexpr int NS = RPW / 2, BATCH = NS < 8 ? NS : 8;
+    static_assert(RPW % 2 == 0 && NS % BATCH == 0, "rows per wave");
+    const int c = lane & 31;
+    const bool col_ok = n0 + c * 8 < a.N;   // N % 8 == 0: a chunk is wholly inside or outside
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += BATCH) {
+        v4i_t v[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int mb = wave * RPW + 2 * (s0 + b);   // uniform and even: rows mb, mb + 1 share a stage array
+            const int m = mb + (lane >> 5);
+            typedef __attribute__((address_space(3))) const v4i_t lds_cv4i_t;
+            v[b] = *(lds_cv4i_t *)(stage_at(ls, __builtin_amdgcn_readfirstlane(mb >> 6)) +
+                                   ((mb & 63) + (lane >> 5)) * 512 + ((c ^ (m & 31)) << 4));
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int m = wave * RPW + 2 * (s0 + b) + (lane >> 5);
+            if (m < rows_valid && col_ok) *(v4i_t *)(a.y + (size_t)(row0 + m) * a.N + n0 + c * 8) = v[b];
+        }
+    }
+    __syncthreads();   // the stage arrays are free again for the next tile
+}
+
+// The tile heights in use: full row tiles are 256 rows; the last (ragged)
+// row tile of an expert takes the smallest height that covers its rows, so a
+// tail of a few rows (and every tile of a decode-sized batch) costs a fraction
+// of a full tile's matrix work.
+typedef BigTile<256, 256, 2> TileM256;
+typedef BigTile<128, 256, 2> TileM128;
+typedef BigTile<64, 256, 4> TileM64;
+typedef BigTile<32, 256, 4> TileM32;
+
+// One GEMM task: token rows [row0, row0 + BM) of x_perm (rows_valid of them
+// readable and stored), W rows [n0, n0 + BN) of expert e.  rows_valid <= 0:
+// no task.
+struct TileJob {
+    int e, row0, rows_valid, n0;
+};
+
+// The W and x buffer resources of a tile.
+struct TileSrc {
+    __amdgpu_buffer_rsrc_t w, x;
+};
+
+__device__ __forceinline__ TileSrc tile_src(const GemmArgs &a, const TileJob &t)
+{
+    TileSrc s;
+    const size_t w_first = (size_t)t.e * a.N + t.n0;
+    s.w = make_rsrc(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
+    // Only the tile's valid rows are readable: rows past a ragged end return 0 without a memory access
+    // (they may belong to a tile that is not yet moved).
+    s.x = make_rsrc(a.x_perm + (size_t)t.row0 * a.d, (size_t)t.rows_valid * a.d * 2);
+    return s;
+}
+
+// Per-lane byte offsets of the slab loads (the same for every tile of a
+// launch): load i covers tile rows (4 i + wave) * 8 + lane / 8, 16 bytes at
+// chunk lane % 8 of the row's 128-byte slab segment.
+struct SlabOffsets {
+    uint32_t v[TileM256::WL];
+};
+
+__device__ __forceinline__ SlabOffsets slab_offsets(const GemmArgs &a, int wave, int lane)
+{
+    SlabOffsets o;
+    const uint32_t row_bytes = (uint32_t)a.d * 2;
+#pragma unroll
+    for (int i = 0; i < TileM256::WL; ++i)
+        o.v[i] = (uint32_t)((4 * i + wave) * 8 + (lane >> 3)) * row_bytes + (uint32_t)(lane & 7) * 16u;
+    return o;
+}
+
+// One tile.  After the main loop the workgroup claims its next task
+// (sc.claim() into `next`; not earlier, so that no workgroup holds a second
+// task while others still look for their first), then runs the epilogue.
 //
 // Slab j (K = 64 j .. 64 j + 63) is computed from LDS buffer j % 2 (W in
 // ls.p[2 (j % 2)], x in ls.p[2 (j % 2) + 1]) in four K = 16 steps, with the
@@ -189,27 +333,18 @@ __device__ __forceinline__ void sched_step()
 // j - 1 was last read before the previous barrier), load slab j + 3 into the
 // registers just freed, barrier, then read step 0 of slab j + 1 during step 3.
 // Slab s lives in register set s % 2, loaded two slabs before it is written.
-template <class C>
-__device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0, int rows_valid, int n0,
-                                              const LdsStages &ls)
+template <class C, class Sched>
+__device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &job, TileJob &next, Sched &sc,
+                                              const LdsStages &ls, const SlabOffsets &so)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps soffsets scalar
     const int lane = threadIdx.x % kWave;
     const int wn = wave % C::WN, wm = wave / C::WN;
-    const size_t w_first = (size_t)e * a.N + n0;
-    const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
-    // Only the tile's valid rows are readable: rows past a ragged end return 0 without a memory access
-    // (they may belong to a tile that is not yet moved).
-    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(a.x_perm + (size_t)row0 * a.d, (size_t)rows_valid * a.d * 2);
+    const TileSrc src = tile_src(a, job);
+    const uint32_t(&voff)[TileM256::WL] = so.v;
     // Loads of slabs past the end go to empty resources: they read 0 without a memory access, and
     // keep the number of loads in flight the same on every path.
     const __amdgpu_buffer_rsrc_t wnone = make_rsrc(a.w, 0), xnone = make_rsrc(a.x_perm, 0);
-    const uint32_t row_bytes = (uint32_t)a.d * 2;
-    uint32_t voff[C::WL];
-#pragma unroll
-    for (int i = 0; i < C::WL; ++i)
-        voff[i] = (uint32_t)((4 * i + wave) * 8 + (lane >> 3)) * row_bytes + (uint32_t)(lane & 7) * 16u;
     const uint32_t st_off = (uint32_t)(lane >> 3) * 128u + (uint32_t)(((lane & 7) ^ ((lane >> 4) + 4 * (wave & 1))) << 4);
     const int KK = __builtin_amdgcn_readfirstlane(a.d / C::BK);   // even (d % 128 == 0); uniform
 
@@ -232,10 +367,10 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
     constexpr int P1 = (NL + 2) / 3, P2 = (2 * NL + 2) / 3;   // the slab write in three parts
     constexpr int NR = C::NI + C::MI;
     SlabRegs<C> r0, r1;
-    load_part<C, 0, NL>(wsrc, xsrc, voff, 0, r0);
-    load_part<C, 0, NL>(wsrc, xsrc, voff, 1, r1);
+    load_part<C, 0, NL>(src.w, src.x, voff, 0, r0);
+    load_part<C, 0, NL>(src.w, src.x, voff, 1, r1);
     store_part<C, 0, NL>(r0, wb[0], xb[0], wave, st_off);
-    load_part<C, 0, NL>(KK > 2 ? wsrc : wnone, KK > 2 ? xsrc : xnone, voff, 2, r0);
+    load_part<C, 0, NL>(KK > 2 ? src.w : wnone, KK > 2 ? src.x : xnone, voff, 2, r0);
     __syncthreads();
     bf16x8_t fa0[C::NI], fb0[C::MI], fa1[C::NI], fb1[C::MI];
     load_frags<C>(wb[0], xb[0], wn, wm, frag_off[0], fa0, fb0);
@@ -248,14 +383,14 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
 #define MK_GEMM_SLAB(B, RN, J, NEXT)                                                                   \
     do {                                                                                               \
         const bool ahead_ = __builtin_amdgcn_readfirstlane((J) + 3 < KK);                              \
-        const __amdgpu_buffer_rsrc_t wl_ = ahead_ ? wsrc : wnone, xl_ = ahead_ ? xsrc : xnone;         \
+        const __amdgpu_buffer_rsrc_t wl_ = ahead_ ? src.w : wnone, xl_ = ahead_ ? src.x : xnone;       \
         lds_char_t *const wo_ = wb[1 - (B)];                                                           \
         lds_char_t *const xo_ = xb[1 - (B)];                                                           \
         load_frags<C>(wb[B], xb[B], wn, wm, frag_off[1], fa1, fb1);                                    \
         mfma_block<C>(fa0, fb0, acc);                                                                  \
         if (NEXT) {                                                                                    \
             store_part<C, 0, P1>(RN, wo_, xo_, wave, st_off);                                          \
-            load_part<C, 0, P1>(wl_, xl_, voff, (J) + 3, RN);                                          \
+            load_part<C, 0, P1>(wl_, xl_, voff, (J) + 3, RN);                                      \
             sched_step<C, NR, P1>();                                                                   \
         } else {                                                                                       \
             sched_step<C, NR, 0>();                                                                    \
@@ -264,7 +399,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
         mfma_block<C>(fa1, fb1, acc);                                                                  \
         if (NEXT) {                                                                                    \
             store_part<C, P1, P2>(RN, wo_, xo_, wave, st_off);                                         \
-            load_part<C, P1, P2>(wl_, xl_, voff, (J) + 3, RN);                                         \
+            load_part<C, P1, P2>(wl_, xl_, voff, (J) + 3, RN);                                     \
             sched_step<C, NR, P2 - P1>();                                                              \
         } else {                                                                                       \
             sched_step<C, NR, 0>();                                                                    \
@@ -273,7 +408,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
         mfma_block<C>(fa0, fb0, acc);                                                                  \
         if (NEXT) {                                                                                    \
             store_part<C, P2, NL>(RN, wo_, xo_, wave, st_off);                                         \
-            load_part<C, P2, NL>(wl_, xl_, voff, (J) + 3, RN);                                         \
+            load_part<C, P2, NL>(wl_, xl_, voff, (J) + 3, RN);                                     \
             sched_step<C, NR, NL - P2>();                                                              \
             __builtin_amdgcn_sched_barrier(0);                                                         \
             __syncthreads();                                                                           \
@@ -294,58 +429,56 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, int e, int row0
     MK_GEMM_SLAB(0, r1, j, true);
     MK_GEMM_SLAB(1, r0, j + 1, false);
 #undef MK_GEMM_SLAB
-    __syncthreads();   // every wave is done with the stages before the next tile refills them
 
-    // epilogue: lane holds y^T[n][m] for n = base + 8*(v/4) + 4*(lane/32) + v%4, m = lane%32
-    const int n_limit = a.N - n0;
-#pragma unroll
-    for (int j = 0; j < C::MI; ++j) {
-        const int m = wm * (C::BM / C::WM) + j * 32 + (lane & 31);
-        if (m >= rows_valid) continue;
-        uint16_t *yrow = a.y + (size_t)(row0 + m) * a.N + n0;
-#pragma unroll
-        for (int i = 0; i < C::NI; ++i) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = wn * (C::BN / C::WN) + i * 32 + 8 * g + 4 * (lane >> 5);
-                if (n < n_limit) {
-                    const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][4 * g + 0]) |
-                                        ((uint32_t)f32_to_bf16(acc[i][j][4 * g + 1]) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][4 * g + 2]) |
-                                        ((uint32_t)f32_to_bf16(acc[i][j][4 * g + 3]) << 16);
-                    *(uint2 *)(yrow + n) = make_uint2(lo, hi);
-                }
-            }
-        }
+    // Epilogue: claim the next task, stage the outputs in LDS, store them as whole row segments.
+    __syncthreads();   // every wave is done with the stages before the epilogue reuses them
+    stage_tile<C>(acc, ls, wave, lane);
+    next = sc.claim();
+    __syncthreads();   // the staged tile is complete
+    store_staged_tile<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
+}
+
+// A Sched made of three callables.
+template <class Cl, class Wa, class Do>
+struct LambdaSched {
+    Cl &claim_;
+    Wa &wait_;
+    Do &done_;
+    __device__ TileJob claim() { return claim_(); }
+    __device__ bool wait(const TileJob &t) { return wait_(t); }
+    __device__ void done() { done_(); }
+};
+
+// The persistent tile loop.  Sched provides: claim() -> the next TileJob of
+// this workgroup (rows_valid <= 0: none left); wait(job) -> false if the
+// workgroup must stop (a failed wait for the job's rows); done() after each
+// tile.
+template <class Sched>
+__device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const LdsStages &ls)
+{
+    const SlabOffsets so = slab_offsets(a, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), threadIdx.x % kWave);
+    TileJob job = sc.claim();
+    while (job.rows_valid > 0) {
+        if (!sc.wait(job)) return;
+        TileJob next;
+        if (job.rows_valid > 128) gemm_tile_big<TileM256>(a, job, next, sc, ls, so);
+        else if (job.rows_valid > 64) gemm_tile_big<TileM128>(a, job, next, sc, ls, so);
+        else if (job.rows_valid > 32) gemm_tile_big<TileM64>(a, job, next, sc, ls, so);
+        else gemm_tile_big<TileM32>(a, job, next, sc, ls, so);
+        sc.done();
+        job = next;
     }
 }
 
-// The tile heights in use: full row tiles are 256 rows; the last (ragged)
-// row tile of an expert takes the smallest height that covers its rows, so a
-// tail of a few rows (and every tile of a decode-sized batch) costs a fraction
-// of a full tile's matrix work.
-typedef BigTile<256, 256, 2> TileM256;
-typedef BigTile<128, 256, 2> TileM128;
-typedef BigTile<64, 256, 4> TileM64;
-typedef BigTile<32, 256, 4> TileM32;
-
-__device__ __forceinline__ void gemm_tile_any(const GemmArgs &a, int e, int row0, int rows_valid, int n0,
-                                              const LdsStages &ls)
+// Task q -> its tile; tasks are ordered expert-major, then column block, then
+// row tile, so consecutive tasks share one W tile.  q >= n_tasks: no task.
+template <class C>
+__device__ __forceinline__ TileJob job_of_task(const GemmArgs &a, const int32_t *tile_off, const int32_t *offsets,
+                                               int NB, int n_tasks, int q)
 {
-    if (rows_valid > 128) gemm_tile_big<TileM256>(a, e, row0, rows_valid, n0, ls);
-    else if (rows_valid > 64) gemm_tile_big<TileM128>(a, e, row0, rows_valid, n0, ls);
-    else if (rows_valid > 32) gemm_tile_big<TileM64>(a, e, row0, rows_valid, n0, ls);
-    else gemm_tile_big<TileM32>(a, e, row0, rows_valid, n0, ls);
-}
-
-// Task q -> (expert, row tile, column block), tasks ordered expert-major, then
-// column block, then row tile, so consecutive tasks share one W tile.
-struct TaskPos {
-    int e, mt, nb;
-};
-__device__ __forceinline__ TaskPos decode_task(const int32_t *tile_off, int E_local, int NB, int q)
-{
-    int lo = 0, hi = E_local;   // find e: tile_off[e]*NB <= q < tile_off[e+1]*NB
+    TileJob t{0, 0, 0, 0};
+    if (q >= n_tasks) return t;
+    int lo = 0, hi = a.E_local;   // find e: tile_off[e]*NB <= q < tile_off[e+1]*NB
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (tile_off[mid] * NB <= q) lo = mid; else hi = mid;
@@ -353,11 +486,12 @@ __device__ __forceinline__ TaskPos decode_task(const int32_t *tile_off, int E_lo
     const int e = lo;
     const int nt = tile_off[e + 1] - tile_off[e];
     const int rem = q - tile_off[e] * NB;
-    TaskPos p;
-    p.e = e;
-    p.nb = rem / nt;
-    p.mt = rem % nt;
-    return p;
+    const int nb = rem / nt, mt = rem % nt;
+    t.e = e;
+    t.row0 = offsets[e] + mt * C::BM;
+    t.rows_valid = min(C::BM, offsets[e + 1] - offsets[e] - mt * C::BM);
+    t.n0 = nb * C::BN;
+    return t;
 }
 
 // Persistent workgroup loop over GEMM tasks.  Workgroup w (of G, G % 8 == 0)
@@ -367,27 +501,21 @@ __device__ __forceinline__ TaskPos decode_task(const int32_t *tile_off, int E_lo
 template <class C>
 __device__ __forceinline__ void gemm_worker(const GemmArgs &a, int w, int G, const LdsStages &ls)
 {
-    const int n_tiles = (int)a.hdr->n_tiles;
-    const int NB = (a.N + C::BN - 1) / C::BN;
-    const int n_tasks = n_tiles * NB;
-    const int slot = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
-    for (int base = 0; base < n_tasks; base += G) {
-        const int q = base + slot;
-        if (q >= n_tasks) continue;
-        const TaskPos p = decode_task(a.tile_off, a.E_local, NB, q);
-        const int cnt = a.offsets[p.e + 1] - a.offsets[p.e];
-        const int rows_valid = min(C::BM, cnt - p.mt * C::BM);
-        const int row0 = a.offsets[p.e] + p.mt * C::BM;
-        if (a.tile_flag) {
-            __shared__ int ok_sh;
-            if (threadIdx.x == 0)
-                ok_sh = wait_flag_eq(a.tile_flag + a.tile_off[p.e] + p.mt, a.epoch, &a.hdr->err,
-                                     a.spin_limit, 0x10000000u | (uint32_t)(a.tile_off[p.e] + p.mt));
-            __syncthreads();
-            if (!ok_sh) return;
+    struct Sched {
+        const GemmArgs &a;
+        int NB, n_tasks, q, G;
+        __device__ TileJob claim()
+        {
+            const TileJob t = job_of_task<C>(a, a.tile_off, a.offsets, NB, n_tasks, q);
+            q += G;
+            return t;
         }
-        gemm_tile_any(a, p.e, row0, rows_valid, p.nb * C::BN, ls);
-    }
+        __device__ bool wait(const TileJob &) { return true; }
+        __device__ void done() {}
+    };
+    const int NB = (a.N + C::BN - 1) / C::BN;
+    Sched sc{a, NB, (int)a.hdr->n_tiles * NB, (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w, G};
+    gemm_run(a, sc, ls);
 }
 
 }  // namespace mk

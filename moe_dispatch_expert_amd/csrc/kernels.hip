@@ -77,30 +77,23 @@ __global__ __launch_bounds__(256) void k_move(SrcRows src, const int32_t *row_to
 template <class C>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE], s1[C::STAGE], s2[C::STAGE], s3[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
     LdsStages ls;
-    ls.p[0] = (lds_char_t *)s0;
-    ls.p[1] = (lds_char_t *)s1;
-    ls.p[2] = (lds_char_t *)s2;
-    ls.p[3] = (lds_char_t *)s3;
+    for (int k = 0; k < 4; ++k) ls.p[k] = (lds_char_t *)(stg + k * C::STAGE);
     gemm_worker<C>(a, blockIdx.x, gridDim.x, ls);
 }
 
 template <class C>
 __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) char s0[C::STAGE], s1[C::STAGE], s2[C::STAGE], s3[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
     __shared__ int32_t off[1025], toff[1025], uoff[1025];
     LdsStages ls;
-    ls.p[0] = (lds_char_t *)s0;
-    ls.p[1] = (lds_char_t *)s1;
-    ls.p[2] = (lds_char_t *)s2;
-    ls.p[3] = (lds_char_t *)s3;
     char *st[4];   // filled one by one: a constant initializer would become a static one
-    st[0] = s0;
-    st[1] = s1;
-    st[2] = s2;
-    st[3] = s3;
+    for (int k = 0; k < 4; ++k) {
+        st[k] = stg + k * C::STAGE;
+        ls.p[k] = (lds_char_t *)st[k];
+    }
     fused_kernel_body<C>(a, st, ls, off, toff, uoff);
 }
 
