@@ -158,6 +158,7 @@ def trace_summary(tr: dict) -> dict:
         v = v[v > 0]
         if v.size:
             out[name + "_max_us"] = us(v.max())
+            out[name + "_p50_us"] = us(np.median(v))
     ft = tr["first_task"][live]
     ft = ft[ft > 0]
     if ft.size:

@@ -253,6 +253,8 @@ __device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, i
     static_assert(RPW % 2 == 0 && NS % BATCH == 0, "rows per wave");
     const int c = lane & 31;
     const bool col_ok = n0 + c * 8 < a.N;   // N % 8 == 0: a chunk is wholly inside or outside
+    // Rows past rows_valid fall outside the resource: those stores are dropped.
+    const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(a.y + (size_t)row0 * a.N + n0, (size_t)rows_valid * a.N * 2);
 #pragma unroll
     for (int s0 = 0; s0 < NS; s0 += BATCH) {
         v4i_t v[BATCH];
@@ -267,7 +269,7 @@ __device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, i
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
             const int m = wave * RPW + 2 * (s0 + b) + (lane >> 5);
-            if (m < rows_valid && col_ok) *(v4i_t *)(a.y + (size_t)(row0 + m) * a.N + n0 + c * 8) = v[b];
+            if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(v[b], ysrc, (uint32_t)(m * a.N + c * 8) * 2u, 0, 0);
         }
     }
     __syncthreads();   // the stage arrays are free again for the next tile

@@ -25,10 +25,20 @@ struct RouterArgs {
     int32_t T, d, E;
 };
 
+// Row t of the token matrix.  The shard pointers are kernel arguments: when
+// every lane of the wave reads from one shard (always for S == 1, and for
+// whole blocks of rows otherwise) the pointer is a scalar load; a per-lane
+// shard index would need a vector load of the pointer, whose wait would also
+// drain every load the wave has in flight.
 __device__ __forceinline__ const uint16_t *token_row(const SrcRows &s, int t, int d)
 {
+    if (s.S == 1) return s.p[0] + (size_t)t * d;
     const int sh = t / s.rows_per_src;
-    return s.p[sh] + (size_t)(t - sh * s.rows_per_src) * d;
+    const int sh0 = __builtin_amdgcn_readfirstlane(sh);
+    const uint16_t *base;
+    if (__builtin_amdgcn_ballot_w64(sh != sh0) == 0) base = s.p[sh0];
+    else base = s.p[sh];
+    return base + (size_t)(t - sh * s.rows_per_src) * d;
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -114,15 +124,20 @@ __device__ __forceinline__ void router_unit_tiled(const RouterArgs &a, int unit,
     // wait counts exact).
     u32x4_t xrA[XPT], xrB[XPT];
     float wrA[WPT], wrB[WPT];
+    // The token rows this thread fetches from, fixed for the whole unit: computed once, so the
+    // chunk loop has no pointer loads (whose waits would drain the prefetches in flight).
+    const uint16_t *xrow[XPT];
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+        const int c = min(tid + j * 256, BT * cpr - 1);
+        const int row = c / cpr, cc = c - row * cpr;
+        const int t = min(tb * BT + row, a.T - 1);
+        xrow[j] = token_row(a.src, t, a.d) + k_base + cc * 8;
+    }
 #define MK_ROUTER_FETCH(xr, wrg, chunk)                                                           \
     do {                                                                                          \
         const int k0_ = min((chunk), nk - 1) * KC;                                                \
-        _Pragma("unroll") for (int j = 0; j < XPT; ++j) {                                         \
-            const int c = min(tid + j * 256, BT * cpr - 1);                                       \
-            const int row = c / cpr, cc = c - row * cpr;                                          \
-            const int t = min(tb * BT + row, a.T - 1);                                            \
-            xr[j] = *(const u32x4_t *)(token_row(a.src, t, a.d) + k_base + k0_ + cc * 8);        \
-        }                                                                                         \
+        _Pragma("unroll") for (int j = 0; j < XPT; ++j) xr[j] = *(const u32x4_t *)(xrow[j] + k0_); \
         _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                         \
             const int c = min(tid + j * 256, KC * BE - 1);                                        \
             const int kk = c / BE, e = c - kk * BE;                                               \
