@@ -154,7 +154,7 @@ mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *
  *   *ticks_per_us per microsecond); 10 GEMM tasks run, 11 ticks spent
  *   waiting for tiles, 12 hardware XCD id, 13 mover units copied, 14 ticks
  *   copying rows, 15 ticks publishing moved units, 16 token-parallel
- *   selection done (E > 64 only); words 17.. are zero.
+ *   selection done (routing inside only); words 17.. are zero.
  * For profiling the overlap of the roles; the host reads it after a sync. */
 mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,
                                   int32_t *words, int32_t *ticks_per_us);

@@ -291,6 +291,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.tile_off = tile_off;
         fa.tile_cnt = (uint32_t *)(ws + L.tile_flag);
         fa.xcd_next = hdr->xcd_next;
+        fa.bar_flag = (uint32_t *)(ws + L.bar_flag);
         fa.hdr = hdr;
         fa.spin_limit = spin_limit_ticks();
         fa.T = s->T;
@@ -304,6 +305,7 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         static_assert(256 % kMoveRows == 0, "mover units tile the GEMM row tiles");
         fa.has_sim = (src->chunk_rows > 0 && src->sim_delay_us) ? 1 : 0;
         const int G = grid - fa.has_sim;
+        if (G > kBarrierWGs) return MK_EUNSUPPORTED;
         fa.n_mover = tu.n_mover_wg < 1 ? 1 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);
         fa.max_tiles = L.max_tiles;
         fa.ticks_per_us = (uint32_t)ticks_per_us();

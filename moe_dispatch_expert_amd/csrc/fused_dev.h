@@ -54,6 +54,7 @@ struct FusedArgs {
     int32_t *tile_off;           // [E_local + 1]
     uint32_t *tile_cnt;          // [max_tiles] row chunks moved into each tile (reset every call)
     uint32_t *xcd_next;          // [8] per-XCD task counters (reset every call)
+    uint32_t *bar_flag;          // [kBarrierWGs] grid barrier: generation each workgroup has reached
     WsHeader *hdr;
     uint64_t spin_limit;
     int32_t T, d, E, k, e_begin, E_local, nblk, bm;
@@ -81,22 +82,52 @@ __device__ __forceinline__ int fused_participants(const FusedArgs &a) { return (
 // Grid barrier over the participating workgroups (the simulator stays out).
 __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detail)
 {
+    // Arrival: each workgroup publishes its writes and then its own arrival word (release store, so
+    // no two workgroups contend for one counter); workgroup 0 polls all the words, then releases
+    // the generation that the others wait for.  Every participant reads the generation before its
+    // arrival, so all agree on it; it does not change until all have arrived.
     wait_vmem_all();   // every wave's stores of the phase have reached L2
     __syncthreads();
+    __shared__ uint32_t g_shared;
     __shared__ int ok_shared;
     if (threadIdx.x == 0) {
-        const uint32_t g = ld_acquire(&a.hdr->bar_gen);
-        const uint32_t arrived =
-            __hip_atomic_fetch_add(&a.hdr->bar_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        bool ok = true;
-        if (arrived == (uint32_t)fused_participants(a)) {
-            __hip_atomic_store(&a.hdr->bar_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            st_release(&a.hdr->bar_gen, g + 1u);
-        } else {
-            ok = wait_flag_eq(&a.hdr->bar_gen, g + 1u, &a.hdr->err, a.spin_limit, detail);
-        }
-        ok_shared = ok ? 1 : 0;
+        const uint32_t g = ld_relaxed(&a.hdr->bar_gen);
+        g_shared = g;
+        st_release(a.bar_flag + blockIdx.x, g + 1u);
     }
+    __syncthreads();
+    const uint32_t want = g_shared + 1u;
+    bool ok = true;
+    if (blockIdx.x == 0) {
+        const int G = fused_participants(a);
+        const uint64_t t0 = now_ticks();
+        for (;;) {
+            int here = 1;
+            for (int i = threadIdx.x; i < G; i += blockDim.x) here &= ld_relaxed(a.bar_flag + i) == want;
+            int bad = 0;
+            if (threadIdx.x == 0) {
+                if (ld_relaxed(&a.hdr->err) != 0) {
+                    bad = 1;
+                } else if (now_ticks() - t0 > a.spin_limit) {
+                    raise_error(&a.hdr->err, kErrTimeout, detail);
+                    bad = 1;
+                }
+            }
+            if (__syncthreads_and(here)) break;   // both reductions are workgroup-uniform
+            if (__syncthreads_or(bad)) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (ok && threadIdx.x == 0) {
+            fence_acquire_agent();
+            st_release(&a.hdr->bar_gen, want);
+        }
+        __syncthreads();
+        return ok;
+    }
+    if (threadIdx.x == 0) ok_shared = wait_flag_eq(&a.hdr->bar_gen, want, &a.hdr->err, a.spin_limit, detail) ? 1 : 0;
     __syncthreads();
     return ok_shared != 0;
 }
@@ -331,9 +362,9 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     if (w == 0 && threadIdx.x < 8) a.xcd_next[threadIdx.x] = 0u;
     for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x) a.tile_cnt[i] = 0u;
 
-    // Token-per-wave selection (E > 64) builds the block masks with atomic ORs:
+    // The token-per-wave selection builds the block masks with atomic ORs:
     // clear them before barrier A.
-    const bool wave_topk = !a.ids_in && a.E > 64;
+    const bool wave_topk = !a.ids_in;
     if (wave_topk)
         for (int i = w * (int)blockDim.x + threadIdx.x; i < a.nblk * a.E_local; i += G * (int)blockDim.x)
             a.ca.blkmask[i] = 0ull;
@@ -346,11 +377,11 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
         if (!fused_barrier(a, 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
     }
-    // ---- phase 2: top-k, histogram and ranks.  E > 64: the selection runs
-    // token-parallel over every workgroup (one token per wave) and ORs each
-    // token into its block's mask of every local expert it chose; after the
-    // barrier the masks give the counts and ranks.  E <= 64 or given ids: per
-    // 64-token block, selection (or copy) and histogram in one workgroup.
+    // ---- phase 2: top-k, histogram and ranks.  Routing inside: the selection
+    // runs token-parallel over every workgroup (one token per wave) and ORs
+    // each token into its block's mask of every local expert it chose; after
+    // the barrier the masks give the counts and ranks.  Given ids: per 64-token
+    // block, copy and histogram in one workgroup.
     if (wave_topk) {
         const int units = topk_wave_units(a.T);
         for (int u = w; u < units; u += G) topk_wave_unit(a.ta, u);
@@ -363,18 +394,14 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
         int32_t *cnt_lds = (int32_t *)(st[1] + kTokBlock * kMaxK * 4);  // E_local ints (<= 4 KiB)
         uint64_t *mask_lds = (uint64_t *)(st[1] + 16384);               // E_local uint64 (<= 8 KiB)
         for (int blk = w; blk < a.nblk; blk += G) {
-            if (!a.ids_in) {
-                topk_block(a.ta, blk, (float *)st[0], ids_lds);
-            } else {
-                const int base_t = blk * kTokBlock;
-                const int n_t = min(kTokBlock, a.T - base_t);
-                for (int i = threadIdx.x; i < n_t * a.k; i += blockDim.x) {
-                    const size_t o = (size_t)base_t * a.k + i;
-                    const int32_t id = a.ids_in[o];
-                    ids_lds[i] = id;
-                    a.ta.ids[o] = id;
-                    if (a.ids_user) a.ids_user[o] = id;
-                }
+            const int base_t = blk * kTokBlock;
+            const int n_t = min(kTokBlock, a.T - base_t);
+            for (int i = threadIdx.x; i < n_t * a.k; i += blockDim.x) {
+                const size_t o = (size_t)base_t * a.k + i;
+                const int32_t id = a.ids_in[o];
+                ids_lds[i] = id;
+                a.ta.ids[o] = id;
+                if (a.ids_user) a.ids_user[o] = id;
             }
             __syncthreads();
             count_block(a.ca, blk, ids_lds, cnt_lds, mask_lds);
@@ -524,6 +551,9 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     auto done = [&]() { ++n_done; };
     LambdaSched<decltype(claim_job), decltype(wait), decltype(done)> sc{claim_job, wait, done};
     gemm_run(g, sc, ls);
+    // Write this XCD's dirty L2 lines (the outputs) back now, while other workgroups still compute,
+    // rather than leaving them to the next call's first release.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     trace_put(a, kTrDone, now_ticks());
     trace_put(a, kTrTasks, n_done);
     trace_put(a, kTrWaitTicks, wait_ticks);

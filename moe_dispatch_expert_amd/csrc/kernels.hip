@@ -21,17 +21,7 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a)
     router_unit(a, blockIdx.x, st0, st0 + xb, st1, st1 + xb);
 }
 
-__global__ __launch_bounds__(256) void k_topk(TopkArgs ta, CountArgs ca, int do_count)
-{
-    __shared__ float lg[kTopkLdsBytes / 4];
-    __shared__ int32_t ids_lds[kTokBlock * kMaxK];
-    __shared__ int32_t cnt_lds[1024];
-    __shared__ uint64_t mask_lds[1024];
-    topk_block(ta, blockIdx.x, lg, ids_lds);
-    if (do_count) count_block(ca, blockIdx.x, ids_lds, cnt_lds, mask_lds);
-}
-
-// Token-per-wave top-k (E > 64), four tokens per workgroup.
+// Token-per-wave top-k, four tokens per workgroup.
 __global__ __launch_bounds__(256) void k_topk_wave(TopkArgs ta) { topk_wave_unit(ta, blockIdx.x); }
 
 __global__ __launch_bounds__(256) void k_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user,
@@ -107,17 +97,12 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 
 hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s)
 {
-    if (ta.E > 64) {
-        // token-parallel selection, then the per-block histogram from the ids it wrote
-        hipLaunchKernelGGL(k_topk_wave, dim3(topk_wave_units(ta.T)), dim3(256), 0, s, ta);
-        if (!do_count) return hipGetLastError();
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_count_given(ta.ids, ta.ids, nullptr, ca, s);
-    }
-    const int nblk = (ta.T + kTokBlock - 1) / kTokBlock;
-    hipLaunchKernelGGL(k_topk, dim3(nblk), dim3(256), 0, s, ta, ca, do_count ? 1 : 0);
-    return hipGetLastError();
+    // token-parallel selection, then the per-block histogram from the ids it wrote
+    hipLaunchKernelGGL(k_topk_wave, dim3(topk_wave_units(ta.T)), dim3(256), 0, s, ta);
+    if (!do_count) return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_count_given(ta.ids, ta.ids, nullptr, ca, s);
 }
 
 hipError_t launch_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user, const CountArgs &ca,

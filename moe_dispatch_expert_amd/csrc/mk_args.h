@@ -35,7 +35,7 @@ struct SrcFlags {
 struct WsHeader {
     uint32_t err;          // 0 or an mk_status code
     uint32_t err_detail;
-    uint32_t bar_count;    // grid barrier arrivals (returns to 0)
+    uint32_t bar_spare;    // unused
     uint32_t bar_gen;      // grid barrier generation (grows by one per barrier)
     uint32_t n_tiles;      // GEMM row tiles of the current call
     uint32_t R;            // routed local rows of the current call
@@ -48,9 +48,10 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 // Byte offsets of the workspace segments (all 256-byte aligned).
 constexpr int kTraceWGs = 1024;   // workgroups the trace segment has room for
 constexpr int kTraceWords = 32;   // uint64 records per workgroup
+constexpr int kBarrierWGs = 1024; // workgroups the grid barrier's arrival words have room for
 
 struct WsLayout {
-    size_t hdr, part, ids, lrank, blkcnt, blkbase, blkmask, tile_off, tile_flag, row_token, trace, x_perm, total;
+    size_t hdr, bar_flag, part, ids, lrank, blkcnt, blkbase, blkmask, tile_off, tile_flag, row_token, trace, x_perm, total;
     int32_t nblk, max_tiles, r_cap, x_perm_rows;
 };
 
@@ -65,6 +66,7 @@ inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_
     L.x_perm_rows = L.r_cap + 256;   // a full tile past the last row stays in bounds
     size_t o = 0;
     L.hdr = o;       o += align256(sizeof(WsHeader));
+    L.bar_flag = o;  o += align256((size_t)kBarrierWGs * 4);
     L.part = o;      o += align256((size_t)kRouterSegments * T * E * 4);
     L.ids = o;       o += align256((size_t)T * k * 4);
     L.lrank = o;     o += align256((size_t)T * k * 4);

@@ -241,91 +241,8 @@ struct TopkArgs {
     int32_t T, E, k, e_begin, E_local;
 };
 
-// Row stride (floats) of one token's logits in LDS: padded by one for E <= 64,
-// where one lane reads one token's row, so that the lanes' rows fall in
-// different banks; unpadded above, where one wave reads one row.
-__host__ __device__ inline int topk_lg_stride(int E) { return E <= 64 ? E + 1 : E; }
-
-constexpr int kTopkLdsBytes = 32768;   // LDS for the logits of one top-k sub-block
-
-// Tokens per LDS sub-block of the top-k step: SB rows of logits fit in kTopkLdsBytes.
-__host__ __device__ inline int topk_subblock(int E)
-{
-    int sb = kTokBlock;
-    while (sb > 1 && (long)sb * topk_lg_stride(E) * 4 > kTopkLdsBytes) sb >>= 1;
-    return sb;
-}
-
-// Logits of tokens [t0, t0 + nt) into LDS: lg[tl * stride + e] = ((P0 + P1) + ... + P7) + bias.
-// Each thread keeps the 8 partial loads of 4 logits in flight.
-__device__ __forceinline__ void block_logits(const TopkArgs &a, int t0, int nt, float *lg)
-{
-#pragma clang fp contract(off)
-    const int n = nt * a.E;
-    const size_t sstride = (size_t)a.E * a.T;
-    const float *blk = a.part + (size_t)t0 * a.E;   // a segment's [nt][E] partials are contiguous
-    for (int base = 0; base < n; base += 4 * (int)blockDim.x) {
-        float p[4][kRouterSegments];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = base + u * (int)blockDim.x + (int)threadIdx.x;
-            const int i2 = idx < n ? idx : n - 1;
-#pragma unroll
-            for (int s = 0; s < kRouterSegments; ++s) p[u][s] = blk[s * sstride + i2];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int idx = base + u * (int)blockDim.x + (int)threadIdx.x;
-            if (idx >= n) break;
-            const int tl = idx / a.E, e = idx % a.E;
-            float v = p[u][0];
-#pragma unroll
-            for (int s = 1; s < kRouterSegments; ++s) v = v + p[u][s];
-            if (a.bias) v = v + a.bias[e];
-            lg[tl * topk_lg_stride(a.E) + e] = v;
-        }
-    }
-}
-
-// Top-k and gate for one token whose E logits are in `row` (LDS), lane = token
-// (E <= 64): a sequential selection over ascending ids, where a strict '>'
-// keeps the lower id on ties (and -0 ties with +0, as float compare does).
-// The chosen ids go to ids_row (LDS, k entries).
-__device__ __forceinline__ void topk_one_lane(const TopkArgs &a, const float *row, int t, int32_t *ids_row)
-{
-    float lv[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) lv[e] = e < a.E ? row[e] : 0.0f;
-    uint64_t taken = 0;
-    float top = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        int best = -1;
-        float bl = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 64; ++e) {
-            if (e < a.E && !((taken >> e) & 1ull) && (best < 0 || lv[e] > bl)) {
-                best = e;
-                bl = lv[e];
-            }
-        }
-        taken |= 1ull << best;
-        if (j == 0) top = bl;
-        ids_row[j] = best;
-        const size_t o = (size_t)t * a.k + j;
-        a.ids[o] = best;
-        if (a.ids_user) a.ids_user[o] = best;
-    }
-    if (a.w_user) {
-        float zsum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 64; ++e)
-            if (e < a.E) zsum += expf(lv[e] - top);
-        for (int j = 0; j < a.k; ++j) a.w_user[(size_t)t * a.k + j] = expf(row[ids_row[j]] - top) / zsum;
-    }
-}
-
 // Top-k and gate of token t with the lanes of one wave spanning the experts
-// (e = lane + 64 v, v < NV, E <= 64 NV), for E > 64.  The 8 partial sums of
+// (e = lane + 64 v, v < NV, E <= 64 NV).  The 8 partial sums of
 // each logit come straight from the workspace (a token's E partials of one
 // segment are contiguous, so the loads coalesce), all 8 NV of them in flight;
 // the logit is their ordered sum plus the bias.  Then k rounds of a wave-wide
@@ -393,7 +310,7 @@ __device__ __forceinline__ void topk_token_wave(const TopkArgs &a, int t)
     }
 }
 
-// Token-per-wave top-k (E > 64): workgroup unit u covers tokens 4u .. 4u+3, one per wave.
+// Token-per-wave top-k: workgroup unit u covers tokens 4u .. 4u+3, one per wave.
 __host__ __device__ inline int topk_wave_units(int T) { return (T + 3) / 4; }
 __device__ __forceinline__ void topk_wave_unit(const TopkArgs &a, int u)
 {
@@ -405,23 +322,6 @@ __device__ __forceinline__ void topk_wave_unit(const TopkArgs &a, int u)
     else topk_token_wave<16>(a, t);
 }
 
-// Top-k and gate for tokens [blk*64, blk*64 + 64) (E <= 64), in sub-blocks whose
-// logits are first gathered into LDS (lg: kTopkLdsBytes).  ids_lds: [64][k] (LDS).
-__device__ __forceinline__ void topk_block(const TopkArgs &a, int blk, float *lg, int32_t *ids_lds)
-{
-    const int w = threadIdx.x / kWave;
-    const int l = threadIdx.x % kWave;
-    const int sb = topk_subblock(a.E);
-    const int t_end = min(a.T, (blk + 1) * kTokBlock);
-    for (int t0 = blk * kTokBlock; t0 < t_end; t0 += sb) {
-        const int nt = min(sb, t_end - t0);
-        block_logits(a, t0, nt, lg);
-        __syncthreads();
-        if (w == 0 && l < nt)
-            topk_one_lane(a, lg + l * topk_lg_stride(a.E), t0 + l, ids_lds + (t0 - blk * kTokBlock + l) * a.k);
-        __syncthreads();
-    }
-}
 
 struct CountArgs {
     const int32_t *ids;   // [T, k]
