@@ -132,7 +132,12 @@ size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src
  *                      flag epochs), so two calls in flight must not share one.
  *   tune               NULL or all zeros = per-shape table
  * Device-side failures (a wait that timed out, bad topk_ids_in) are reported by
- * mk_poll_error after the stream is synchronised; outputs are then undefined. */
+ * mk_poll_error after the stream is synchronised; outputs are then undefined.
+ * The fused kernel runs one workgroup per resident slot of the device and
+ * synchronises them with grid barriers: they must all become resident, so
+ * work of other streams on the device only delays it, and a wait longer than
+ * the bound (MK_TIMEOUT_US microseconds, default 2000000) ends the call with
+ * MK_ETIMEOUT rather than hanging. */
 mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src,
                            const float *w_router, const float *bias,
                            const int32_t *topk_ids_in,

@@ -30,7 +30,8 @@ hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x
 hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s);
 // Largest co-resident grid of the GEMM kernel for this tile shape.
 int gemm_max_grid(int bm, int bn);
-// The persistent fused kernel (cooperative launch: the whole grid is co-resident).
+// The persistent fused kernel: one workgroup per resident slot of the device (its grid barriers need them all
+// resident together).
 hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
 int fused_max_grid();
 
