@@ -551,9 +551,6 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     auto done = [&]() { ++n_done; };
     LambdaSched<decltype(claim_job), decltype(wait), decltype(done)> sc{claim_job, wait, done};
     gemm_run(g, sc, ls);
-    // Write this XCD's dirty L2 lines (the outputs) back now, while other workgroups still compute,
-    // rather than leaving them to the next call's first release.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     trace_put(a, kTrDone, now_ticks());
     trace_put(a, kTrTasks, n_done);
     trace_put(a, kTrWaitTicks, wait_ticks);
