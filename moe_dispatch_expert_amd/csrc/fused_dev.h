@@ -371,8 +371,9 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
 
     // ---- phase 1: router logits
     if (!a.ids_in) {
-        const int units = router_units(a.T, a.E);
-        for (int u = w; u < units; u += G) router_unit(a.ra, u, st[0], st[2], st[1], st[3]);
+        const int tasks = router_tasks(a.T, a.E);
+        const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+        for (int q = w * 4 + wave; q < tasks; q += G * 4) router_task(a.ra, q);
         trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());

@@ -11,14 +11,11 @@
 
 namespace mk {
 
-// One router work unit per workgroup.
+// Router partial sums: one wave task per wave, four per workgroup.
 __global__ __launch_bounds__(256) void k_router(RouterArgs a)
 {
-    // a stage is the x tile followed by the W tile: at most 32 KiB + 2 KiB (E <= 8)
-    __shared__ __attribute__((aligned(16))) char st0[34816], st1[34816];
-    const RouterCfg c = router_cfg(a.E);
-    const int xb = c.BT * kRouterXS * 2;
-    router_unit(a, blockIdx.x, st0, st0 + xb, st1, st1 + xb);
+    const int q = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    if (q < router_tasks(a.T, a.E)) router_task(a, q);
 }
 
 // Token-per-wave top-k, four tokens per workgroup.
@@ -91,7 +88,7 @@ __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_router, dim3(router_units(a.T, a.E)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_router, dim3((router_tasks(a.T, a.E) + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

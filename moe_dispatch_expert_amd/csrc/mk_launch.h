@@ -15,7 +15,7 @@ struct SlotArgs;
 struct GemmArgs;
 struct FusedArgs;
 
-// Router partial sums, one unit per wave (router_units).
+// Router partial sums, one wave task per wave (router_tasks).
 hipError_t launch_router(const RouterArgs &a, hipStream_t s);
 // Top-k + gate for all tokens; with do_count also the per-block histogram and ranks.
 hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s);

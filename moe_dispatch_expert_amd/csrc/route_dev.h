@@ -55,180 +55,250 @@ __device__ __forceinline__ void unpack8(const u32x4_t v, float (&f)[8])
 
 // ---------------------------------------------------------------- partial sums
 // part[s][t][e] = fma chain over i in K segment s, ascending (fp32, one rounding
-// per step).  Each of the 8 segments is an independent small SIMT GEMM
-// [T x seg] . [seg x E]; one workgroup unit = (segment, block of BT tokens,
-// block of BE experts), staged through LDS in K chunks of KC with the chunks
-// two ahead prefetched into registers; thread (ty, tx) owns TT tokens x TE experts
-// and walks k in ascending order, so every accumulator is one chain.
-struct RouterCfg {
-    int BE, TE, TT, BT;
+// per step).  The work is split into wave tasks (segment s, block of 64 tokens,
+// group of TE experts); lane l owns token 64 b + l and the TE chains of that
+// token.  Per K step a lane needs one x value (its own row: 16 K values in two
+// 16-byte loads) and TE router weights that are the same for every lane.  The
+// weights travel 16 to a VGPR (lane i of each 16-lane row holds weight i) and
+// reach the FMAs by DPP row broadcast, so a weight costs 4 bytes of load
+// return per row instead of 4 bytes per lane; broadcasting them through LDS or
+// same-address loads would bound the loop by data return, and scalar loads
+// (out-of-order returns, so every use waits for all of them) expose the L2
+// latency once per batch.  All loads are vector loads, in order, several
+// groups ahead; no LDS and no barrier.  Tasks are numbered expert group
+// fastest, so consecutive tasks (the waves of one workgroup) read the same
+// token rows and share them in L1/L2.
+
+// Experts per lane: 8 when there are many tasks (fewer bf16 unpacks per FMA), else 4.
+__host__ __device__ inline int router_te(int T, int E)
+{
+    return ((T + kTokBlock - 1) / kTokBlock) * ((E + 7) / 8) * kRouterSegments >= 2048 ? 8 : 4;
+}
+__host__ __device__ inline int router_tasks(int T, int E)
+{
+    const int te = router_te(T, E);
+    return ((T + kTokBlock - 1) / kTokBlock) * ((E + te - 1) / te) * kRouterSegments;
+}
+
+constexpr int kRouterQK = 16;   // K steps per quarter: one FMA block per W float4 set
+constexpr int kRouterGQ = 4;    // quarters per group: 64 K steps, one 128-byte line of x per lane
+constexpr int kRouterGD = 3;    // groups in flight per wave
+
+// The FMA blocks: acc[j] += W[step][j] * x[step] over the block's K steps in
+// ascending order, with W from DPP row broadcasts of a float4 set (see the
+// load layout in router_task_body).  The leading s_nop covers the DPP read
+// hazards (a VALU or EXEC write of the broadcast registers just before).  DPP
+// on the accumulating FMA is written out because the compiler does not fold a
+// separate DPP move into it.
+// TE = 4: 16 K steps; lane q of the set holds step q, component j expert j.
+__device__ __forceinline__ void fma_block4(float (&acc)[4], const f32x4_t w, const float (&x)[16])
+{
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]),
+          "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]),
+          "v"(x[14]), "v"(x[15]));
+}
+// TE = 8: 8 K steps; lane 2 r + j / 4 of the set holds step r, component j % 4 expert j.
+__device__ __forceinline__ void fma_block8(float (&acc)[8], const f32x4_t w, const float *x)
+{
+    asm("s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %8, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %8, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %10, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %8, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %10, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
+          "+v"(acc[7])
+        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]),
+          "v"(x[5]), "v"(x[6]), "v"(x[7]));
+}
+
+// W float4 sets per quarter: TE / 4.  Lane p (of each 16-lane row) loads, for
+// set h of the quarter at K step k0, the four weights
+//   TE = 4: row k0 + p,              columns e0 .. e0 + 3;
+//   TE = 8: row k0 + 8 h + p / 2,    columns e0 + 4 (p % 2) .. + 3,
+// so a set holds 64 weights in 4 VGPRs, and each weight costs 4 bytes of load
+// return per 16 lanes.  FULL: the four columns exist and are 16-byte aligned
+// (one dwordx4 load); otherwise one load per column, columns past E repeating
+// the last (those chains are never stored).
+template <int TE, bool FULL>
+struct RouterW {
+    const float *p;   // this lane's first weight of quarter 0, set 0
+    int E, clast;     // row stride; last valid column offset from this lane's first column
+    __device__ __forceinline__ f32x4_t load(int quarter, int h) const
+    {
+        const float *q = p + ((size_t)quarter * kRouterQK + (TE == 8 ? 8 * h : 0)) * E;
+        if (FULL) return *(const f32x4_t *)q;
+        f32x4_t v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = q[min(c, clast)];
+        return v;
+    }
 };
 
-// The configurations, by index; router_cfg_index picks one from E.
-__host__ __device__ __forceinline__ constexpr RouterCfg router_cfg_at(int ci)
+template <int TE, bool FULL>
+__device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int tb, int e0)
 {
-    return ci == 0 ? RouterCfg{8, 4, 1, 128}
-         : ci == 1 ? RouterCfg{16, 8, 1, 128}
-         : ci == 2 ? RouterCfg{32, 8, 2, 128}
-         : ci == 3 ? RouterCfg{64, 8, 4, 128}
-                   : RouterCfg{32, 4, 1, 32};
-}
-__host__ __device__ __forceinline__ constexpr int router_cfg_index(int E)
-{
-    return E <= 8 ? 0 : E <= 16 ? 1 : E <= 32 ? 2 : E <= 64 ? 3 : 4;
-}
-__host__ __device__ __forceinline__ constexpr RouterCfg router_cfg(int E) { return router_cfg_at(router_cfg_index(E)); }
-
-__host__ __device__ inline int router_units(int T, int E)
-{
-    const RouterCfg c = router_cfg(E);
-    return ((T + c.BT - 1) / c.BT) * ((E + c.BE - 1) / c.BE) * kRouterSegments;
-}
-
-constexpr int kRouterKC = 64;   // K chunk per LDS stage (a smaller divisor of the segment if needed)
-// LDS row stride of the x tile (bf16): 16 bytes of padding per row put the
-// rows that the lanes of one read touch in different banks.
-constexpr int kRouterXS = kRouterKC + 8;
-
-template <int CI>
-__device__ __forceinline__ void router_unit_tiled(const RouterArgs &a, int unit, char *x0, char *w0, char *x1, char *w1)
-{
-#pragma clang fp contract(off)
-    constexpr int BE = router_cfg_at(CI).BE, TE = router_cfg_at(CI).TE, TT = router_cfg_at(CI).TT;
-    constexpr int NX = BE / TE;            // threads along the experts
-    constexpr int NY = 256 / NX;           // threads along the tokens
-    constexpr int BT = NY * TT;
-    static_assert(router_cfg_at(CI).BT == BT, "the thread layout covers the configured token block");
-    constexpr int XCH = BT * kRouterKC / 8;              // 16-byte x chunks per stage (max)
-    constexpr int XPT = (XCH + 255) / 256;               // per thread
-    constexpr int WPT = (kRouterKC * BE + 255) / 256;    // W floats per thread per stage (max)
-    const int seg = a.d / kRouterSegments;
-    const int KC = seg % kRouterKC == 0 ? kRouterKC : (seg % 32 == 0 ? 32 : 16);
-    const int ntb = (a.T + BT - 1) / BT;
-    const int neb = (a.E + BE - 1) / BE;
-    const int tb = unit % ntb;
-    const int eb = (unit / ntb) % neb;
-    const int s = unit / (ntb * neb);
-    const int tid = threadIdx.x;
-    const int tx = tid % NX, ty = tid / NX;
-    const int k_base = s * seg;
-
-    // a stage is an x tile [BT][kRouterXS] bf16 (<= 32 KiB) and a W tile [kRouterKC][BE] fp32 (<= 16 KiB)
-    static_assert(BT * kRouterXS * 2 <= 32768 && kRouterKC * BE * 4 <= 16384, "router stage sizes");
-    static_assert(BT * kRouterXS * 2 + kRouterKC * BE * 4 <= 34816, "router stage fits one 34 KiB array");
-    const int cpr = KC / 8;
-    const int nk = seg / KC;
-    // Two register sets of prefetched chunks (A, B): a chunk is fetched two
-    // chunk-computations before it is written to LDS.  Fetches past the last
-    // chunk re-read the last one (unconditional loads keep the compiler's
-    // wait counts exact).
-    u32x4_t xrA[XPT], xrB[XPT];
-    float wrA[WPT], wrB[WPT];
-    // The token rows this thread fetches from, fixed for the whole unit: computed once, so the
-    // chunk loop has no pointer loads (whose waits would drain the prefetches in flight).
-    const uint16_t *xrow[XPT];
+    constexpr int WQ = TE / 4;   // W sets per quarter
+    const int lane = threadIdx.x % kWave;
+    const int seg = a.d / kRouterSegments;   // a multiple of 16 (d % 128 == 0)
+    const int t = tb * kTokBlock + lane;
+    const uint16_t *xr = token_row(a.src, min(t, a.T - 1), a.d) + (size_t)s * seg;
+    const int p = lane & 15;
+    const int row = TE == 4 ? p : p / 2, col = TE == 4 ? 0 : 4 * (p % 2);
+    const RouterW<TE, FULL> W{a.wr + ((size_t)s * seg + row) * a.E + e0 + min(col, a.E - 1 - e0), a.E,
+                              a.E - 1 - e0 - min(col, a.E - 1 - e0)};
+    float acc[TE];
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-        const int c = min(tid + j * 256, BT * cpr - 1);
-        const int row = c / cpr, cc = c - row * cpr;
-        const int t = min(tb * BT + row, a.T - 1);
-        xrow[j] = token_row(a.src, t, a.d) + k_base + cc * 8;
-    }
-#define MK_ROUTER_FETCH(xr, wrg, chunk)                                                           \
-    do {                                                                                          \
-        const int k0_ = min((chunk), nk - 1) * KC;                                                \
-        _Pragma("unroll") for (int j = 0; j < XPT; ++j) xr[j] = *(const u32x4_t *)(xrow[j] + k0_); \
-        _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                         \
-            const int c = min(tid + j * 256, KC * BE - 1);                                        \
-            const int kk = c / BE, e = c - kk * BE;                                               \
-            wrg[j] = a.wr[(size_t)(k_base + k0_ + kk) * a.E + min(eb * BE + e, a.E - 1)];         \
-        }                                                                                         \
-    } while (0)
-#define MK_ROUTER_STASH(xr, wrg, xs, ws)                                                          \
-    do {                                                                                          \
-        _Pragma("unroll") for (int j = 0; j < XPT; ++j) {                                         \
-            const int c = tid + j * 256;                                                          \
-            if (c < BT * cpr)                                                                     \
-                *(u32x4_t *)((uint16_t *)(xs) + (c / cpr) * kRouterXS + (c % cpr) * 8) = xr[j];  \
-        }                                                                                         \
-        _Pragma("unroll") for (int j = 0; j < WPT; ++j) {                                         \
-            const int c = tid + j * 256;                                                          \
-            if (c < KC * BE) ((float *)(ws))[c] = wrg[j];                                        \
-        }                                                                                         \
-    } while (0)
-#define MK_ROUTER_COMPUTE(xs, ws)                                                                 \
-    do {                                                                                          \
-        const uint16_t *xt = (const uint16_t *)(xs);                                              \
-        const float *wt = (const float *)(ws);                                                    \
-        for (int k8 = 0; k8 < KC; k8 += 8) {                                                      \
-            float xf[TT][8];                                                                      \
-            _Pragma("unroll") for (int i = 0; i < TT; ++i)                                        \
-                unpack8(*(const u32x4_t *)(xt + (ty * TT + i) * kRouterXS + k8), xf[i]);         \
-            _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                       \
-                float wv[TE];                                                                     \
-                _Pragma("unroll") for (int j = 0; j < TE; j += 4) {                               \
-                    const float4 w4 = *(const float4 *)(wt + (k8 + q) * BE + tx * TE + j);        \
-                    wv[j] = w4.x;                                                                 \
-                    wv[j + 1] = w4.y;                                                             \
-                    wv[j + 2] = w4.z;                                                             \
-                    wv[j + 3] = w4.w;                                                             \
-                }                                                                                 \
-                _Pragma("unroll") for (int i = 0; i < TT; ++i)                                    \
-                    _Pragma("unroll") for (int j = 0; j < TE; ++j)                                \
-                        acc[i][j] = __builtin_fmaf(xf[i][q], wv[j], acc[i][j]);                   \
-            }                                                                                     \
-        }                                                                                         \
-    } while (0)
-
-    float acc[TT][TE];
-#pragma unroll
-    for (int i = 0; i < TT; ++i)
-#pragma unroll
-        for (int j = 0; j < TE; ++j) acc[i][j] = 0.0f;
-
-    MK_ROUTER_FETCH(xrA, wrA, 0);
-    MK_ROUTER_FETCH(xrB, wrB, 1);
-    MK_ROUTER_STASH(xrA, wrA, x0, w0);
-    MK_ROUTER_FETCH(xrA, wrA, 2);
-    __syncthreads();
-    for (int kc = 0; kc < nk; kc += 2) {
-        // stage 0 holds chunk kc, B holds chunk kc + 1, A holds chunk kc + 2
-        MK_ROUTER_COMPUTE(x0, w0);
-        MK_ROUTER_STASH(xrB, wrB, x1, w1);
-        MK_ROUTER_FETCH(xrB, wrB, kc + 3);
-        __syncthreads();
-        if (kc + 1 >= nk) break;
-        MK_ROUTER_COMPUTE(x1, w1);
-        MK_ROUTER_STASH(xrA, wrA, x0, w0);
-        MK_ROUTER_FETCH(xrA, wrA, kc + 4);
-        __syncthreads();
-    }
-#undef MK_ROUTER_FETCH
-#undef MK_ROUTER_STASH
-#undef MK_ROUTER_COMPUTE
-#pragma unroll
-    for (int i = 0; i < TT; ++i) {
-        const int t = tb * BT + ty * TT + i;
-        if (t >= a.T) continue;
-#pragma unroll
-        for (int j = 0; j < TE; ++j) {
-            const int e = eb * BE + tx * TE + j;
-            if (e < a.E) a.part[((size_t)s * a.T + t) * a.E + e] = acc[i][j];
+    for (int j = 0; j < TE; ++j) acc[j] = 0.0f;
+    // One quarter (16 K steps) from its x words (16 bf16) and W sets.
+    auto quarter = [&](const u32x4_t (&xw)[2], const f32x4_t *w) {
+        float xf[16];
+        unpack8(xw[0], *(float (*)[8])&xf[0]);
+        unpack8(xw[1], *(float (*)[8])&xf[8]);
+        if constexpr (TE == 4) {
+            fma_block4(acc, w[0], xf);
+        } else {
+            fma_block8(acc, w[0], &xf[0]);
+            fma_block8(acc, w[1], &xf[8]);
         }
+    };
+    const int ng = seg / (kRouterQK * kRouterGQ);
+    if (ng > 0) {
+        // A group: the lane's whole 128-byte x line (8 loads, back to back, so the line is fetched
+        // once) and the W sets of its 4 quarters; GD groups in flight.
+        struct Grp {
+            u32x4_t x[2 * kRouterGQ];
+            f32x4_t w[kRouterGQ * WQ];
+        };
+        auto fetch = [&](int g, Grp &r) {
+#pragma unroll
+            for (int i = 0; i < 2 * kRouterGQ; ++i) r.x[i] = *(const u32x4_t *)(xr + g * 64 + 8 * i);
+#pragma unroll
+            for (int i = 0; i < kRouterGQ * WQ; ++i) r.w[i] = W.load(g * kRouterGQ + i / WQ, i % WQ);
+        };
+        Grp gr[kRouterGD];
+#pragma unroll
+        for (int i = 0; i < kRouterGD; ++i) {   // the same load order as the refills in the loop
+            fetch(min(i, ng - 1), gr[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Group g's quarters, then its registers refilled with group g + GD (past the end: the last
+        // group again, so the number of loads in flight never changes); scheduling barriers keep the
+        // refill after the FMAs and before the next group.
+        auto group = [&](int g, Grp &r) {
+#pragma unroll
+            for (int qq = 0; qq < kRouterGQ; ++qq) {
+                const u32x4_t xw[2] = {r.x[2 * qq], r.x[2 * qq + 1]};
+                quarter(xw, &r.w[qq * WQ]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            fetch(min(g + kRouterGD, ng - 1), r);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // Whole rounds of GD groups without conditions (exact wait counts), then the rest.
+        int g0 = 0;
+        for (; g0 + kRouterGD <= ng; g0 += kRouterGD) {
+#pragma unroll
+            for (int i = 0; i < kRouterGD; ++i) group(g0 + i, gr[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kRouterGD - 1; ++i)
+            if (g0 + i < ng) group(g0 + i, gr[i]);
+    }
+    // Segment lengths that are not a multiple of 64: the remaining quarters one at a time.
+    for (int qi = ng * kRouterGQ; qi < seg / kRouterQK; ++qi) {
+        const u32x4_t xw[2] = {*(const u32x4_t *)(xr + qi * kRouterQK), *(const u32x4_t *)(xr + qi * kRouterQK + 8)};
+        f32x4_t w[WQ];
+#pragma unroll
+        for (int h = 0; h < WQ; ++h) w[h] = W.load(qi, h);
+        quarter(xw, w);
+    }
+    if (t < a.T) {
+        float *dst = a.part + ((size_t)s * a.T + t) * a.E + e0;
+#pragma unroll
+        for (int j = 0; j < TE; ++j)
+            if (e0 + j < a.E) dst[j] = acc[j];
     }
 }
 
-// One workgroup unit of the partial-sum phase; two LDS stages, each an x part
-// (x0, x1: 32 KiB) and a W part (w0, w1: 16 KiB).
-__device__ __forceinline__ void router_unit(const RouterArgs &a, int unit, char *x0, char *w0, char *x1, char *w1)
+template <int TE>
+__device__ __forceinline__ void router_task_te(const RouterArgs &a, int q)
 {
-    switch (router_cfg_index(a.E)) {
-    case 0: router_unit_tiled<0>(a, unit, x0, w0, x1, w1); break;
-    case 1: router_unit_tiled<1>(a, unit, x0, w0, x1, w1); break;
-    case 2: router_unit_tiled<2>(a, unit, x0, w0, x1, w1); break;
-    case 3: router_unit_tiled<3>(a, unit, x0, w0, x1, w1); break;
-    default: router_unit_tiled<4>(a, unit, x0, w0, x1, w1); break;
-    }
+    const int neg = (a.E + TE - 1) / TE;
+    const int ntb = (a.T + kTokBlock - 1) / kTokBlock;
+    const int eg = __builtin_amdgcn_readfirstlane(q % neg);
+    const int tb = __builtin_amdgcn_readfirstlane((q / neg) % ntb);
+    const int s = __builtin_amdgcn_readfirstlane(q / (neg * ntb));
+    if (a.E % 4 == 0 && eg * TE + TE <= a.E) router_task_body<TE, true>(a, s, tb, eg * TE);
+    else router_task_body<TE, false>(a, s, tb, eg * TE);
+}
+
+// Wave task q (< router_tasks(T, E)); q must be uniform over the wave.
+__device__ __forceinline__ void router_task(const RouterArgs &a, int q)
+{
+    if (router_te(a.T, a.E) == 8) router_task_te<8>(a, q);
+    else router_task_te<4>(a, q);
 }
 
 struct TopkArgs {
