@@ -373,7 +373,9 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     if (!a.ids_in) {
         const int tasks = router_tasks(a.T, a.E);
         const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-        for (int q = w * 4 + wave; q < tasks; q += G * 4) router_task(a.ra, q);
+        lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * kRtLdsPerWave;   // the stage arrays are consecutive
+        static_assert(4 * kRtLdsPerWave <= 4 * 32768, "router staging fits the stage arrays");
+        for (int q = w * 4 + wave; q < tasks; q += G * 4) router_task(a.ra, q, rlds);
         trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());

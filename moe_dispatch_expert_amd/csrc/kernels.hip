@@ -14,8 +14,10 @@ namespace mk {
 // Router partial sums: one wave task per wave, four per workgroup.
 __global__ __launch_bounds__(256) void k_router(RouterArgs a)
 {
-    const int q = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    if (q < router_tasks(a.T, a.E)) router_task(a, q);
+    __shared__ __attribute__((aligned(16))) char lds[4 * kRtLdsPerWave];
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int q = (int)blockIdx.x * 4 + wave;
+    if (q < router_tasks(a.T, a.E)) router_task(a, q, (lds_byte_t *)(lds + wave * kRtLdsPerWave));
 }
 
 // Token-per-wave top-k, four tokens per workgroup.

@@ -55,250 +55,153 @@ __device__ __forceinline__ void unpack8(const u32x4_t v, float (&f)[8])
 
 // ---------------------------------------------------------------- partial sums
 // part[s][t][e] = fma chain over i in K segment s, ascending (fp32, one rounding
-// per step).  The work is split into wave tasks (segment s, block of 64 tokens,
-// group of TE experts); lane l owns token 64 b + l and the TE chains of that
-// token.  Per K step a lane needs one x value (its own row: 16 K values in two
-// 16-byte loads) and TE router weights that are the same for every lane.  The
-// weights travel 16 to a VGPR (lane i of each 16-lane row holds weight i) and
-// reach the FMAs by DPP row broadcast, so a weight costs 4 bytes of load
-// return per row instead of 4 bytes per lane; broadcasting them through LDS or
-// same-address loads would bound the loop by data return, and scalar loads
-// (out-of-order returns, so every use waits for all of them) expose the L2
-// latency once per batch.  All loads are vector loads, in order, several
-// groups ahead; no LDS and no barrier.  Tasks are numbered expert group
-// fastest, so consecutive tasks (the waves of one workgroup) read the same
-// token rows and share them in L1/L2.
+// per step).  The chains run on the matrix cores: v_mfma_f32_4x4x1_16b_f32 is
+// 16 independent 4x4 outer products with K = 1, i.e. for each of its 256
+// outputs exactly one fused multiply-add, and a sequence of them over
+// ascending i is the fma chain itself (bit-exact against fmaf chains on
+// gfx950).  It retires 256 fmas in 8 cycles, twice the rate of scalar-lane
+// fp32 FMAs, and needs each weight in only one lane per output column.
+//
+// A wave task is (segment s, block of 32 tokens, group of 8 experts).  MFMA
+// operand layout (A: lanes 4b .. 4b + 3 of block b give its 4 rows; B: lane l
+// gives column l % 4 of block l / 4; output lane l, register r is row
+// 4 (l / 4) + r, column l of the blocks' B lanes):
+//   A lane l = x of token 32 tb + (l % 32)  (lanes 32..63 repeat 0..31)
+//   B lane l = W_r[i][e0 + 4 (l / 32) + l % 4]
+// so output lane l, register r is token 32 tb + 4 ((l % 32) / 4) + r,
+// expert e0 + 4 (l / 32) + l % 4.
+// Both operands are staged per wave in LDS, a chunk of kRtKC steps at a time,
+// double buffered, from coalesced loads one chunk ahead: x as 32 token rows
+// (16 lanes per 256-byte row segment, so a load touches whole lines; a lane
+// then reads its own row 8 steps at a time), the weights transposed to 8
+// expert rows (padded so the rows sit on distinct banks; a lane reads 4 steps
+// of its column at a time).
+constexpr int kRtTok = 32;                    // tokens per wave task
+constexpr int kRtExp = 8;                     // experts per wave task
+constexpr int kRtKC = 128;                    // K steps per staged chunk
+constexpr int kRtWS = kRtKC + 4;              // LDS row stride of the staged weights (floats)
+constexpr int kRtXS = kRtKC + 8;              // LDS row stride of the staged x rows (bf16)
+constexpr int kRtWBuf = kRtExp * kRtWS * 4;   // bytes of one weight buffer
+constexpr int kRtXBuf = kRtTok * kRtXS * 2;   // bytes of one x buffer
+constexpr int kRtLdsPerWave = 2 * (kRtWBuf + kRtXBuf);
 
-// Experts per lane: 8 when there are many tasks (fewer bf16 unpacks per FMA), else 4.
-__host__ __device__ inline int router_te(int T, int E)
-{
-    return ((T + kTokBlock - 1) / kTokBlock) * ((E + 7) / 8) * kRouterSegments >= 2048 ? 8 : 4;
-}
 __host__ __device__ inline int router_tasks(int T, int E)
 {
-    const int te = router_te(T, E);
-    return ((T + kTokBlock - 1) / kTokBlock) * ((E + te - 1) / te) * kRouterSegments;
+    return ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp) * kRouterSegments;
 }
 
-constexpr int kRouterQK = 16;   // K steps per quarter: one FMA block per W float4 set
-constexpr int kRouterGQ = 4;    // quarters per group: 64 K steps, one 128-byte line of x per lane
-constexpr int kRouterGD = 3;    // groups in flight per wave
+typedef __attribute__((address_space(3))) float lds_float_t;
+typedef __attribute__((address_space(3))) char lds_byte_t;
 
-// The FMA blocks: acc[j] += W[step][j] * x[step] over the block's K steps in
-// ascending order, with W from DPP row broadcasts of a float4 set (see the
-// load layout in router_task_body).  The leading s_nop covers the DPP read
-// hazards (a VALU or EXEC write of the broadcast registers just before).  DPP
-// on the accumulating FMA is written out because the compiler does not fold a
-// separate DPP move into it.
-// TE = 4: 16 K steps; lane q of the set holds step q, component j expert j.
-__device__ __forceinline__ void fma_block4(float (&acc)[4], const f32x4_t w, const float (&x)[16])
+// FULL: the 8 columns exist and E % 4 == 0 (16-byte weight loads); otherwise
+// one load per column, columns past E repeating the last (never stored).
+// lds: this wave's kRtLdsPerWave bytes.
+template <bool FULL>
+__device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int tb, int e0, lds_byte_t *lds)
 {
-    asm("s_nop 4\n\t"
-        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %8 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %9 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %10 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %11 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %12 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %13 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %14 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %17 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %18 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %19 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %20 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %21 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %22 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %4, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %5, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %6, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %7, %23 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]),
-          "v"(x[5]), "v"(x[6]), "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]),
-          "v"(x[14]), "v"(x[15]));
-}
-// TE = 8: 8 K steps; lane 2 r + j / 4 of the set holds step r, component j % 4 expert j.
-__device__ __forceinline__ void fma_block8(float (&acc)[8], const f32x4_t w, const float *x)
-{
-    asm("s_nop 4\n\t"
-        "v_fmac_f32_dpp %0, %8, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %12 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %12 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %13 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %13 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %14 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %14 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %15 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %15 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %16 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %16 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %17 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %17 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %18 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %0, %8, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %1, %9, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %10, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %3, %11, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %8, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %5, %9, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %10, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t" "v_fmac_f32_dpp %7, %11, %19 row_newbcast:15 row_mask:0xf bank_mask:0xf\n\t"
-        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]), "+v"(acc[5]), "+v"(acc[6]),
-          "+v"(acc[7])
-        : "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]),
-          "v"(x[5]), "v"(x[6]), "v"(x[7]));
-}
-
-// W float4 sets per quarter: TE / 4.  Lane p (of each 16-lane row) loads, for
-// set h of the quarter at K step k0, the four weights
-//   TE = 4: row k0 + p,              columns e0 .. e0 + 3;
-//   TE = 8: row k0 + 8 h + p / 2,    columns e0 + 4 (p % 2) .. + 3,
-// so a set holds 64 weights in 4 VGPRs, and each weight costs 4 bytes of load
-// return per 16 lanes.  FULL: the four columns exist and are 16-byte aligned
-// (one dwordx4 load); otherwise one load per column, columns past E repeating
-// the last (those chains are never stored).
-template <int TE, bool FULL>
-struct RouterW {
-    const float *p;   // this lane's first weight of quarter 0, set 0
-    int E, clast;     // row stride; last valid column offset from this lane's first column
-    __device__ __forceinline__ f32x4_t load(int quarter, int h) const
-    {
-        const float *q = p + ((size_t)quarter * kRouterQK + (TE == 8 ? 8 * h : 0)) * E;
-        if (FULL) return *(const f32x4_t *)q;
-        f32x4_t v;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[c] = q[min(c, clast)];
-        return v;
-    }
-};
-
-template <int TE, bool FULL>
-__device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int tb, int e0)
-{
-    constexpr int WQ = TE / 4;   // W sets per quarter
+    typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
+    typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
     const int lane = threadIdx.x % kWave;
     const int seg = a.d / kRouterSegments;   // a multiple of 16 (d % 128 == 0)
-    const int t = tb * kTokBlock + lane;
-    const uint16_t *xr = token_row(a.src, min(t, a.T - 1), a.d) + (size_t)s * seg;
-    const int p = lane & 15;
-    const int row = TE == 4 ? p : p / 2, col = TE == 4 ? 0 : 4 * (p % 2);
-    const RouterW<TE, FULL> W{a.wr + ((size_t)s * seg + row) * a.E + e0 + min(col, a.E - 1 - e0), a.E,
-                              a.E - 1 - e0 - min(col, a.E - 1 - e0)};
-    float acc[TE];
+    const int nch = (seg + kRtKC - 1) / kRtKC;
+    const int eb = 4 * (lane >> 5) + (lane & 3);   // this lane's B column in the group
+    // x staging: lane l loads rows 4 i + l / 16 (i < 8), 16 bytes at piece l % 16 of the chunk's 256 bytes.
+    const uint16_t *xrow[8];
 #pragma unroll
-    for (int j = 0; j < TE; ++j) acc[j] = 0.0f;
-    // One quarter (16 K steps) from its x words (16 bf16) and W sets.
-    auto quarter = [&](const u32x4_t (&xw)[2], const f32x4_t *w) {
-        float xf[16];
-        unpack8(xw[0], *(float (*)[8])&xf[0]);
-        unpack8(xw[1], *(float (*)[8])&xf[8]);
-        if constexpr (TE == 4) {
-            fma_block4(acc, w[0], xf);
-        } else {
-            fma_block8(acc, w[0], &xf[0]);
-            fma_block8(acc, w[1], &xf[8]);
-        }
+    for (int i = 0; i < 8; ++i)
+        xrow[i] = token_row(a.src, min(tb * kRtTok + 4 * i + (lane >> 4), a.T - 1), a.d) + (size_t)s * seg +
+                  8 * (lane & 15);
+    // Weight staging: lane l loads rows (l / 2) + 32 i (i < 4) of a chunk, columns 4 (l % 2) .. + 3.
+    const int c0 = min(4 * (lane & 1), a.E - 1 - e0);
+    const int clast = a.E - 1 - e0 - c0;
+    const float *wsrc = a.wr + (size_t)s * seg * a.E + e0 + c0;
+    struct Regs {
+        u32x4_t x[8];
+        f32x4_t w[4];
     };
-    const int ng = seg / (kRouterQK * kRouterGQ);
-    if (ng > 0) {
-        // A group: the lane's whole 128-byte x line (8 loads, back to back, so the line is fetched
-        // once) and the W sets of its 4 quarters; GD groups in flight.
-        struct Grp {
-            u32x4_t x[2 * kRouterGQ];
-            f32x4_t w[kRouterGQ * WQ];
-        };
-        auto fetch = [&](int g, Grp &r) {
+    // Chunk c into registers (past the end: the last chunk again; steps past the segment: clamped).
+    auto fetch = [&](int c, Regs &r) {
+        const int cc = min(c, nch - 1);
 #pragma unroll
-            for (int i = 0; i < 2 * kRouterGQ; ++i) r.x[i] = *(const u32x4_t *)(xr + g * 64 + 8 * i);
+        for (int i = 0; i < 4; ++i) {
+            const int row = min(cc * kRtKC + (lane >> 1) + 32 * i, seg - 1);
+            const float *q = wsrc + (size_t)row * a.E;
+            if (FULL) {
+                r.w[i] = *(const f32x4_t *)q;
+            } else {
 #pragma unroll
-            for (int i = 0; i < kRouterGQ * WQ; ++i) r.w[i] = W.load(g * kRouterGQ + i / WQ, i % WQ);
-        };
-        Grp gr[kRouterGD];
-#pragma unroll
-        for (int i = 0; i < kRouterGD; ++i) {   // the same load order as the refills in the loop
-            fetch(min(i, ng - 1), gr[i]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // Group g's quarters, then its registers refilled with group g + GD (past the end: the last
-        // group again, so the number of loads in flight never changes); scheduling barriers keep the
-        // refill after the FMAs and before the next group.
-        auto group = [&](int g, Grp &r) {
-#pragma unroll
-            for (int qq = 0; qq < kRouterGQ; ++qq) {
-                const u32x4_t xw[2] = {r.x[2 * qq], r.x[2 * qq + 1]};
-                quarter(xw, &r.w[qq * WQ]);
+                for (int j = 0; j < 4; ++j) r.w[i][j] = q[min(j, clast)];
             }
-            __builtin_amdgcn_sched_barrier(0);
-            fetch(min(g + kRouterGD, ng - 1), r);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        // Whole rounds of GD groups without conditions (exact wait counts), then the rest.
-        int g0 = 0;
-        for (; g0 + kRouterGD <= ng; g0 += kRouterGD) {
-#pragma unroll
-            for (int i = 0; i < kRouterGD; ++i) group(g0 + i, gr[i]);
         }
+        const int k0 = min(cc * kRtKC + 8 * (lane & 15), seg - 8) - 8 * (lane & 15);
 #pragma unroll
-        for (int i = 0; i < kRouterGD - 1; ++i)
-            if (g0 + i < ng) group(g0 + i, gr[i]);
+        for (int i = 0; i < 8; ++i) r.x[i] = *(const u32x4_t *)(xrow[i] + k0);
+    };
+    auto wbuf = [&](int c) { return (lds_float_t *)(lds + (c & 1) * kRtWBuf); };
+    auto xbuf = [&](int c) { return lds + 2 * kRtWBuf + (c & 1) * kRtXBuf; };
+    auto stash = [&](const Regs &r, int c) {
+        lds_float_t *wb = wbuf(c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wb[(4 * (lane & 1) + j) * kRtWS + (lane >> 1) + 32 * i] = r.w[i][j];
+        lds_byte_t *xb = xbuf(c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *(lds_u32x4_t *)(xb + ((4 * i + (lane >> 4)) * kRtXS + 8 * (lane & 15)) * 2) = r.x[i];
+    };
+    Regs r;
+    fetch(0, r);
+    stash(r, 0);
+    fetch(1, r);
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < nch; ++c) {
+        const lds_float_t *wb = wbuf(c) + eb * kRtWS;
+        const lds_byte_t *xb = xbuf(c) + (lane & 31) * kRtXS * 2;
+        const int len = min(kRtKC, seg - c * kRtKC);   // a multiple of 16
+#pragma unroll
+        for (int b = 0; b < kRtKC / 16; ++b) {
+            if (b * 16 < len) {
+                const u32x4_t x0 = *(const lds_u32x4_t *)(xb + 32 * b);
+                const u32x4_t x1 = *(const lds_u32x4_t *)(xb + 32 * b + 16);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const f32x4_t w4 = *(const lds_f32x4_t *)(wb + 16 * b + 4 * h);
+                    const u32x4_t xw = h < 2 ? x0 : x1;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t word = xw[2 * (h & 1) + j / 2];
+                        const float xf = __uint_as_float((j & 1) ? (word & 0xFFFF0000u) : (word << 16));
+                        acc = __builtin_amdgcn_mfma_f32_4x4x1f32(xf, w4[j], acc, 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // chunk c + 1 into the other buffers (last read as chunk c - 1, before this chunk's reads; a
+        // wave's LDS accesses complete in order), then chunk c + 2 into the registers.  (Keeping more
+        // chunks in flight measured slower on every workload shape.)
+        stash(r, c + 1);
+        fetch(c + 2, r);
     }
-    // Segment lengths that are not a multiple of 64: the remaining quarters one at a time.
-    for (int qi = ng * kRouterGQ; qi < seg / kRouterQK; ++qi) {
-        const u32x4_t xw[2] = {*(const u32x4_t *)(xr + qi * kRouterQK), *(const u32x4_t *)(xr + qi * kRouterQK + 8)};
-        f32x4_t w[WQ];
+    const int e = e0 + eb;
 #pragma unroll
-        for (int h = 0; h < WQ; ++h) w[h] = W.load(qi, h);
-        quarter(xw, w);
-    }
-    if (t < a.T) {
-        float *dst = a.part + ((size_t)s * a.T + t) * a.E + e0;
-#pragma unroll
-        for (int j = 0; j < TE; ++j)
-            if (e0 + j < a.E) dst[j] = acc[j];
+    for (int q = 0; q < 4; ++q) {
+        const int t = tb * kRtTok + 4 * ((lane & 31) >> 2) + q;
+        if (t < a.T && e < a.E) a.part[((size_t)s * a.T + t) * a.E + e] = acc[q];
     }
 }
 
-template <int TE>
-__device__ __forceinline__ void router_task_te(const RouterArgs &a, int q)
+// Wave task q (< router_tasks(T, E)); q uniform over the wave.  Task numbers
+// run expert group fastest, so the waves of a workgroup share token rows.
+__device__ __forceinline__ void router_task(const RouterArgs &a, int q, lds_byte_t *lds)
 {
-    const int neg = (a.E + TE - 1) / TE;
-    const int ntb = (a.T + kTokBlock - 1) / kTokBlock;
+    const int neg = (a.E + kRtExp - 1) / kRtExp;
+    const int ntb = (a.T + kRtTok - 1) / kRtTok;
     const int eg = __builtin_amdgcn_readfirstlane(q % neg);
     const int tb = __builtin_amdgcn_readfirstlane((q / neg) % ntb);
     const int s = __builtin_amdgcn_readfirstlane(q / (neg * ntb));
-    if (a.E % 4 == 0 && eg * TE + TE <= a.E) router_task_body<TE, true>(a, s, tb, eg * TE);
-    else router_task_body<TE, false>(a, s, tb, eg * TE);
-}
-
-// Wave task q (< router_tasks(T, E)); q must be uniform over the wave.
-__device__ __forceinline__ void router_task(const RouterArgs &a, int q)
-{
-    if (router_te(a.T, a.E) == 8) router_task_te<8>(a, q);
-    else router_task_te<4>(a, q);
+    if (a.E % 4 == 0 && eg * kRtExp + kRtExp <= a.E) router_task_body<true>(a, s, tb, eg * kRtExp, lds);
+    else router_task_body<false>(a, s, tb, eg * kRtExp, lds);
 }
 
 struct TopkArgs {

@@ -78,6 +78,30 @@ def test_route_topk_matches_oracle(name):
     assert_w_close(w.cpu().numpy(), ref_w, name)
 
 
+@pytest.mark.parametrize("name,changes", [
+    ("tiny", {}), ("mixtral", {}), ("skewed", {}), ("decode", {}),
+    ("tiny", dict(T=96, d=384, E=6, k=3, E_local=6)),      # 48-step segments, E % 4 != 0
+    ("tiny", dict(T=700, d=256, E=10, k=3, E_local=10)),   # 32-step segments, a partial expert group
+    ("tiny", dict(T=33, d=128, E=1, k=1, E_local=1)),       # one expert, 16-step segments, a 1-token block
+])
+def test_router_logits_bit_exact(name, changes):
+    """The router's per-segment partial sums (left in the mk_route_topk workspace, [8, T, E] fp32),
+    added in the fixed order, equal the oracle's fp32 logits bit for bit: every chain is the same
+    sequence of fused multiply-adds."""
+    wl = W.scaled(W.WORKLOADS[name], **changes) if changes else W.WORKLOADS[name]
+    inp = W.make_inputs(wl, 3, with_experts=False)
+    ws = torch.zeros(mk.mk_route_topk_workspace_bytes(wl.T, wl.E), dtype=torch.uint8, device="cuda")
+    mk.mk_route_topk(inp["x"].cuda(), inp["w_router"].cuda(), wl.k, workspace=ws)
+    torch.cuda.synchronize()
+    part = ws[:8 * wl.T * wl.E * 4].view(torch.float32).reshape(8, wl.T, wl.E).cpu().numpy()
+    lg = part[0].copy()
+    for s in range(1, 8):
+        lg = (lg + part[s]).astype(np.float32)
+    ref = oracle.logits(inp["x"], inp["w_router"])
+    bad = lg.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} logits differ; first at {tuple(np.argwhere(bad)[0])}"
+
+
 # ---------------------------------------------------------------- the five workloads
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
