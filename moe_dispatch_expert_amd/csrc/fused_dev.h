@@ -386,8 +386,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     // the barrier the masks give the counts and ranks.  Given ids: per 64-token
     // block, copy and histogram in one workgroup.
     if (wave_topk) {
-        const int units = topk_wave_units(a.T);
-        for (int u = w; u < units; u += G) topk_wave_unit(a.ta, u);
+        topk_wave_loop(a.ta, w, G);
         trace_put(a, kTrSelected, now_ticks());
         trace_put(a, kTrCounted, now_ticks());
         if (!fused_barrier(a, 0x04000000u)) return;
@@ -462,27 +461,44 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     if (w < a.n_mover) {
         int32_t *tok_lds = (int32_t *)st[2] + 256;   // kMoveRows ints after the scan's partials
         const int n_units_all = uoff[a.E_local];
-        for (int u = w; u < n_units_all; u += a.n_mover) {
+        // The arrival counter of unit u's tile.
+        auto unit_tile = [&](int u, int &e, int &q0, int &q1) {
             int lo = 0, hi = a.E_local;   // expert e with uoff[e] <= u < uoff[e+1]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
                 if (uoff[mid] <= u) lo = mid; else hi = mid;
             }
-            const int e = lo;
-            const int q = u - uoff[e];
-            const int q0 = q * kMoveRows;
-            const int q1 = min(off[e + 1] - off[e], q0 + kMoveRows);
-            const int mt = q0 / a.bm;
+            e = lo;
+            q0 = (u - uoff[e]) * kMoveRows;
+            q1 = min(off[e + 1] - off[e], q0 + kMoveRows);
+            return a.tile_cnt + toff[e] + q0 / a.bm;
+        };
+        // Rows resident: one release after all of this workgroup's units (each agent-scope release
+        // writes back the XCD's L2, so one per unit serialises the movers), then relaxed counter
+        // bumps.  Rows from peers: a release per unit, so tiles start as their chunks arrive.
+        const bool batch = a.fl.chunk_rows == 0;
+        for (int u = w; u < n_units_all; u += a.n_mover) {
+            int e, q0, q1;
+            uint32_t *ctr = unit_tile(u, e, q0, q1);
             const uint64_t c0 = now_ticks();
             const bool ok = fused_move_unit(a, cnt, off, e, q0, q1, tok_lds);
             __syncthreads();
             if (!ok) return;
             const uint64_t c1 = now_ticks();
-            if (threadIdx.x == 0)
-                __hip_atomic_fetch_add(a.tile_cnt + toff[e] + mt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            if (!batch && threadIdx.x == 0)
+                __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             copy_ticks += c1 - c0;
             release_ticks += now_ticks() - c1;
             ++n_units;
+        }
+        if (batch && n_units > 0 && threadIdx.x == 0) {   // every wave's stores reached L2 (fused_move_unit)
+            const uint64_t c1 = now_ticks();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            for (int u = w; u < n_units_all; u += a.n_mover) {
+                int e, q0, q1;
+                __hip_atomic_fetch_add(unit_tile(u, e, q0, q1), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            release_ticks += now_ticks() - c1;
         }
     }
     trace_put(a, kTrMoved, now_ticks());

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a)
 }
 
 // Token-per-wave top-k, four tokens per workgroup.
-__global__ __launch_bounds__(256) void k_topk_wave(TopkArgs ta) { topk_wave_unit(ta, blockIdx.x); }
+__global__ __launch_bounds__(256) void k_topk_wave(TopkArgs ta) { topk_wave_loop(ta, blockIdx.x, gridDim.x); }
 
 __global__ __launch_bounds__(256) void k_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user,
                                                      CountArgs ca)

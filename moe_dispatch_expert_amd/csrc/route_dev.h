@@ -215,33 +215,44 @@ struct TopkArgs {
 };
 
 // Top-k and gate of token t with the lanes of one wave spanning the experts
-// (e = lane + 64 v, v < NV, E <= 64 NV).  The 8 partial sums of
-// each logit come straight from the workspace (a token's E partials of one
-// segment are contiguous, so the loads coalesce), all 8 NV of them in flight;
-// the logit is their ordered sum plus the bias.  Then k rounds of a wave-wide
-// max over (logit, -id) keys; ids and gates go to global memory only.
+// (e = lane + 64 v, v < NV, E <= 64 NV).  The 8 partial sums of each logit
+// come straight from the workspace (a token's E partials of one segment are
+// contiguous, so the loads coalesce); the logit is their ordered sum plus the
+// bias.  Then k rounds of a wave-wide max over (logit, -id) keys; ids and
+// gates go to global memory only.  A wave that handles several tokens loads
+// the next token's partials before it selects the current one.
 template <int NV>
-__device__ __forceinline__ void topk_token_wave(const TopkArgs &a, int t)
+struct TopkPartials {
+    float p[NV][kRouterSegments];
+};
+
+template <int NV>
+__device__ __forceinline__ void topk_load(const TopkArgs &a, int t, TopkPartials<NV> &r)
 {
-#pragma clang fp contract(off)
     const int l = threadIdx.x % kWave;
     const size_t sstride = (size_t)a.T * a.E;
     const float *row = a.part + (size_t)t * a.E;
-    float p[NV][kRouterSegments];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int e = min(l + v * kWave, a.E - 1);
 #pragma unroll
-        for (int s = 0; s < kRouterSegments; ++s) p[v][s] = row[s * sstride + e];
+        for (int s = 0; s < kRouterSegments; ++s) r.p[v][s] = row[s * sstride + e];
     }
+}
+
+template <int NV>
+__device__ __forceinline__ void topk_select(const TopkArgs &a, int t, const TopkPartials<NV> &r)
+{
+#pragma clang fp contract(off)
+    const int l = threadIdx.x % kWave;
     float lv[NV];
     uint64_t key[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int e = l + v * kWave;
-        float x = p[v][0];
+        float x = r.p[v][0];
 #pragma unroll
-        for (int s = 1; s < kRouterSegments; ++s) x = x + p[v][s];
+        for (int s = 1; s < kRouterSegments; ++s) x = x + r.p[v][s];
         if (a.bias) x = x + a.bias[min(e, a.E - 1)];
         lv[v] = x;
         key[v] = e < a.E ? topk_key(x, e) : 0ull;
@@ -285,14 +296,35 @@ __device__ __forceinline__ void topk_token_wave(const TopkArgs &a, int t)
 
 // Token-per-wave top-k: workgroup unit u covers tokens 4u .. 4u+3, one per wave.
 __host__ __device__ inline int topk_wave_units(int T) { return (T + 3) / 4; }
-__device__ __forceinline__ void topk_wave_unit(const TopkArgs &a, int u)
+
+// Units u0, u0 + stride, ... (< topk_wave_units(T)) of one workgroup, the next
+// token's partials in flight while the current one is selected.
+template <int NV>
+__device__ __forceinline__ void topk_wave_units_nv(const TopkArgs &a, int u0, int stride)
 {
-    const int t = u * 4 + (int)threadIdx.x / kWave;
-    if (t >= a.T) return;
-    if (a.E <= 128) topk_token_wave<2>(a, t);
-    else if (a.E <= 256) topk_token_wave<4>(a, t);
-    else if (a.E <= 512) topk_token_wave<8>(a, t);
-    else topk_token_wave<16>(a, t);
+    const int wave = (int)threadIdx.x / kWave;
+    const int units = topk_wave_units(a.T);
+    int t = u0 * 4 + wave;
+    if (u0 >= units || t >= a.T) return;
+    TopkPartials<NV> cur, nxt;
+    topk_load<NV>(a, t, cur);
+    for (int u = u0; u < units; u += stride) {
+        const int tn = (u + stride) * 4 + wave;
+        const bool more = u + stride < units && tn < a.T;
+        if (more) topk_load<NV>(a, tn, nxt);
+        topk_select<NV>(a, t, cur);
+        if (!more) break;
+        cur = nxt;
+        t = tn;
+    }
+}
+
+__device__ __forceinline__ void topk_wave_loop(const TopkArgs &a, int u0, int stride)
+{
+    if (a.E <= 128) topk_wave_units_nv<2>(a, u0, stride);
+    else if (a.E <= 256) topk_wave_units_nv<4>(a, u0, stride);
+    else if (a.E <= 512) topk_wave_units_nv<8>(a, u0, stride);
+    else topk_wave_units_nv<16>(a, u0, stride);
 }
 
 
