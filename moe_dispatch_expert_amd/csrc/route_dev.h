@@ -374,7 +374,7 @@ __device__ __forceinline__ void count_block(const CountArgs &a, int blk, const i
             if (active == 0) break;
             const int leader = __ffsll((unsigned long long)active) - 1;
             const int my_first = pend ? ids_lds[l * a.k + (__ffs(pend) - 1)] : -1;
-            const int e = __shfl(my_first, leader, kWave);
+            const int e = __builtin_amdgcn_readlane(my_first, __builtin_amdgcn_readfirstlane(leader));   // uniform
             int jj = -1;
             for (int j = 0; j < a.k; ++j)
                 if (((pend >> j) & 1u) && ids_lds[l * a.k + j] == e) jj = j;
