@@ -13,6 +13,7 @@ zubnet.ai, paragraph 2):
   layout()     per-local-expert counts, exclusive offsets, slots in ascending
                token order, the inverse row -> token map
   expert_rows() fp64 expert GEMM y[r] = x[row_token[r]] . W[e]^T for chosen rows
+  combine()    the next step: out[t] = sum over local choices j of w[t][j] y[slot_of[t][j]]
 """
 import ctypes
 import os
@@ -43,9 +44,11 @@ def _load():
                                   _i32p, _i32p, _i32p, _i32p]
     lib.oracle_expert_rows.argtypes = [_u16p, ctypes.c_int, _u16p, ctypes.c_int, _i32p, ctypes.c_int,
                                        _i32p, _i32p, ctypes.c_int, _f64p]
+    lib.oracle_combine.argtypes = [_f64p, _i32p, ctypes.c_int, ctypes.c_int, _i32p, _f64p, ctypes.c_int,
+                                   ctypes.c_int, _f64p]
     lib.oracle_num_threads.argtypes = []
     for f in (lib.oracle_logits, lib.oracle_topk, lib.oracle_layout, lib.oracle_expert_rows,
-              lib.oracle_num_threads):
+              lib.oracle_combine, lib.oracle_num_threads):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -138,6 +141,27 @@ def expert_rows(x, w_experts, offsets, row_token, rows):
                               _ptr(row_token, _i32p), _ptr(rows, _i32p), rows.size, _ptr(y, _f64p)):
         raise ValueError("oracle_expert_rows: row index out of range")
     return y
+
+
+def combine(y, slot_rows, slot_of, w):
+    """fp64 out [T,N] = sum over local choices j (slot_of >= 0) of w[t][j] * y[row of slot_of[t][j]];
+    y [n,N] holds the rows of the slots slot_rows [n] (every chosen slot must be listed)."""
+    lib = _load()
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float64))
+    slot_rows = np.ascontiguousarray(np.asarray(slot_rows, dtype=np.int32).reshape(-1))
+    slot_of = np.ascontiguousarray(np.asarray(slot_of, dtype=np.int32))
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float64))
+    T, k = slot_of.shape
+    n, N = y.shape
+    assert slot_rows.size == n and w.shape == (T, k)
+    out = np.empty((T, N), dtype=np.float64)
+    if y.size == 0:
+        y = np.zeros((1, max(N, 1)), dtype=np.float64)
+        slot_rows = np.full(1, -2, dtype=np.int32)
+    if lib.oracle_combine(_ptr(y, _f64p), _ptr(slot_rows, _i32p), n, N, _ptr(slot_of, _i32p), _ptr(w, _f64p),
+                          T, k, _ptr(out, _f64p)):
+        raise ValueError("oracle_combine: a chosen slot has no row in y")
+    return out
 
 
 def run(x, w_router, w_experts, k, e_begin=0, bias=None, rows=None):

@@ -190,6 +190,45 @@ int oracle_expert_rows(const uint16_t *x, int d, const uint16_t *w, int N,
     return 0;
 }
 
+/* Step 8 (the next step after the path: combine).  The weighted un-permute
+ * that brings a token's expert outputs back to its own row:
+ *   out[t][n] = sum over j = 0 .. k-1 with slot_of[t][j] >= 0 of
+ *               w[t][j] * y[row_of_slot(slot_of[t][j])][n],
+ * in ascending j, fp64.  Choices that are not local (slot -1) add nothing; the
+ * gate weights are the softmax over all experts (not renormalised), so the
+ * sums of all ranks' partial outputs make the full combine.
+ * y [n_rows,N] fp64 holds the rows of the slots listed in slot_rows [n_rows];
+ * slot_of [T,k]; w [T,k] fp64; out [T,N] fp64.
+ * Returns 1 if a chosen slot is not among slot_rows. */
+int oracle_combine(const double *y, const int32_t *slot_rows, int n_rows, int N,
+                   const int32_t *slot_of, const double *w, int T, int k,
+                   double *out)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(|:bad)
+    for (int t = 0; t < T; ++t) {
+        double *o = out + (size_t)t * N;
+        for (int n = 0; n < N; ++n)
+            o[n] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            const int32_t slot = slot_of[(size_t)t * k + j];
+            if (slot < 0)
+                continue;
+            int q = 0;
+            while (q < n_rows && slot_rows[q] != slot)
+                ++q;
+            if (q == n_rows) {
+                bad = 1;
+                continue;
+            }
+            const double wt = w[(size_t)t * k + j];
+            for (int n = 0; n < N; ++n)
+                o[n] += wt * y[(size_t)q * N + n];
+        }
+    }
+    return bad;
+}
+
 /* Threads the OpenMP loops above use (reported by the CPU baseline). */
 int oracle_num_threads(void)
 {

@@ -288,3 +288,47 @@ def test_mixtral_workload_is_near_uniform():
     count, *_ = oracle.layout(ids, 0, wl.E_local)
     mean = wl.T * wl.k / wl.E
     assert (np.abs(count - mean) < 0.1 * mean).all()
+
+
+# ---------------------------------------------------------------- step 8 (next): combine
+
+def test_combine_golden(golden_dir):
+    """Hand-worked dyadic example (exact): weighted sum over the local choices only."""
+    with open(os.path.join(golden_dir, "combine_example.json")) as f:
+        g = json.load(f)
+    y = np.array(g["y_rows"], dtype=np.float64)
+    out = oracle.combine(y, np.arange(len(y)), np.array(g["slot_of"]), np.array(g["w"]))
+    assert out.tolist() == g["expect"]
+
+
+def test_combine_gate_normalisation():
+    """k = E, every expert local, unit expert outputs: each token's output is the sum of its softmax gate
+    over all experts, which is 1 (ties combine to the gate of step 3, computed independently)."""
+    wl = W.scaled(W.WORKLOADS["tiny"], T=40, d=128, E=6, k=6, E_local=6)
+    inp = W.make_inputs(wl, 7, with_experts=False)
+    _, ids, w = oracle.route(inp["x"], inp["w_router"].numpy(), wl.k)
+    _, offsets, slot_of, _ = oracle.layout(ids, 0, wl.E_local)
+    R = int(offsets[-1])
+    out = oracle.combine(np.ones((R, 3)), np.arange(R), slot_of, w)
+    assert np.abs(out - 1.0).max() < 1e-12
+
+
+def test_combine_choice_order_and_locality():
+    """Permuting a token's choices (slots with their weights) leaves the output unchanged, and a
+    non-local choice (slot -1) equals the same choice with weight 0 (dyadic data: every sum exact)."""
+    rng = np.random.default_rng(11)
+    T, k, N, R = 30, 5, 7, 60
+    y = rng.integers(-64, 64, size=(R, N)) / 8.0
+    slot_of = np.stack([rng.permutation(R)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.integers(0, 32, size=(T, k)) / 64.0
+    base = oracle.combine(y, np.arange(R), slot_of, w)
+    perm = np.stack([rng.permutation(k) for _ in range(T)])
+    rows = np.arange(T)[:, None]
+    assert np.array_equal(oracle.combine(y, np.arange(R), slot_of[rows, perm], w[rows, perm]), base)
+    drop = rng.random((T, k)) < 0.3
+    s2 = np.where(drop, -1, slot_of).astype(np.int32)
+    assert np.array_equal(oracle.combine(y, np.arange(R), s2, w), oracle.combine(y, np.arange(R), slot_of,
+                                                                                  np.where(drop, 0.0, w)))
+    # k = 1, weight 1: the combine is the inverse permutation of the layout (the token's own row)
+    one = oracle.combine(y, np.arange(R), slot_of[:, :1], np.ones((T, 1)))
+    assert np.array_equal(one, y[slot_of[:, 0]])
