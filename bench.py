@@ -170,6 +170,32 @@ def trace_summary(tr: dict) -> dict:
     return out
 
 
+def time_combine(bufs: dict, R: int, steps: int, warmup: int) -> dict:
+    """mk_combine (weighted un-permute of y_perm back to token rows) on the outputs of a step: K launches
+    between two events on the current stream.  Algorithmic bytes: every routed row of y_perm read once,
+    the [T, N] output written once, slot_of and topk_w read once."""
+    import torch
+    import moe_dispatch_expert_amd as mk
+    y, slot_of, gate = bufs["y_perm"], bufs["slot_of"], bufs["topk_w"]
+    T, k = slot_of.shape
+    N = y.shape[1]
+    out = torch.empty(T, N, dtype=torch.bfloat16, device=y.device)
+    for _ in range(warmup):
+        mk.mk_combine(y, slot_of, gate, rows=R, out=out)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        mk.mk_combine(y, slot_of, gate, rows=R, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    alg = R * N * 2 + T * N * 2 + T * k * 8
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"kernel": "k_combine", "ms": round(ms, 4), "alg_bytes": alg, "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
     import oracle
     wl = inp["wl"]
@@ -213,6 +239,8 @@ def main():
     ap.add_argument("--write-traffic", default="", metavar="DIR",
                     help="only turn the rocprofv3 --pmc outputs under DIR into profiles/<kernel>_<workload>_hbm_traffic.json")
     ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"), help="kernel for --write-traffic")
+    ap.add_argument("--combine", action="store_true",
+                    help="also time the next step, mk_combine, on the step's outputs (reported apart, not in value)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -322,6 +350,8 @@ def main():
     if args.trace and not args.staged:
         rec["trace"] = trace_summary(mk.mk_dispatch_gemm_trace(ws, wl.T, wl.d, wl.E, wl.k, wl.e_begin,
                                                                wl.E_local, wl.N, wl.S))
+    if args.combine:
+        rec["combine"] = time_combine(bufs, R, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, R)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)

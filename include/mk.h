@@ -164,6 +164,25 @@ mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *
 mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,
                                   int32_t *words, int32_t *ticks_per_us);
 
+/* Combine, the step after the path: the weighted un-permute that brings each
+ * token's expert outputs back to its own row,
+ *   out[t, n] = bf16_rne( sum over j = 0 .. k-1 with 0 <= slot_of[t, j] < rows
+ *                         of topk_w[t, j] * y_perm[slot_of[t, j], n] ),
+ * fp32 accumulation in ascending j.  A slot of -1 (a choice that is not local)
+ * adds nothing, and so does any slot outside [0, rows); a token without a local
+ * choice gets a zero row.  The gates are used as given (softmax over all
+ * experts, not renormalised), so the outputs of all expert-parallel ranks add
+ * up to the full combine.  The pages name the dispatch kernel and the dynamic
+ * routing of tokens to experts that may live elsewhere (zubnet.ai, paragraph 2;
+ * lefilia.fr, paragraph 3) but do not write this step out; the sum above is
+ * this library's reading.
+ *   y_perm [rows, N] bf16 (mk_dispatch_gemm's output)   slot_of [T, k] int32
+ *   topk_w [T, k] fp32                                  out [T, N] bf16 (out)
+ * Requires T >= 0, 1 <= k <= 32, rows >= 0, N > 0, N % 8 == 0.  T == 0 is a
+ * no-op returning MK_OK.  No workspace. */
+mk_status mk_combine(const void *y_perm, int32_t rows, const int32_t *slot_of, const float *topk_w,
+                     int32_t T, int32_t k, int32_t N, void *out, void *stream);
+
 /* Synchronous: reads the device error word of a dispatch workspace (the caller
  * must have synchronised the stream).  Returns MK_OK, MK_ETIMEOUT or MK_EINVAL;
  * *detail (if non-NULL) receives which wait or id failed.  Clears the word. */

@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
     lib.mk_dispatch_gemm_trace.argtypes = [P(MkShape), P(MkSources), P(ctypes.c_size_t), P(_c_i32), P(_c_i32),
                                            P(_c_i32)]
     lib.mk_dispatch_gemm_trace.restype = _c_i32
+    lib.mk_combine.argtypes = [_vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp]
+    lib.mk_combine.restype = _c_i32
     _lib = lib
     return lib
 
@@ -249,3 +251,19 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
     o["workspace"] = workspace
     o["_sources"] = srcs
     return o
+
+
+def mk_combine(y_perm: torch.Tensor, slot_of: torch.Tensor, topk_w: torch.Tensor, rows: Optional[int] = None,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Weighted un-permute (mk_combine): out[t] = bf16(sum over local choices j of topk_w[t, j] *
+    y_perm[slot_of[t, j]]).  rows = the valid rows of y_perm (default: all of them).  Returns out [T, N]."""
+    T, k = slot_of.shape
+    N = y_perm.shape[1]
+    if rows is None:
+        rows = y_perm.shape[0]
+    if out is None:
+        out = torch.empty(T, N, dtype=torch.bfloat16, device=slot_of.device)
+    st = load().mk_combine(_ptr(y_perm), int(rows), _ptr(slot_of), _ptr(topk_w), T, k, N, _ptr(out),
+                           _stream(stream))
+    _check(st, "mk_combine")
+    return out

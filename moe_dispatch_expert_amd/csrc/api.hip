@@ -416,6 +416,20 @@ mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_
     return MK_OK;
 }
 
+mk_status mk_combine(const void *y_perm, int32_t rows, const int32_t *slot_of, const float *topk_w, int32_t T,
+                     int32_t k, int32_t N, void *out, void *stream)
+{
+    if (T < 0 || k < 1 || k > kMaxK || rows < 0 || N <= 0 || N % 8 != 0) return MK_EINVAL;
+    if (T == 0) return MK_OK;
+    if (!slot_of || !topk_w || !out || (rows > 0 && !y_perm)) return MK_EINVAL;
+    if (!aligned16(slot_of) || !aligned16(topk_w) || !aligned16(out) || (y_perm && !aligned16(y_perm)))
+        return MK_EINVAL;
+    if (launch_combine((const uint16_t *)y_perm, rows, slot_of, topk_w, T, k, N, (uint16_t *)out,
+                       (hipStream_t)stream) != hipSuccess)
+        return MK_EHIP;
+    return MK_OK;
+}
+
 mk_status mk_poll_error(void *workspace, int32_t *detail)
 {
     if (!workspace) return MK_EINVAL;

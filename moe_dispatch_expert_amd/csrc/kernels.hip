@@ -3,6 +3,8 @@
 // persistent kernel, one launch per step.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "fused_dev.h"
 #include "gemm_dev.h"
 #include "layout_dev.h"
@@ -86,6 +88,55 @@ __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
     fused_kernel_body<C>(a, st, ls, off, toff, uoff);
 }
 
+// Combine: wave task q = (token q / nc, 512-column chunk q % nc); the lane owns
+// 8 consecutive columns (16 bytes).  The token's slots and gates are read by
+// the first k lanes and taken one at a time with readlane (uniform), the rows
+// of four choices are loaded before they are accumulated.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *y, int32_t rows, const int32_t *slot_of,
+                                                 const float *gate, int32_t T, int32_t k, int32_t N, uint16_t *out)
+{
+    const int lane = threadIdx.x % kWave;
+    const int nc = (N + 8 * kWave - 1) / (8 * kWave);
+    const int waves = (int)gridDim.x * (int)(blockDim.x / kWave);
+    for (int q = (int)blockIdx.x * (int)(blockDim.x / kWave) + (int)threadIdx.x / kWave; q < T * nc; q += waves) {
+        const int t = __builtin_amdgcn_readfirstlane(q / nc);
+        const int col = (q - t * nc) * 8 * kWave + 8 * lane;
+        const bool in = col < N;   // N % 8 == 0: a lane's 8 columns are all inside or all outside
+        const int my_slot = lane < k ? slot_of[(size_t)t * k + lane] : -1;
+        const float my_w = lane < k ? gate[(size_t)t * k + lane] : 0.0f;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j0 = 0; j0 < k; j0 += 4) {
+            u32x4_t v[4];
+            float wj[4];
+            bool ok[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = min(j0 + u, k - 1);
+                const int slot = __builtin_amdgcn_readlane(my_slot, j);
+                wj[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+                ok[u] = j0 + u < k && slot >= 0 && slot < rows;
+                v[u] = ok[u] && in ? *(const u32x4_t *)(y + (size_t)slot * N + col) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!ok[u]) continue;   // uniform
+                float f[8];
+                unpack8(v[u], f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj[u], f[i], acc[i]);
+            }
+        }
+        if (in) {
+            u32x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+            *(u32x4_t *)(out + (size_t)t * N + col) = o;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- wrappers
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s)
@@ -131,6 +182,15 @@ hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x
                        hipStream_t s)
 {
     hipLaunchKernelGGL(k_move, dim3(1024), dim3(256), 0, s, src, row_token, x_perm, d, hdr);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t *y, int32_t rows, const int32_t *slot_of, const float *gate, int32_t T,
+                          int32_t k, int32_t N, uint16_t *out, hipStream_t s)
+{
+    const long tasks = (long)T * ((N + 8 * kWave - 1) / (8 * kWave));
+    const int grid = (int)std::min<long>((tasks + 3) / 4, 65536);
+    hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, y, rows, slot_of, gate, T, k, N, out);
     return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, h
 hipError_t launch_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user, const CountArgs &ca,
                               hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+// Combine: out[t] = bf16(sum over local choices of gate * y_perm[slot]).
+hipError_t launch_combine(const uint16_t *y, int32_t rows, const int32_t *slot_of, const float *gate, int32_t T,
+                          int32_t k, int32_t N, uint16_t *out, hipStream_t s);
 hipError_t launch_slots(const SlotArgs &a, hipStream_t s);
 hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x_perm, int d, const WsHeader *hdr,
                        hipStream_t s);
