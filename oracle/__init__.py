@@ -14,6 +14,8 @@ zubnet.ai, paragraph 2):
                token order, the inverse row -> token map
   expert_rows() fp64 expert GEMM y[r] = x[row_token[r]] . W[e]^T for chosen rows
   combine()    the next step: out[t] = sum over local choices j of w[t][j] y[slot_of[t][j]]
+  swiglu(), grouped_rows()  the expert FFN after the gate|up GEMM: h = silu(g) * u, then the
+               down-projection z[r] = h[r] . Wd[e]^T over the same expert layout
 """
 import ctypes
 import os
@@ -46,9 +48,12 @@ def _load():
                                        _i32p, _i32p, ctypes.c_int, _f64p]
     lib.oracle_combine.argtypes = [_f64p, _i32p, ctypes.c_int, ctypes.c_int, _i32p, _f64p, ctypes.c_int,
                                    ctypes.c_int, _f64p]
+    lib.oracle_swiglu.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _f64p]
+    lib.oracle_grouped_rows.argtypes = [_u16p, ctypes.c_int, _u16p, ctypes.c_int, _i32p, ctypes.c_int, _i32p,
+                                        ctypes.c_int, _f64p]
     lib.oracle_num_threads.argtypes = []
     for f in (lib.oracle_logits, lib.oracle_topk, lib.oracle_layout, lib.oracle_expert_rows,
-              lib.oracle_combine, lib.oracle_num_threads):
+              lib.oracle_combine, lib.oracle_swiglu, lib.oracle_grouped_rows, lib.oracle_num_threads):
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -162,6 +167,34 @@ def combine(y, slot_rows, slot_of, w):
                           T, k, _ptr(out, _f64p)):
         raise ValueError("oracle_combine: a chosen slot has no row in y")
     return out
+
+
+def swiglu(gu):
+    """fp64 h [rows, F] = silu(g) * u of bf16 rows gu [rows, 2F] (g = first F columns, u = the rest)."""
+    lib = _load()
+    b = _bits(gu)
+    rows, F2 = b.shape
+    assert F2 % 2 == 0
+    h = np.empty((rows, F2 // 2), dtype=np.float64)
+    if lib.oracle_swiglu(_ptr(b, _u16p), rows, F2 // 2, _ptr(h, _f64p)):
+        raise ValueError("oracle_swiglu: bad shape")
+    return h
+
+
+def grouped_rows(a, w, offsets, rows):
+    """fp64 z [len(rows), N]: row r of bf16 a [R, K] times W[e]^T (bf16 w [E_local, N, K]), e the expert of r."""
+    lib = _load()
+    ab, wb = _bits(a), _bits(w)
+    R, K = ab.shape
+    E_local, N, K2 = wb.shape
+    assert K2 == K
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    z = np.empty((rows.size, N), dtype=np.float64)
+    if lib.oracle_grouped_rows(_ptr(ab, _u16p), K, _ptr(wb, _u16p), N, _ptr(offsets, _i32p), E_local,
+                               _ptr(rows, _i32p), rows.size, _ptr(z, _f64p)):
+        raise ValueError("oracle_grouped_rows: row index out of range")
+    return z
 
 
 def run(x, w_router, w_experts, k, e_begin=0, bias=None, rows=None):

@@ -229,6 +229,52 @@ int oracle_combine(const double *y, const int32_t *slot_rows, int n_rows, int N,
     return bad;
 }
 
+/* Next row, expert FFN.  SwiGLU of the gate|up expert output rows:
+ * gu [rows, 2F] holds g = columns [0, F) and u = columns [F, 2F) of each row;
+ * h[r][f] = silu(g) * u with silu(g) = g / (1 + e^-g), fp64.  gu is bf16 bits. */
+int oracle_swiglu(const uint16_t *gu, int rows, int F, double *h)
+{
+    if (rows < 0 || F < 1)
+        return 1;
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int f = 0; f < F; ++f) {
+            const double g = (double)bf16_bits_to_float(gu[(size_t)r * 2 * F + f]);
+            const double u = (double)bf16_bits_to_float(gu[(size_t)r * 2 * F + F + f]);
+            h[(size_t)r * F + f] = g / (1.0 + exp(-g)) * u;
+        }
+    return 0;
+}
+
+/* Next row, expert FFN.  Grouped GEMM over the expert layout for chosen rows:
+ * z[q][n] = sum_i a[rows[q]][i] * w[e][n][i], e the expert whose offsets range
+ * holds rows[q]; a [R, K] and w [E_local, N, K] bf16 bits, z [n_rows, N] fp64. */
+int oracle_grouped_rows(const uint16_t *a, int K, const uint16_t *w, int N,
+                        const int32_t *offsets, int E_local, const int32_t *rows,
+                        int n_rows, double *z)
+{
+    const int R = offsets[E_local];
+    for (int q = 0; q < n_rows; ++q)
+        if (rows[q] < 0 || rows[q] >= R)
+            return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int q = 0; q < n_rows; ++q) {
+        const int r = rows[q];
+        int e = 0;
+        while (!(offsets[e] <= r && r < offsets[e + 1]))
+            ++e;
+        const uint16_t *ar = a + (size_t)r * K;
+        for (int n = 0; n < N; ++n) {
+            const uint16_t *wr = w + ((size_t)e * N + n) * K;
+            double acc = 0.0;
+            for (int i = 0; i < K; ++i)
+                acc += (double)bf16_bits_to_float(ar[i]) * (double)bf16_bits_to_float(wr[i]);
+            z[(size_t)q * N + n] = acc;
+        }
+    }
+    return 0;
+}
+
 /* Threads the OpenMP loops above use (reported by the CPU baseline). */
 int oracle_num_threads(void)
 {

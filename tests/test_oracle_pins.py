@@ -332,3 +332,42 @@ def test_combine_choice_order_and_locality():
     # k = 1, weight 1: the combine is the inverse permutation of the layout (the token's own row)
     one = oracle.combine(y, np.arange(R), slot_of[:, :1], np.ones((T, 1)))
     assert np.array_equal(one, y[slot_of[:, 0]])
+
+
+# ---------------------------------------------------------------- next row: expert FFN (SwiGLU, down-projection)
+
+def test_swiglu_closed_forms():
+    """silu(g) = g * sigmoid(g): with u = 1, h(g) - h(-g) = g and h(g) + h(-g) = g * tanh(g / 2) (library
+    tanh), h(0) = 0; a row [g | u] pairs column f of g with column f of u."""
+    g = np.array([0.0, 0.5, 1.0, 2.0, 3.0, -1.5, 8.0], dtype=np.float32)
+    gb = torch.tensor(g).bfloat16().float().numpy().astype(np.float64)   # exact in bf16
+    F = g.size
+    rows = torch.tensor(np.stack([np.concatenate([g, np.ones(F)]), np.concatenate([-g, np.ones(F)])]),
+                        dtype=torch.float32).bfloat16()
+    h = oracle.swiglu(rows)
+    assert np.allclose(h[0] - h[1], gb, rtol=0, atol=1e-13)
+    assert np.allclose(h[0] + h[1], gb * np.tanh(gb / 2), rtol=1e-13, atol=1e-14)
+    assert h[0][0] == 0.0
+    # split: u_f scales only column f
+    u = np.array([2.0, -1.0, 0.25, 4.0, 1.0, 0.5, -3.0], dtype=np.float32)
+    h2 = oracle.swiglu(torch.tensor(np.concatenate([g, u])[None, :]).bfloat16())
+    assert np.allclose(h2[0], h[0] * u.astype(np.float64), rtol=1e-14, atol=0)
+
+
+def test_grouped_rows_matches_library_matmul():
+    """Each row of the layout times its own expert's W^T: fp64 library matmul per expert range."""
+    rng = np.random.default_rng(5)
+    E_local, K, N = 4, 32, 12
+    counts = np.array([3, 0, 5, 2])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    a = torch.tensor(rng.standard_normal((R, K)), dtype=torch.float32).bfloat16()
+    w = torch.tensor(rng.standard_normal((E_local, N, K)), dtype=torch.float32).bfloat16()
+    z = oracle.grouped_rows(a, w, offsets, np.arange(R))
+    af, wf = a.double().numpy(), w.double().numpy()
+    for e in range(E_local):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            assert np.allclose(z[lo:hi], af[lo:hi] @ wf[e].T, rtol=1e-12, atol=1e-12)
+    sub = np.array([9, 0, 4])
+    assert np.array_equal(oracle.grouped_rows(a, w, offsets, sub), z[sub])
