@@ -196,6 +196,51 @@ def time_combine(bufs: dict, R: int, steps: int, warmup: int) -> dict:
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int) -> dict:
+    """The expert FFN after the step, its y_perm read as [gate | up] (F = N / 2): mk_swiglu, then the
+    down-projection mk_grouped_gemm with a seeded W_down [E_local, d, F] ~ N(0, 1/F).  Each timed K times
+    between two events on the current stream."""
+    import torch
+    import moe_dispatch_expert_amd as mk
+    y = bufs["y_perm"]
+    F = wl.N // 2
+    if wl.N % 2 or F % 128:
+        return {"skipped": f"F = N / 2 = {wl.N / 2} is not a multiple of 128"}
+    g = torch.Generator().manual_seed(seed * 1000 + 5)
+    wd = torch.empty(wl.E_local, wl.d, F, dtype=torch.bfloat16)
+    for e in range(wl.E_local):
+        wd[e] = (torch.randn(wl.d, F, generator=g) / F ** 0.5).to(torch.bfloat16)
+    wd = wd.to(y.device)
+    h = torch.empty(y.shape[0], F, dtype=torch.bfloat16, device=y.device)
+    z = torch.empty(y.shape[0], wl.d, dtype=torch.bfloat16, device=y.device)
+    ws = torch.empty(mk.mk_grouped_gemm_workspace_bytes(wl.E_local), dtype=torch.uint8, device=y.device)
+    off = bufs["expert_offsets"]
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms_act = timed(lambda: mk.mk_swiglu(y, rows=R, out=h))
+    ms_down = timed(lambda: mk.mk_grouped_gemm(h, off, wd, out=z, workspace=ws))
+    act_bytes = R * 3 * F * 2
+    flops = 2.0 * R * F * wl.d
+    return {"F": F,
+            "swiglu": {"kernel": "k_swiglu", "ms": round(ms_act, 4), "alg_bytes": act_bytes,
+                       "achieved": round(act_bytes / (ms_act * 1e-3) / 1e9, 1), "unit": "GB/s",
+                       "frac": round(act_bytes / (ms_act * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "down": {"kernel": "k_gemm", "ms": round(ms_down, 4), "flops": flops,
+                     "achieved": round(flops / (ms_down * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                     "frac": round(flops / (ms_down * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+
+
 def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
     import oracle
     wl = inp["wl"]
@@ -239,6 +284,9 @@ def main():
     ap.add_argument("--write-traffic", default="", metavar="DIR",
                     help="only turn the rocprofv3 --pmc outputs under DIR into profiles/<kernel>_<workload>_hbm_traffic.json")
     ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"), help="kernel for --write-traffic")
+    ap.add_argument("--ffn", action="store_true",
+                    help="also time the expert FFN after the step (its y_perm read as [gate | up], F = N / 2): "
+                         "mk_swiglu and the down-projection mk_grouped_gemm (reported apart, not in value)")
     ap.add_argument("--combine", action="store_true",
                     help="also time the next step, mk_combine, on the step's outputs (reported apart, not in value)")
     args = ap.parse_args()
@@ -352,6 +400,8 @@ def main():
                                                                wl.E_local, wl.N, wl.S))
     if args.combine:
         rec["combine"] = time_combine(bufs, R, args.steps, args.warmup)
+    if args.ffn:
+        rec["ffn"] = time_ffn(bufs, R, wl, args.seed, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, R)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)

@@ -183,6 +183,29 @@ mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_
 mk_status mk_combine(const void *y_perm, int32_t rows, const int32_t *slot_of, const float *topk_w,
                      int32_t T, int32_t k, int32_t N, void *out, void *stream);
 
+/* Expert FFN after the gate|up GEMM (next row: the pages name the MoE
+ * Dispatch+GEMM kernel, zubnet.ai paragraph 2, whose experts in MoE models are
+ * gated FFNs; the activation and the down-projection below are this library's
+ * reading).  With w_experts of mk_dispatch_gemm holding the gate rows and then
+ * the up rows of every expert ([E_local, 2F, d]), y_perm rows are [g | u]:
+ *   h[r, f] = bf16_rne( silu(g[r, f]) * u[r, f] ),  silu(g) = g / (1 + e^-g), fp32.
+ *   gate_up [rows, 2F] bf16    h [rows, F] bf16 (out)
+ * Requires rows >= 0, F > 0, F % 8 == 0; rows == 0 is a no-op. */
+mk_status mk_swiglu(const void *gate_up, int32_t rows, int32_t F, void *h, void *stream);
+
+/* Grouped GEMM over an expert layout (the down-projection of the expert FFN):
+ *   y[r, n] = bf16_rne( sum_i a[r, i] * w[e, n, i] ),  fp32 accumulation,
+ * for every row r of expert e, offsets[e] <= r < offsets[e + 1] (the layout
+ * mk_dispatch_gemm returns).  R = offsets[E_local] is read on the device.
+ *   a [>= R, K] bf16    expert_offsets [E_local + 1] int32 (non-decreasing, offsets[0] = 0)
+ *   w [E_local, N, K] bf16 (K contiguous)    y [>= R, N] bf16 (out; rows >= R untouched)
+ *   workspace mk_grouped_gemm_workspace_bytes(E_local) bytes, any contents
+ * Requires 1 <= E_local <= 1024, K % 128 == 0 (else MK_EUNSUPPORTED for K % 8 == 0),
+ * N > 0, N % 8 == 0. */
+size_t mk_grouped_gemm_workspace_bytes(int32_t E_local);
+mk_status mk_grouped_gemm(const void *a, const int32_t *expert_offsets, int32_t E_local, const void *w, int32_t K,
+                          int32_t N, void *y, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Synchronous: reads the device error word of a dispatch workspace (the caller
  * must have synchronised the stream).  Returns MK_OK, MK_ETIMEOUT or MK_EINVAL;
  * *detail (if non-NULL) receives which wait or id failed.  Clears the word. */

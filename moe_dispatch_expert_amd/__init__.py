@@ -83,6 +83,12 @@ def load() -> ctypes.CDLL:
     lib.mk_dispatch_gemm_trace.restype = _c_i32
     lib.mk_combine.argtypes = [_vp, _c_i32, _vp, _vp, _c_i32, _c_i32, _c_i32, _vp, _vp]
     lib.mk_combine.restype = _c_i32
+    lib.mk_swiglu.argtypes = [_vp, _c_i32, _c_i32, _vp, _vp]
+    lib.mk_swiglu.restype = _c_i32
+    lib.mk_grouped_gemm_workspace_bytes.argtypes = [_c_i32]
+    lib.mk_grouped_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.mk_grouped_gemm.argtypes = [_vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.mk_grouped_gemm.restype = _c_i32
     _lib = lib
     return lib
 
@@ -267,3 +273,34 @@ def mk_combine(y_perm: torch.Tensor, slot_of: torch.Tensor, topk_w: torch.Tensor
                            _stream(stream))
     _check(st, "mk_combine")
     return out
+
+
+def mk_swiglu(gate_up: torch.Tensor, rows: Optional[int] = None, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """h = bf16(silu(g) * u) of [g | u] rows (mk_swiglu).  Returns h [rows_total, F]."""
+    R2, F2 = gate_up.shape
+    F = F2 // 2
+    if rows is None:
+        rows = R2
+    if out is None:
+        out = torch.empty(R2, F, dtype=torch.bfloat16, device=gate_up.device)
+    _check(load().mk_swiglu(_ptr(gate_up), int(rows), F, _ptr(out), _stream(stream)), "mk_swiglu")
+    return out
+
+
+def mk_grouped_gemm(a: torch.Tensor, expert_offsets: torch.Tensor, w: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """y[r] = bf16(a[r] . W[e]^T) for the rows r of each expert e of the layout (mk_grouped_gemm)."""
+    E_local, N, K = w.shape
+    if out is None:
+        out = torch.empty(a.shape[0], N, dtype=torch.bfloat16, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(mk_grouped_gemm_workspace_bytes(E_local), dtype=torch.uint8, device=a.device)
+    _check(load().mk_grouped_gemm(_ptr(a), _ptr(expert_offsets), E_local, _ptr(w), K, N, _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)), "mk_grouped_gemm")
+    return out
+
+
+def mk_grouped_gemm_workspace_bytes(E_local: int) -> int:
+    return int(load().mk_grouped_gemm_workspace_bytes(E_local))

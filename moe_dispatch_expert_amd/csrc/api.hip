@@ -430,6 +430,53 @@ mk_status mk_combine(const void *y_perm, int32_t rows, const int32_t *slot_of, c
     return MK_OK;
 }
 
+mk_status mk_swiglu(const void *gate_up, int32_t rows, int32_t F, void *h, void *stream)
+{
+    if (rows < 0 || F <= 0 || F % 8 != 0) return MK_EINVAL;
+    if (rows == 0) return MK_OK;
+    if (!gate_up || !h || !aligned16(gate_up) || !aligned16(h)) return MK_EINVAL;
+    if (launch_swiglu((const uint16_t *)gate_up, rows, F, (uint16_t *)h, (hipStream_t)stream) != hipSuccess)
+        return MK_EHIP;
+    return MK_OK;
+}
+
+size_t mk_grouped_gemm_workspace_bytes(int32_t E_local)
+{
+    if (E_local < 1 || E_local > 1024) return 0;
+    return sizeof(WsHeader) + align256((size_t)(E_local + 1) * 4);
+}
+
+mk_status mk_grouped_gemm(const void *a, const int32_t *expert_offsets, int32_t E_local, const void *w, int32_t K,
+                          int32_t N, void *y, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (E_local < 1 || E_local > 1024 || K <= 0 || N <= 0 || N % 8 != 0 || K % 8 != 0) return MK_EINVAL;
+    if (K % 128 != 0) return MK_EUNSUPPORTED;
+    if (!a || !expert_offsets || !w || !y || !workspace) return MK_EINVAL;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(workspace) || !aligned16(expert_offsets))
+        return MK_EINVAL;
+    if (workspace_bytes < mk_grouped_gemm_workspace_bytes(E_local)) return MK_EWORKSPACE;
+    hipStream_t hs = (hipStream_t)stream;
+    WsHeader *hdr = (WsHeader *)workspace;
+    int32_t *tile_off = (int32_t *)((char *)workspace + sizeof(WsHeader));
+    if (launch_tiles(expert_offsets, E_local, 256, tile_off, hdr, hs) != hipSuccess) return MK_EHIP;
+    GemmArgs ga{};
+    ga.x_perm = (const uint16_t *)a;
+    ga.w = (const uint16_t *)w;
+    ga.y = (uint16_t *)y;
+    ga.offsets = expert_offsets;
+    ga.tile_off = tile_off;
+    ga.hdr = hdr;
+    ga.d = K;
+    ga.N = N;
+    ga.E_local = E_local;
+    int grid = gemm_max_grid(256, 256);
+    if (grid <= 0) return MK_EHIP;
+    grid -= grid % 8;
+    if (grid < 8) grid = 8;
+    if (launch_gemm(ga, 256, 256, grid, hs) != hipSuccess) return MK_EHIP;
+    return MK_OK;
+}
+
 mk_status mk_poll_error(void *workspace, int32_t *detail)
 {
     if (!workspace) return MK_EINVAL;

@@ -137,6 +137,41 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *y, int32_t rows
     }
 }
 
+// SwiGLU over gate|up rows: item i = (row i / (F / 8), 8 columns); h = bf16(silu(g) * u), fp32.
+__global__ __launch_bounds__(256) void k_swiglu(const uint16_t *gu, int32_t rows, int32_t F, uint16_t *h)
+{
+    const long items = (long)rows * (F / 8);
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += (long)gridDim.x * blockDim.x) {
+        const long r = i / (F / 8);
+        const int c = (int)(i - r * (F / 8)) * 8;
+        float g[8], u[8];
+        unpack8(*(const u32x4_t *)(gu + r * 2 * F + c), g);
+        unpack8(*(const u32x4_t *)(gu + r * 2 * F + F + c), u);
+        u32x4_t o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = g[2 * q] / (1.0f + expf(-g[2 * q])) * u[2 * q];
+            const float b = g[2 * q + 1] / (1.0f + expf(-g[2 * q + 1])) * u[2 * q + 1];
+            o[q] = pack_bf16x2(a, b);
+        }
+        *(u32x4_t *)(h + r * F + c) = o;
+    }
+}
+
+// The row-tile table of a layout given by its expert offsets (one thread).
+__global__ void k_tiles(const int32_t *offsets, int32_t E_local, int32_t bm, int32_t *tile_off, WsHeader *hdr)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int32_t t = 0;
+    tile_off[0] = 0;
+    for (int e = 0; e < E_local; ++e) {
+        t += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+        tile_off[e + 1] = t;
+    }
+    hdr->n_tiles = (uint32_t)t;
+    hdr->R = (uint32_t)offsets[E_local];
+}
+
 // ---------------------------------------------------------------- wrappers
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s)
@@ -191,6 +226,21 @@ hipError_t launch_combine(const uint16_t *y, int32_t rows, const int32_t *slot_o
     const long tasks = (long)T * ((N + 8 * kWave - 1) / (8 * kWave));
     const int grid = (int)std::min<long>((tasks + 3) / 4, 65536);
     hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, y, rows, slot_of, gate, T, k, N, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const uint16_t *gu, int32_t rows, int32_t F, uint16_t *h, hipStream_t s)
+{
+    const long items = (long)rows * (F / 8);
+    const int grid = (int)std::min<long>((items + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_swiglu, dim3(grid), dim3(256), 0, s, gu, rows, F, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiles(const int32_t *offsets, int32_t E_local, int32_t bm, int32_t *tile_off, WsHeader *hdr,
+                        hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(64), 0, s, offsets, E_local, bm, tile_off, hdr);
     return hipGetLastError();
 }
 

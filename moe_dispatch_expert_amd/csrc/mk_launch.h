@@ -14,6 +14,7 @@ struct ScanArgs;
 struct SlotArgs;
 struct GemmArgs;
 struct FusedArgs;
+struct WsHeader;
 
 // Router partial sums, one wave task per wave (router_tasks).
 hipError_t launch_router(const RouterArgs &a, hipStream_t s);
@@ -23,6 +24,10 @@ hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, h
 hipError_t launch_count_given(const int32_t *ids_in, int32_t *ids_ws, int32_t *ids_user, const CountArgs &ca,
                               hipStream_t s);
 hipError_t launch_scan(const ScanArgs &a, hipStream_t s);
+// Expert FFN: h = bf16(silu(g) * u) over [g | u] rows; the row-tile table of a given layout.
+hipError_t launch_swiglu(const uint16_t *gu, int32_t rows, int32_t F, uint16_t *h, hipStream_t s);
+hipError_t launch_tiles(const int32_t *offsets, int32_t E_local, int32_t bm, int32_t *tile_off, WsHeader *hdr,
+                        hipStream_t s);
 // Combine: out[t] = bf16(sum over local choices of gate * y_perm[slot]).
 hipError_t launch_combine(const uint16_t *y, int32_t rows, const int32_t *slot_of, const float *gate, int32_t T,
                           int32_t k, int32_t N, uint16_t *out, hipStream_t s);

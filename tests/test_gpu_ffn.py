@@ -1,0 +1,75 @@
+"""Expert FFN after the gate|up GEMM (the next row): mk_swiglu and the
+down-projection mk_grouped_gemm against the oracle on the same seeded bf16
+inputs (made here, not by the HIP path).
+
+Tolerances: SwiGLU is fp32 then one bf16 rounding, |h - ref| <= 2^-8 |ref| +
+1e-6; the grouped GEMM is the expert-output bar, max(1e-2 |ref|, 1e-2)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_dispatch_expert_amd as mk
+import oracle
+from gpu_cases import Y_FLOOR, Y_REL, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name(request):
+    say(f"\n[gpu case] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+def _bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("rows,F", [(300, 520), (1, 8), (64, 2048)])
+def test_swiglu_matches_oracle(rows, F):
+    gu = _bf16((rows, 2 * F), 21 + rows, scale=3.0)
+    h = mk.mk_swiglu(gu.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.swiglu(gu)
+    got = h.float().cpu().numpy()
+    bad = np.abs(got - ref) > 2.0 ** -8 * np.abs(ref) + 1e-6
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
+
+
+def _layout(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("counts,K,N", [
+    ([300, 0, 37, 256, 129], 256, 264),      # empty expert, ragged tails of every tile height
+    ([1, 2, 513], 384, 520),                  # one-row experts, a tile and a half
+    ([64] * 8, 128, 256),
+])
+def test_grouped_gemm_matches_oracle(counts, K, N):
+    offsets = _layout(counts)
+    R, E_local = int(offsets[-1]), len(counts)
+    a = _bf16((R + 5, K), 31 + K)             # 5 rows past R that must not matter
+    w = _bf16((E_local, N, K), 41 + N, scale=K ** -0.5)
+    out = torch.full((R + 5, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    mk.mk_grouped_gemm(a.cuda(), torch.from_numpy(offsets).cuda(), w.cuda(), out=out)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_rows(a[:R], w, offsets, np.arange(R))
+    got = out[:R].float().cpu().numpy()
+    bad = np.abs(got - ref) > np.maximum(Y_REL * np.abs(ref), Y_FLOOR)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
+    assert (out[R:] == 7.0).all(), "rows past R were written"
+
+
+def test_grouped_gemm_empty_layout_and_errors():
+    w = _bf16((3, 16, 128), 1)
+    out = torch.full((4, 16), 7.0, dtype=torch.bfloat16, device="cuda")
+    mk.mk_grouped_gemm(torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda"),
+                       torch.zeros(4, dtype=torch.int32, device="cuda"), w.cuda(), out=out)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+    with pytest.raises(mk.MkError):   # K % 128 != 0: unsupported, nothing launched
+        mk.mk_grouped_gemm(torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda"),
+                           torch.zeros(4, dtype=torch.int32, device="cuda"),
+                           torch.zeros(3, 16, 64, dtype=torch.bfloat16, device="cuda"))
