@@ -284,6 +284,9 @@ def main():
     ap.add_argument("--write-traffic", default="", metavar="DIR",
                     help="only turn the rocprofv3 --pmc outputs under DIR into profiles/<kernel>_<workload>_hbm_traffic.json")
     ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"), help="kernel for --write-traffic")
+    ap.add_argument("--evict-mall", action="store_true",
+                    help="read 1 GiB before every step (outside the launch events) so no input is left in the "
+                         "256 MiB Infinity Cache; value and roofline then come from the launch events")
     ap.add_argument("--ffn", action="store_true",
                     help="also time the expert FFN after the step (its y_perm read as [gate | up], F = N / 2): "
                          "mk_swiglu and the down-projection mk_grouped_gemm (reported apart, not in value)")
@@ -347,14 +350,20 @@ def main():
         raise SystemExit(f"device error {mk.mk_status_str(st)} ({detail})")
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    scratch = torch.ones(1 << 30, dtype=torch.uint8, device=dev) if args.evict_mall else None
     t_start.record()
     for i in range(args.steps):
+        if scratch is not None:   # read, not write: evicted lines are clean, so no write-back lands in the step
+            scratch.sum(dtype=torch.int64)
         step(i)
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     gemm_ms = float(np.mean([_elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in range(args.steps)]))
+    if scratch is not None:   # the evicting writes sit between the steps: time the launches only
+        ms_step = gemm_ms
+        del scratch
     for e in evs:
         hip.hipEventDestroy(e)
 
@@ -395,6 +404,8 @@ def main():
     }
     if args.staged or args.movers:
         rec["config"]["path"] = "staged" if args.staged else f"fused, {args.movers} movers"
+    if args.evict_mall:
+        rec["config"]["mall"] = "1 GiB read before every step; step time = launch time"
     if args.trace and not args.staged:
         rec["trace"] = trace_summary(mk.mk_dispatch_gemm_trace(ws, wl.T, wl.d, wl.E, wl.k, wl.e_begin,
                                                                wl.E_local, wl.N, wl.S))
