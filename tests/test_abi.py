@@ -96,3 +96,29 @@ def test_workspace_bytes_and_tuning_without_gpu():
     assert t["bm"] > 0 and t["bn"] > 0
     with pytest.raises(mk.MkError):
         mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14335)
+
+
+def test_next_steps_argument_errors_are_synchronous():
+    """mk_combine, mk_swiglu and mk_grouped_gemm refuse bad arguments before touching the device, and
+    their empty cases are no-ops."""
+    lib = mk.load()
+    fake = ctypes.c_void_p(0x1000)            # aligned, never dereferenced: every call below returns early
+    odd = ctypes.c_void_p(0x1008)             # 8-byte aligned only
+    # combine: k range, N % 8, T == 0 no-op, null and misaligned pointers
+    assert lib.mk_combine(fake, 4, fake, fake, 4, 0, 64, fake, None) == mk.MK_EINVAL
+    assert lib.mk_combine(fake, 4, fake, fake, 4, 33, 64, fake, None) == mk.MK_EINVAL
+    assert lib.mk_combine(fake, 4, fake, fake, 4, 2, 60, fake, None) == mk.MK_EINVAL
+    assert lib.mk_combine(None, 4, None, None, 0, 2, 64, None, None) == mk.MK_OK
+    assert lib.mk_combine(fake, 4, None, fake, 4, 2, 64, fake, None) == mk.MK_EINVAL
+    assert lib.mk_combine(fake, 4, fake, fake, 4, 2, 64, odd, None) == mk.MK_EINVAL
+    # swiglu: F % 8, rows == 0 no-op, misaligned
+    assert lib.mk_swiglu(fake, 4, 12, fake, None) == mk.MK_EINVAL
+    assert lib.mk_swiglu(None, 0, 16, None, None) == mk.MK_OK
+    assert lib.mk_swiglu(odd, 4, 16, fake, None) == mk.MK_EINVAL
+    # grouped GEMM: E_local range, K % 128 unsupported, workspace size, N % 8
+    assert lib.mk_grouped_gemm(fake, fake, 0, fake, 128, 64, fake, fake, 4096, None) == mk.MK_EINVAL
+    assert lib.mk_grouped_gemm(fake, fake, 4, fake, 64, 64, fake, fake, 4096, None) == mk.MK_EUNSUPPORTED
+    assert lib.mk_grouped_gemm(fake, fake, 4, fake, 128, 60, fake, fake, 4096, None) == mk.MK_EINVAL
+    need = lib.mk_grouped_gemm_workspace_bytes(4)
+    assert need > 0 and lib.mk_grouped_gemm_workspace_bytes(0) == 0
+    assert lib.mk_grouped_gemm(fake, fake, 4, fake, 128, 64, fake, fake, need - 1, None) == mk.MK_EWORKSPACE
