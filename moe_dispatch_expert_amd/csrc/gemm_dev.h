@@ -432,6 +432,19 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
     MK_GEMM_SLAB(1, r0, j + 1, false);
 #undef MK_GEMM_SLAB
 
+    // Distance between the last MFMA and the first read of its accumulators.  The compiler pads that
+    // read to its own model of the instruction's latency; a build whose first read came 11 wait
+    // states after the last 32x32x16 MFMA got stale values for that register block, one of 13 has
+    // not.  Three more s_nops make the distance independent of how the epilogue is scheduled: the
+    // empty statements take the accumulators as operands, so every later read or copy follows them.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::MI; ++j) asm volatile("" : "+a"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
+
     // Epilogue: claim the next task, stage the outputs in LDS, store them as whole row segments.
     __syncthreads();   // every wave is done with the stages before the epilogue reuses them
     stage_tile<C>(acc, ls, wave, lane);
