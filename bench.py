@@ -196,10 +196,11 @@ def time_combine(bufs: dict, R: int, steps: int, warmup: int) -> dict:
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int) -> dict:
+def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int, x_dev, w_experts) -> dict:
     """The expert FFN after the step, its y_perm read as [gate | up] (F = N / 2): mk_swiglu, then the
-    down-projection mk_grouped_gemm with a seeded W_down [E_local, d, F] ~ N(0, 1/F).  Each timed K times
-    between two events on the current stream."""
+    down-projection mk_grouped_gemm with a seeded W_down [E_local, d, F] ~ N(0, 1/F).  Also the gate|up
+    GEMM over the permuted rows both ways: mk_grouped_gemm + mk_swiglu, and mk_grouped_gemm_swiglu
+    (SwiGLU in the GEMM's epilogue).  Each timed K times between two events on the current stream."""
     import torch
     import moe_dispatch_expert_amd as mk
     y = bufs["y_perm"]
@@ -230,6 +231,13 @@ def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int) -> dict
 
     ms_act = timed(lambda: mk.mk_swiglu(y, rows=R, out=h))
     ms_down = timed(lambda: mk.mk_grouped_gemm(h, off, wd, out=z, workspace=ws))
+    a = x_dev[bufs["row_token"][:R].long()].contiguous()   # the permuted rows (gathered outside the timing)
+    gu = torch.empty(R, wl.N, dtype=torch.bfloat16, device=y.device)
+    h2 = torch.empty(R, F, dtype=torch.bfloat16, device=y.device)
+    ms_sep = timed(lambda: (mk.mk_grouped_gemm(a, off, w_experts, out=gu, workspace=ws),
+                            mk.mk_swiglu(gu, rows=R, out=h2)))
+    ms_fused = timed(lambda: mk.mk_grouped_gemm_swiglu(a, off, w_experts, out=h2, workspace=ws))
+    gu_flops = 2.0 * R * wl.d * wl.N
     act_bytes = R * 3 * F * 2
     flops = 2.0 * R * F * wl.d
     return {"F": F,
@@ -238,7 +246,13 @@ def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int) -> dict
                        "frac": round(act_bytes / (ms_act * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "down": {"kernel": "k_gemm", "ms": round(ms_down, 4), "flops": flops,
                      "achieved": round(flops / (ms_down * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                     "frac": round(flops / (ms_down * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+                     "frac": round(flops / (ms_down * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "gate_up_then_swiglu": {"kernels": "k_gemm + k_swiglu", "ms": round(ms_sep, 4), "flops": gu_flops,
+                                    "achieved": round(gu_flops / (ms_sep * 1e-3) / 1e12, 2), "unit": "TFLOP/s"},
+            "gate_up_swiglu_fused": {"kernel": "k_gemm (SwiGLU epilogue)", "ms": round(ms_fused, 4),
+                                     "flops": gu_flops,
+                                     "achieved": round(gu_flops / (ms_fused * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                                     "frac": round(gu_flops / (ms_fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
 
 
 def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
@@ -412,7 +426,8 @@ def main():
     if args.combine:
         rec["combine"] = time_combine(bufs, R, args.steps, args.warmup)
     if args.ffn:
-        rec["ffn"] = time_ffn(bufs, R, wl, args.seed, args.steps, args.warmup)
+        rec["ffn"] = time_ffn(bufs, R, wl, args.seed, args.steps, args.warmup,
+                              xs if wl.S == 1 else torch.cat(xs), we)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, R)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)

@@ -206,6 +206,21 @@ size_t mk_grouped_gemm_workspace_bytes(int32_t E_local);
 mk_status mk_grouped_gemm(const void *a, const int32_t *expert_offsets, int32_t E_local, const void *w, int32_t K,
                           int32_t N, void *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* The expert FFN's gate|up GEMM with the SwiGLU of mk_swiglu in its epilogue
+ * (the same reading of the pages as mk_swiglu): for every row r of expert e,
+ *   g = bf16_rne( sum_i a[r, i] * w_gate_up[e, f, i] ),  u = bf16_rne( sum_i a[r, i] * w_gate_up[e, F + f, i] ),
+ *   h[r, f] = bf16_rne( silu(g) * u ),  fp32 accumulation and activation,
+ * i.e. bit for bit mk_grouped_gemm (N = 2F) followed by mk_swiglu, without the
+ * [R, 2F] intermediate in memory.
+ *   a [>= R, K] bf16    expert_offsets [E_local + 1] int32 as for mk_grouped_gemm
+ *   w_gate_up [E_local, 2F, K] bf16 (gate rows, then up rows; K contiguous)
+ *   h [>= R, F] bf16 (out; rows >= R untouched)
+ *   workspace mk_grouped_gemm_workspace_bytes(E_local) bytes, any contents
+ * Requires 1 <= E_local <= 1024, K % 128 == 0 (else MK_EUNSUPPORTED for K % 8 == 0),
+ * F > 0, F % 8 == 0, (2F + 256) * K * 2 < 2^31 (else MK_EUNSUPPORTED). */
+mk_status mk_grouped_gemm_swiglu(const void *a, const int32_t *expert_offsets, int32_t E_local, const void *w_gate_up,
+                                 int32_t K, int32_t F, void *h, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Synchronous: reads the device error word of a dispatch workspace (the caller
  * must have synchronised the stream).  Returns MK_OK, MK_ETIMEOUT or MK_EINVAL;
  * *detail (if non-NULL) receives which wait or id failed.  Clears the word. */

@@ -89,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.mk_grouped_gemm_workspace_bytes.restype = ctypes.c_size_t
     lib.mk_grouped_gemm.argtypes = [_vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]
     lib.mk_grouped_gemm.restype = _c_i32
+    lib.mk_grouped_gemm_swiglu.argtypes = [_vp, _vp, _c_i32, _vp, _c_i32, _c_i32, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.mk_grouped_gemm_swiglu.restype = _c_i32
     _lib = lib
     return lib
 
@@ -299,6 +301,23 @@ def mk_grouped_gemm(a: torch.Tensor, expert_offsets: torch.Tensor, w: torch.Tens
         workspace = torch.empty(mk_grouped_gemm_workspace_bytes(E_local), dtype=torch.uint8, device=a.device)
     _check(load().mk_grouped_gemm(_ptr(a), _ptr(expert_offsets), E_local, _ptr(w), K, N, _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)), "mk_grouped_gemm")
+    return out
+
+
+def mk_grouped_gemm_swiglu(a: torch.Tensor, expert_offsets: torch.Tensor, w_gate_up: torch.Tensor,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """h[r] = bf16(silu(g) * u) with [g | u] = bf16(a[r] . W[e]^T), W[e] = [gate; up] of 2F rows
+    (mk_grouped_gemm_swiglu)."""
+    E_local, two_f, K = w_gate_up.shape
+    F = two_f // 2
+    if out is None:
+        out = torch.empty(a.shape[0], F, dtype=torch.bfloat16, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(mk_grouped_gemm_workspace_bytes(E_local), dtype=torch.uint8, device=a.device)
+    _check(load().mk_grouped_gemm_swiglu(_ptr(a), _ptr(expert_offsets), E_local, _ptr(w_gate_up), K, F,
+                                         _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mk_grouped_gemm_swiglu")
     return out
 
 

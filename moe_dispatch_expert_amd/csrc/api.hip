@@ -477,6 +477,40 @@ mk_status mk_grouped_gemm(const void *a, const int32_t *expert_offsets, int32_t 
     return MK_OK;
 }
 
+mk_status mk_grouped_gemm_swiglu(const void *a, const int32_t *expert_offsets, int32_t E_local, const void *w_gate_up,
+                                 int32_t K, int32_t F, void *h, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (E_local < 1 || E_local > 1024 || K <= 0 || F <= 0 || F % 8 != 0 || K % 8 != 0) return MK_EINVAL;
+    if (K % 128 != 0) return MK_EUNSUPPORTED;
+    // the tiles' W row offsets are 32-bit: 2F + 256 rows of K bf16 must stay below 2 GiB
+    if ((int64_t)(2 * (int64_t)F + 256) * K * 2 >= ((int64_t)1 << 31)) return MK_EUNSUPPORTED;
+    if (!a || !expert_offsets || !w_gate_up || !h || !workspace) return MK_EINVAL;
+    if (!aligned16(a) || !aligned16(w_gate_up) || !aligned16(h) || !aligned16(workspace) || !aligned16(expert_offsets))
+        return MK_EINVAL;
+    if (workspace_bytes < mk_grouped_gemm_workspace_bytes(E_local)) return MK_EWORKSPACE;
+    hipStream_t hs = (hipStream_t)stream;
+    WsHeader *hdr = (WsHeader *)workspace;
+    int32_t *tile_off = (int32_t *)((char *)workspace + sizeof(WsHeader));
+    if (launch_tiles(expert_offsets, E_local, 256, tile_off, hdr, hs) != hipSuccess) return MK_EHIP;
+    GemmArgs ga{};
+    ga.x_perm = (const uint16_t *)a;
+    ga.w = (const uint16_t *)w_gate_up;
+    ga.y = (uint16_t *)h;
+    ga.offsets = expert_offsets;
+    ga.tile_off = tile_off;
+    ga.hdr = hdr;
+    ga.d = K;
+    ga.N = 2 * F;
+    ga.F = F;
+    ga.E_local = E_local;
+    int grid = gemm_max_grid(256, 256);
+    if (grid <= 0) return MK_EHIP;
+    grid -= grid % 8;
+    if (grid < 8) grid = 8;
+    if (launch_gemm_swiglu(ga, grid, hs) != hipSuccess) return MK_EHIP;
+    return MK_OK;
+}
+
 mk_status mk_poll_error(void *workspace, int32_t *detail)
 {
     if (!workspace) return MK_EINVAL;

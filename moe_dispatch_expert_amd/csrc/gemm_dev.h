@@ -56,6 +56,9 @@ struct GemmArgs {
     const int32_t *tile_off;     // [E_local + 1] exclusive prefix of row tiles
     WsHeader *hdr;
     int32_t d, N, E_local;
+    // SwiGLU launches only: F features per expert; W holds 2F rows per expert (gate rows, then up rows),
+    // so N == 2F, and y is h [rows, F] = silu(gate) * up.
+    int32_t F;
 };
 
 template <int BM_, int BN_, int WN_ = 2>
@@ -103,15 +106,20 @@ struct SlabRegs {
 // per-lane offset (voff[i] = row * row_bytes + chunk * 16), which the buffer
 // range check covers, so rows past the end of a resource read 0 without a
 // memory access; the K part (slab * 128 bytes, always inside the row) is the
-// scalar offset.
-template <class C, int I0, int I1>
+// scalar offset.  SwiGLU tiles (SW): voff[i >= WL / 2] carry the up rows' skip (slab_offsets<true>);
+// the x loads that share those offsets take it off again.
+template <class C, int I0, int I1, bool SW = false>
 __device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t wsrc, __amdgpu_buffer_rsrc_t xsrc,
-                                          const uint32_t (&voff)[C::WL], int slab, SlabRegs<C> &r)
+                                          const uint32_t (&voff)[C::WL], int slab, SlabRegs<C> &r,
+                                          uint32_t up_skip = 0)
 {
     const uint32_t k0 = (uint32_t)slab * C::BK * 2;
 #pragma unroll
-    for (int i = I0; i < I1; ++i)
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < C::WL ? wsrc : xsrc, voff[i < C::WL ? i : i - C::WL], k0, 0);
+    for (int i = I0; i < I1; ++i) {
+        const int vi = i < C::WL ? i : i - C::WL;
+        const uint32_t vo = (SW && i >= C::WL && vi >= C::WL / 2) ? voff[vi] - up_skip : voff[vi];
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < C::WL ? wsrc : xsrc, vo, k0, 0);
+    }
 }
 
 // Writes [I0, I1) of a slab from registers into an LDS buffer (128 B per row,
@@ -275,6 +283,44 @@ __device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, i
     __syncthreads();   // the stage arrays are free again for the next tile
 }
 
+// SwiGLU epilogue, after a barrier that follows stage_tile: staged columns 0..127 are the gate values
+// and 128..255 the up values of features f0 .. f0 + 127, both already rounded to bf16 (as a gate|up
+// GEMM stores them); h = bf16(silu(g) * u) in fp32, the same expression as the separate SwiGLU
+// kernel, so the two routes give the same bits.  Lane: row mb + lane / 16, 8 features 8 (lane % 16).
+template <class C>
+__device__ __forceinline__ void store_staged_swiglu(const GemmArgs &a, int row0, int rows_valid, int f0,
+                                                    const LdsStages &ls, int wave, int lane)
+{
+    int lo_ = lane;
+    asm volatile("" : "+v"(lo_));
+    lane = lo_;
+    constexpr int RPW = C::BM / 4;
+    static_assert(RPW % 4 == 0, "rows per wave");
+    const int c = lane & 15;
+    const bool col_ok = f0 + c * 8 < a.F;   // F % 8 == 0
+    const __amdgpu_buffer_rsrc_t hsrc = make_rsrc(a.y + (size_t)row0 * a.F + f0, (size_t)rows_valid * a.F * 2);
+#pragma unroll 2
+    for (int s0 = 0; s0 < RPW; s0 += 4) {
+        const int mb = wave * RPW + s0;   // uniform, a multiple of 4: rows mb .. mb + 3 share a stage array
+        const int m = mb + (lane >> 4);
+        typedef __attribute__((address_space(3))) const v4i_t lds_cv4i_t;
+        const lds_char_t *row = stage_at(ls, __builtin_amdgcn_readfirstlane(mb >> 6)) + (m & 63) * 512;
+        const v4i_t gv = *(lds_cv4i_t *)(row + ((c ^ (m & 31)) << 4));
+        const v4i_t uv = *(lds_cv4i_t *)(row + (((c + 16) ^ (m & 31)) << 4));
+        v4i_t o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float g0 = __uint_as_float((uint32_t)gv[q] << 16), g1 = __uint_as_float((uint32_t)gv[q] & 0xFFFF0000u);
+            const float u0 = __uint_as_float((uint32_t)uv[q] << 16), u1 = __uint_as_float((uint32_t)uv[q] & 0xFFFF0000u);
+            const float h0 = g0 / (1.0f + expf(-g0)) * u0;
+            const float h1 = g1 / (1.0f + expf(-g1)) * u1;
+            o[q] = (int32_t)pack_bf16x2(h0, h1);
+        }
+        if (col_ok) __builtin_amdgcn_raw_buffer_store_b128(o, hsrc, (uint32_t)(m * a.F + c * 8) * 2u, 0, 0);
+    }
+    __syncthreads();   // the stage arrays are free again for the next tile
+}
+
 // The tile heights in use: full row tiles are 256 rows; the last (ragged)
 // row tile of an expert takes the smallest height that covers its rows, so a
 // tail of a few rows (and every tile of a decode-sized batch) costs a fraction
@@ -314,13 +360,18 @@ struct SlabOffsets {
     uint32_t v[TileM256::WL];
 };
 
+// SwiGLU tiles (SW): tile rows 0..127 are gate rows f0.., rows 128..255 the up rows F + f0.., so the
+// W loads of the second half (i >= WL / 2: rows >= 128) skip F - 128 rows.
+template <bool SW = false>
 __device__ __forceinline__ SlabOffsets slab_offsets(const GemmArgs &a, int wave, int lane)
 {
     SlabOffsets o;
     const uint32_t row_bytes = (uint32_t)a.d * 2;
+    const uint32_t up_skip = SW ? (uint32_t)(a.F - 128) * row_bytes : 0u;
 #pragma unroll
     for (int i = 0; i < TileM256::WL; ++i)
-        o.v[i] = (uint32_t)((4 * i + wave) * 8 + (lane >> 3)) * row_bytes + (uint32_t)(lane & 7) * 16u;
+        o.v[i] = (uint32_t)((4 * i + wave) * 8 + (lane >> 3)) * row_bytes + (uint32_t)(lane & 7) * 16u +
+                 (i >= TileM256::WL / 2 ? up_skip : 0u);
     return o;
 }
 
@@ -335,7 +386,7 @@ __device__ __forceinline__ SlabOffsets slab_offsets(const GemmArgs &a, int wave,
 // j - 1 was last read before the previous barrier), load slab j + 3 into the
 // registers just freed, barrier, then read step 0 of slab j + 1 during step 3.
 // Slab s lives in register set s % 2, loaded two slabs before it is written.
-template <class C, class Sched>
+template <class C, bool SW, class Sched>
 __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &job, TileJob &next, Sched &sc,
                                               const LdsStages &ls, const SlabOffsets &so)
 {
@@ -369,10 +420,11 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
     constexpr int P1 = (NL + 2) / 3, P2 = (2 * NL + 2) / 3;   // the slab write in three parts
     constexpr int NR = C::NI + C::MI;
     SlabRegs<C> r0, r1;
-    load_part<C, 0, NL>(src.w, src.x, voff, 0, r0);
-    load_part<C, 0, NL>(src.w, src.x, voff, 1, r1);
+    const uint32_t up_skip = SW ? (uint32_t)__builtin_amdgcn_readfirstlane((a.F - 128) * a.d * 2) : 0u;
+    load_part<C, 0, NL, SW>(src.w, src.x, voff, 0, r0, up_skip);
+    load_part<C, 0, NL, SW>(src.w, src.x, voff, 1, r1, up_skip);
     store_part<C, 0, NL>(r0, wb[0], xb[0], wave, st_off);
-    load_part<C, 0, NL>(KK > 2 ? src.w : wnone, KK > 2 ? src.x : xnone, voff, 2, r0);
+    load_part<C, 0, NL, SW>(KK > 2 ? src.w : wnone, KK > 2 ? src.x : xnone, voff, 2, r0, up_skip);
     __syncthreads();
     bf16x8_t fa0[C::NI], fb0[C::MI], fa1[C::NI], fb1[C::MI];
     load_frags<C>(wb[0], xb[0], wn, wm, frag_off[0], fa0, fb0);
@@ -392,7 +444,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
         mfma_block<C>(fa0, fb0, acc);                                                                  \
         if (NEXT) {                                                                                    \
             store_part<C, 0, P1>(RN, wo_, xo_, wave, st_off);                                          \
-            load_part<C, 0, P1>(wl_, xl_, voff, (J) + 3, RN);                                      \
+            load_part<C, 0, P1, SW>(wl_, xl_, voff, (J) + 3, RN, up_skip);                                 \
             sched_step<C, NR, P1>();                                                                   \
         } else {                                                                                       \
             sched_step<C, NR, 0>();                                                                    \
@@ -401,7 +453,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
         mfma_block<C>(fa1, fb1, acc);                                                                  \
         if (NEXT) {                                                                                    \
             store_part<C, P1, P2>(RN, wo_, xo_, wave, st_off);                                         \
-            load_part<C, P1, P2>(wl_, xl_, voff, (J) + 3, RN);                                     \
+            load_part<C, P1, P2, SW>(wl_, xl_, voff, (J) + 3, RN, up_skip);                                \
             sched_step<C, NR, P2 - P1>();                                                              \
         } else {                                                                                       \
             sched_step<C, NR, 0>();                                                                    \
@@ -410,7 +462,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
         mfma_block<C>(fa0, fb0, acc);                                                                  \
         if (NEXT) {                                                                                    \
             store_part<C, P2, NL>(RN, wo_, xo_, wave, st_off);                                         \
-            load_part<C, P2, NL>(wl_, xl_, voff, (J) + 3, RN);                                     \
+            load_part<C, P2, NL, SW>(wl_, xl_, voff, (J) + 3, RN, up_skip);                                \
             sched_step<C, NR, NL - P2>();                                                              \
             __builtin_amdgcn_sched_barrier(0);                                                         \
             __syncthreads();                                                                           \
@@ -450,7 +502,8 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
     stage_tile<C>(acc, ls, wave, lane);
     next = sc.claim();
     __syncthreads();   // the staged tile is complete
-    store_staged_tile<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
+    if constexpr (SW) store_staged_swiglu<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
+    else store_staged_tile<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
 }
 
 // A Sched made of three callables.
@@ -468,18 +521,18 @@ struct LambdaSched {
 // this workgroup (rows_valid <= 0: none left); wait(job) -> false if the
 // workgroup must stop (a failed wait for the job's rows); done() after each
 // tile.
-template <class Sched>
+template <bool SW = false, class Sched>
 __device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const LdsStages &ls)
 {
-    const SlabOffsets so = slab_offsets(a, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), threadIdx.x % kWave);
+    const SlabOffsets so = slab_offsets<SW>(a, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), threadIdx.x % kWave);
     TileJob job = sc.claim();
     while (job.rows_valid > 0) {
         if (!sc.wait(job)) return;
         TileJob next;
-        if (job.rows_valid > 128) gemm_tile_big<TileM256>(a, job, next, sc, ls, so);
-        else if (job.rows_valid > 64) gemm_tile_big<TileM128>(a, job, next, sc, ls, so);
-        else if (job.rows_valid > 32) gemm_tile_big<TileM64>(a, job, next, sc, ls, so);
-        else gemm_tile_big<TileM32>(a, job, next, sc, ls, so);
+        if (job.rows_valid > 128) gemm_tile_big<TileM256, SW>(a, job, next, sc, ls, so);
+        else if (job.rows_valid > 64) gemm_tile_big<TileM128, SW>(a, job, next, sc, ls, so);
+        else if (job.rows_valid > 32) gemm_tile_big<TileM64, SW>(a, job, next, sc, ls, so);
+        else gemm_tile_big<TileM32, SW>(a, job, next, sc, ls, so);
         sc.done();
         job = next;
     }
@@ -487,7 +540,8 @@ __device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const Lds
 
 // Task q -> its tile; tasks are ordered expert-major, then column block, then
 // row tile, so consecutive tasks share one W tile.  q >= n_tasks: no task.
-template <class C>
+// A SwiGLU column block is 128 features (256 W rows: their gate and up rows).
+template <class C, bool SW = false>
 __device__ __forceinline__ TileJob job_of_task(const GemmArgs &a, const int32_t *tile_off, const int32_t *offsets,
                                                int NB, int n_tasks, int q)
 {
@@ -505,7 +559,7 @@ __device__ __forceinline__ TileJob job_of_task(const GemmArgs &a, const int32_t 
     t.e = e;
     t.row0 = offsets[e] + mt * C::BM;
     t.rows_valid = min(C::BM, offsets[e + 1] - offsets[e] - mt * C::BM);
-    t.n0 = nb * C::BN;
+    t.n0 = nb * (SW ? C::BN / 2 : C::BN);
     return t;
 }
 
@@ -513,7 +567,7 @@ __device__ __forceinline__ TileJob job_of_task(const GemmArgs &a, const int32_t 
 // runs task round*G + slot(w); slot() gives the workgroups of one XCD
 // (w % 8 == x, dispatched round-robin over the 8 XCDs) a contiguous run of
 // tasks, so tasks sharing a W tile share that XCD's L2.
-template <class C>
+template <class C, bool SW = false>
 __device__ __forceinline__ void gemm_worker(const GemmArgs &a, int w, int G, const LdsStages &ls)
 {
     struct Sched {
@@ -521,16 +575,16 @@ __device__ __forceinline__ void gemm_worker(const GemmArgs &a, int w, int G, con
         int NB, n_tasks, q, G;
         __device__ TileJob claim()
         {
-            const TileJob t = job_of_task<C>(a, a.tile_off, a.offsets, NB, n_tasks, q);
+            const TileJob t = job_of_task<C, SW>(a, a.tile_off, a.offsets, NB, n_tasks, q);
             q += G;
             return t;
         }
         __device__ bool wait(const TileJob &) { return true; }
         __device__ void done() {}
     };
-    const int NB = (a.N + C::BN - 1) / C::BN;
+    const int NB = SW ? (a.F + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
     Sched sc{a, NB, (int)a.hdr->n_tiles * NB, (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w, G};
-    gemm_run(a, sc, ls);
+    gemm_run<SW>(a, sc, ls);
 }
 
 }  // namespace mk

@@ -65,13 +65,13 @@ __global__ __launch_bounds__(256) void k_move(SrcRows src, const int32_t *row_to
     for (int r = wid; r < R; r += waves) move_row(src, row_token, x_perm, d, r, threadIdx.x % kWave);
 }
 
-template <class C>
+template <class C, bool SW = false>
 __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
     LdsStages ls;
     for (int k = 0; k < 4; ++k) ls.p[k] = (lds_char_t *)(stg + k * C::STAGE);
-    gemm_worker<C>(a, blockIdx.x, gridDim.x, ls);
+    gemm_worker<C, SW>(a, blockIdx.x, gridDim.x, ls);
 }
 
 template <class C>
@@ -253,6 +253,12 @@ hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t 
         return hipGetLastError();
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_swiglu(const GemmArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_gemm<Tile256, true>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 int gemm_max_grid(int bm, int bn)

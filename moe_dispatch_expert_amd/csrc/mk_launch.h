@@ -36,6 +36,8 @@ hipError_t launch_move(const SrcRows &src, const int32_t *row_token, uint16_t *x
                        hipStream_t s);
 // Grouped GEMM over the tile table; bm/bn select the tile shape.
 hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s);
+// The grouped gate|up GEMM with the SwiGLU epilogue (a.F features per expert, a.N == 2 a.F).
+hipError_t launch_gemm_swiglu(const GemmArgs &a, int grid, hipStream_t s);
 // Largest co-resident grid of the GEMM kernel for this tile shape.
 int gemm_max_grid(int bm, int bn);
 // The persistent fused kernel: one workgroup per resident slot of the device (its grid barriers need them all

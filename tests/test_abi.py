@@ -99,7 +99,7 @@ def test_workspace_bytes_and_tuning_without_gpu():
 
 
 def test_next_steps_argument_errors_are_synchronous():
-    """mk_combine, mk_swiglu and mk_grouped_gemm refuse bad arguments before touching the device, and
+    """mk_combine, mk_swiglu, mk_grouped_gemm and mk_grouped_gemm_swiglu refuse bad arguments before touching the device, and
     their empty cases are no-ops."""
     lib = mk.load()
     fake = ctypes.c_void_p(0x1000)            # aligned, never dereferenced: every call below returns early
@@ -122,3 +122,11 @@ def test_next_steps_argument_errors_are_synchronous():
     need = lib.mk_grouped_gemm_workspace_bytes(4)
     assert need > 0 and lib.mk_grouped_gemm_workspace_bytes(0) == 0
     assert lib.mk_grouped_gemm(fake, fake, 4, fake, 128, 64, fake, fake, need - 1, None) == mk.MK_EWORKSPACE
+    # gate|up GEMM with the SwiGLU epilogue: the same checks, F % 8, and 32-bit W row offsets
+    sw = lib.mk_grouped_gemm_swiglu
+    assert sw(fake, fake, 0, fake, 128, 64, fake, fake, need, None) == mk.MK_EINVAL
+    assert sw(fake, fake, 4, fake, 64, 64, fake, fake, need, None) == mk.MK_EUNSUPPORTED
+    assert sw(fake, fake, 4, fake, 128, 60, fake, fake, need, None) == mk.MK_EINVAL
+    assert sw(fake, fake, 4, fake, 128, 64, fake, fake, need - 1, None) == mk.MK_EWORKSPACE
+    assert sw(fake, fake, 4, fake, 8192, 131072, fake, fake, need, None) == mk.MK_EUNSUPPORTED
+    assert sw(fake, fake, 4, fake, 128, 64, odd, fake, need, None) == mk.MK_EINVAL

@@ -73,3 +73,43 @@ def test_grouped_gemm_empty_layout_and_errors():
         mk.mk_grouped_gemm(torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda"),
                            torch.zeros(4, dtype=torch.int32, device="cuda"),
                            torch.zeros(3, 16, 64, dtype=torch.bfloat16, device="cuda"))
+
+
+def _silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+@pytest.mark.parametrize("counts,K,F", [
+    ([300, 0, 37, 256, 129], 256, 264),      # empty expert, every tile height, a 8-feature last block
+    ([1, 2, 513], 384, 136),                  # one-row experts; gate and up blocks overlap (F < 256)
+    ([40, 3], 128, 8),                        # F < 128: the up rows sit before the tile's second half
+    ([64] * 8, 128, 256),
+])
+def test_grouped_gemm_swiglu(counts, K, F):
+    """The gate|up GEMM with the SwiGLU epilogue gives the bits of mk_grouped_gemm (N = 2F) followed by
+    mk_swiglu, and matches the oracle chain (GEMM, bf16 rounding, SwiGLU) within the bar derived from
+    one bf16 step of g or u: |dh| <= 2^-7 (|g silu'(g) u| + |silu(g) u|) + 2^-8 |h| + 1e-6."""
+    offsets = _layout(counts)
+    R, E_local = int(offsets[-1]), len(counts)
+    a = _bf16((R + 3, K), 51 + K)
+    w = _bf16((E_local, 2 * F, K), 61 + F, scale=2.0 * K ** -0.5)
+    dev_off = torch.from_numpy(offsets).cuda()
+    h = torch.full((R + 3, F), 7.0, dtype=torch.bfloat16, device="cuda")
+    mk.mk_grouped_gemm_swiglu(a.cuda(), dev_off, w.cuda(), out=h)
+    gu = mk.mk_grouped_gemm(a.cuda(), dev_off, w.cuda())
+    h2 = mk.mk_swiglu(gu[:R].contiguous())
+    torch.cuda.synchronize()
+    assert (h[R:] == 7.0).all(), "rows past R were written"
+    ne = (h[:R] != h2).cpu().numpy()
+    assert not ne.any(), (f"fused epilogue differs from GEMM + SwiGLU at {int(ne.sum())} of {ne.size}; "
+                          f"first at {tuple(np.argwhere(ne)[0])}")
+    ref_gu = torch.from_numpy(oracle.grouped_rows(a[:R], w, offsets, np.arange(R))).to(torch.bfloat16)
+    ref = oracle.swiglu(ref_gu)
+    g = ref_gu[:, :F].double().numpy()
+    u = ref_gu[:, F:].double().numpy()
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    tol = 2.0 ** -7 * (np.abs(g * dsilu * u) + np.abs(_silu(g) * u)) + 2.0 ** -8 * np.abs(ref) + 1e-6
+    got = h[:R].float().cpu().numpy()
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
