@@ -374,7 +374,8 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    gemm_ms = float(np.mean([_elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in range(args.steps)]))
+    launch_all = [_elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in range(args.steps)]
+    gemm_ms = float(np.mean(launch_all))
     if scratch is not None:   # the evicting writes sit between the steps: time the launches only
         ms_step = gemm_ms
         del scratch
@@ -402,6 +403,7 @@ def main():
     roof.update({"traffic": traffic,
                  "kernel": "grouped expert GEMM (k_gemm)" if args.staged else "fused dispatch+GEMM (k_fused)",
                  "launch_ms": round(gemm_ms, 4),
+                 "launch_ms_p10_p50_p90": [round(float(v), 4) for v in np.percentile(launch_all, [10, 50, 90])],
                  "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes})
     rec = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
