@@ -63,12 +63,18 @@ def test_grouped_gemm_matches_oracle(counts, K, N):
 
 
 def test_grouped_gemm_empty_layout_and_errors():
+    """An empty layout (all offsets 0) launches no task: the outputs stay as they were; K % 128 != 0 is refused."""
     w = _bf16((3, 16, 128), 1)
     out = torch.full((4, 16), 7.0, dtype=torch.bfloat16, device="cuda")
     mk.mk_grouped_gemm(torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda"),
                        torch.zeros(4, dtype=torch.int32, device="cuda"), w.cuda(), out=out)
     torch.cuda.synchronize()
     assert (out == 7.0).all()
+    h = torch.full((4, 8), 7.0, dtype=torch.bfloat16, device="cuda")   # the SwiGLU variant: F = 8
+    mk.mk_grouped_gemm_swiglu(torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros(4, dtype=torch.int32, device="cuda"), w.cuda(), out=h)
+    torch.cuda.synchronize()
+    assert (h == 7.0).all()
     with pytest.raises(mk.MkError):   # K % 128 != 0: unsupported, nothing launched
         mk.mk_grouped_gemm(torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda"),
                            torch.zeros(4, dtype=torch.int32, device="cuda"),
