@@ -206,8 +206,10 @@ size_t mk_grouped_gemm_workspace_bytes(int32_t E_local);
 mk_status mk_grouped_gemm(const void *a, const int32_t *expert_offsets, int32_t E_local, const void *w, int32_t K,
                           int32_t N, void *y, void *workspace, size_t workspace_bytes, void *stream);
 
-/* The expert FFN's gate|up GEMM with the SwiGLU of mk_swiglu in its epilogue
- * (the same reading of the pages as mk_swiglu): for every row r of expert e,
+/* The expert FFN's gate|up GEMM with the SwiGLU of mk_swiglu in its epilogue.
+ * The pages name the MoE Dispatch+GEMM kernel (zubnet.ai, paragraph 2), whose
+ * experts in MoE models are gated FFNs; the gated form below is this library's
+ * reading, the same as for mk_swiglu.  For every row r of expert e,
  *   g = bf16_rne( sum_i a[r, i] * w_gate_up[e, f, i] ),  u = bf16_rne( sum_i a[r, i] * w_gate_up[e, F + f, i] ),
  *   h[r, f] = bf16_rne( silu(g) * u ),  fp32 accumulation and activation,
  * i.e. bit for bit mk_grouped_gemm (N = 2F) followed by mk_swiglu, without the
