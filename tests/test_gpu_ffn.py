@@ -119,3 +119,34 @@ def test_grouped_gemm_swiglu(counts, K, F):
     got = h[:R].float().cpu().numpy()
     bad = np.abs(got - ref) > tol
     assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
+
+
+def test_grouped_gemm_swiglu_mixtral_size():
+    """Mixtral's expert FFN shape (8 experts of 1024 rows plus a ragged 37-row tail on one, K = 4096, F = 7168):
+    the SwiGLU-epilogue GEMM equals GEMM + SwiGLU bit for bit on every output, and 12 sampled rows (every
+    expert's first and last, and the tail) match the oracle chain within the derived bar."""
+    counts = [1024] * 7 + [1061]
+    K, F = 4096, 7168
+    offsets = _layout(counts)
+    R, E_local = int(offsets[-1]), len(counts)
+    a = _bf16((R, K), 71)
+    w = _bf16((E_local, 2 * F, K), 81, scale=2.0 * K ** -0.5)
+    dev_off = torch.from_numpy(offsets).cuda()
+    a_d, w_d = a.cuda(), w.cuda()
+    h = mk.mk_grouped_gemm_swiglu(a_d, dev_off, w_d)
+    h2 = mk.mk_swiglu(mk.mk_grouped_gemm(a_d, dev_off, w_d))
+    torch.cuda.synchronize()
+    ne = int((h != h2).sum().item())
+    assert ne == 0, f"fused epilogue differs from GEMM + SwiGLU at {ne} outputs"
+    rows = np.array(sorted({int(offsets[e]) for e in range(E_local)} | {int(offsets[e + 1]) - 1 for e in (0, 3)}
+                           | {R - 1, R - 20}), dtype=np.int64)
+    ref_gu = torch.from_numpy(oracle.grouped_rows(a, w, offsets, rows.astype(np.int32))).to(torch.bfloat16)
+    ref = oracle.swiglu(ref_gu)
+    g = ref_gu[:, :F].double().numpy()
+    u = ref_gu[:, F:].double().numpy()
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    tol = 2.0 ** -7 * (np.abs(g * dsilu * u) + np.abs(_silu(g) * u)) + 2.0 ** -8 * np.abs(ref) + 1e-6
+    got = h[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
