@@ -150,3 +150,24 @@ def test_grouped_gemm_swiglu_mixtral_size():
     got = h[torch.from_numpy(rows).cuda()].float().cpu().numpy()
     bad = np.abs(got - ref) > tol
     assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
+
+
+def test_down_projection_mixtral_size():
+    """The down-projection at Mixtral's expert FFN shape (K = F = 7168, N = d = 4096, 8 experts, a ragged tail):
+    12 sampled rows against the oracle within the expert-output bar; rows past R untouched."""
+    counts = [1024] * 7 + [1061]
+    K, N = 7168, 4096
+    offsets = _layout(counts)
+    R, E_local = int(offsets[-1]), len(counts)
+    a = _bf16((R, K), 91)
+    w = _bf16((E_local, N, K), 101, scale=K ** -0.5)
+    out = torch.full((R + 4, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    mk.mk_grouped_gemm(a.cuda(), torch.from_numpy(offsets).cuda(), w.cuda(), out=out)
+    torch.cuda.synchronize()
+    assert (out[R:] == 7.0).all(), "rows past R were written"
+    rows = np.array(sorted({int(offsets[e]) for e in range(E_local)} | {int(offsets[e + 1]) - 1 for e in (0, 3)}
+                           | {R - 1, R - 20}), dtype=np.int64)
+    ref = oracle.grouped_rows(a, w, offsets, rows.astype(np.int32))
+    got = out[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+    bad = np.abs(got - ref) > np.maximum(Y_REL * np.abs(ref), Y_FLOOR)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size}; first at {tuple(np.argwhere(bad)[0])}"
