@@ -147,6 +147,40 @@ def copy_calibration(mib: int, reps: int = 3):
     print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
 
 
+def library_gemm(wl, steps: int, warmup: int):
+    """The library GEMM (torch linear, hipBLASLt) on the workload's expert shape, bf16 random data, R = T * k
+    rows (what a uniform routing gives), two ways: one dense GEMM y[R, N] = x[R, d] . W[N, d]^T with a single
+    W (reused by every row), and one GEMM per local expert on its R / E_local rows with its own W (the
+    grouped problem: every expert's W is streamed once).  Each timed K times between two events."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    R, N, K, E = wl.T * min(wl.k, wl.E_local), wl.N, wl.d, wl.E_local
+    x = torch.randn(R, K, device="cuda", generator=g).to(torch.bfloat16)
+    ws = [(torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16) for _ in range(E)]
+    xs = list(x.split(R // E))
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    flops = 2.0 * R * N * K
+    res = {"library_gemm": "torch.nn.functional.linear (hipBLASLt), bf16", "M": R, "N": N, "K": K}
+    for name, fn in (("dense_one_W", lambda: torch.nn.functional.linear(x, ws[0])),
+                     ("per_expert", lambda: [torch.nn.functional.linear(xe, we) for xe, we in zip(xs, ws)])):
+        ms = timed(fn)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps(res), flush=True)
+
+
 def trace_summary(tr: dict) -> dict:
     """Phase boundaries of the fused kernel (max over workgroups, microseconds from the first start)."""
     live = tr["start"] > 0
@@ -304,6 +338,8 @@ def main():
     ap.add_argument("--ffn", action="store_true",
                     help="also time the expert FFN after the step (its y_perm read as [gate | up], F = N / 2): "
                          "mk_swiglu and the down-projection mk_grouped_gemm (reported apart, not in value)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the dense library GEMM (torch linear) of the workload's expert shape and exit")
     ap.add_argument("--combine", action="store_true",
                     help="also time the next step, mk_combine, on the step's outputs (reported apart, not in value)")
     args = ap.parse_args()
@@ -323,6 +359,9 @@ def main():
     import workloads as W
 
     wl = W.WORKLOADS[args.workload]
+    if args.library_gemm:
+        library_gemm(wl, args.steps, args.warmup)
+        return
     inp = W.make_inputs(wl, args.seed)
     dev = torch.device("cuda:0")
     x = inp["x"]
@@ -335,19 +374,18 @@ def main():
     if wl.route_outside:   # the sources route their own tokens before the payload arrives (untimed)
         parts = [mk.mk_route_topk(xs[s], wr, wl.k)[0] for s in range(wl.S)]
         ids_in = torch.cat(parts).contiguous()
+    base_tune = {}
+    if args.staged:
+        base_tune["n_mover_wg"] = mk.MK_MOVERS_STAGED
+    elif args.movers:
+        base_tune["n_mover_wg"] = args.movers
     ws = torch.zeros(mk.mk_dispatch_gemm_workspace_bytes(wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N,
-                                                         wl.S), dtype=torch.uint8, device=dev)
+                                                         wl.S, tune=base_tune), dtype=torch.uint8, device=dev)
     out = mk.mk_dispatch_gemm(xs, we, wl.k, w_router=wr, bias=bias, topk_ids_in=ids_in, E=wl.E,
-                              e_begin=wl.e_begin, workspace=ws)
+                              e_begin=wl.e_begin, workspace=ws, tune=base_tune)
     bufs = {k: out[k] for k in ("y_perm", "slot_of", "expert_offsets", "topk_ids", "topk_w", "row_token")}
     hip = _hip()
     evs = _events(hip, 2 * args.steps)
-
-    base_tune = {}
-    if args.staged:
-        base_tune["n_mover_wg"] = -1
-    elif args.movers:
-        base_tune["n_mover_wg"] = args.movers
 
     def step(i=None):
         tune = dict(base_tune)

@@ -73,15 +73,39 @@ typedef struct {
     const void *const *sim_payload;
 } mk_sources;
 
-/* Role split and tile sizes.  All zeros = the per-shape table (mk_select_tuning).
- * n_mover_wg workgroups start in the dispatch (mover) role and join the GEMM
- * role when the dispatch work is done; n_compute_wg workgroups start in the
- * GEMM role.  bm/bn/bk: rows, columns and depth of one GEMM tile.
- * ev_gemm_begin / ev_gemm_end: NULL, or hipEvent_t handles the library records
- * on `stream` immediately before and after the launch that runs the expert
- * GEMM, so a caller can time that kernel alone. */
+/* Role split, grid and tile sizes ("UC Berkeley presenta mKernel ..."
+ * (edge.aivizor.me), paragraph 2, and "mKernel : une bibliotheque de noyaux
+ * fusionnes ..." (lefilia.fr), paragraph 2: the number of thread blocks per
+ * role is set per tensor shape).  All zeros = the per-shape table
+ * (mk_select_tuning); a zero field means "the table's value".
+ *   n_mover_wg    > 0: that many workgroups start in the dispatch (mover) role:
+ *                 they copy token rows into an expert-contiguous buffer tile by
+ *                 tile (waiting for the source chunks' ready flags when rows
+ *                 arrive from peers) and then join the GEMM role;
+ *                 MK_MOVERS_NONE: no mover role: the GEMM reads each tile's
+ *                 token rows in place through the slot -> token map (one
+ *                 resident source only, T * d * 2 < 4 GiB; else
+ *                 MK_EUNSUPPORTED);
+ *                 MK_MOVERS_STAGED: one kernel launch per step instead of the
+ *                 persistent kernel (no overlap; for comparison).
+ *   n_compute_wg  > 0: workgroups that start in the GEMM role; the grid is then
+ *                 n_compute_wg (+ n_mover_wg), and must fit the device at once
+ *                 (else MK_EUNSUPPORTED).  0: every workgroup the device holds.
+ *   bm, bn, bk    0 or the one tile this build has: 256 token rows, 256 output
+ *                 columns, K slabs of 64 (the last row tile of each expert
+ *                 shrinks to 128, 64 or 32 rows by itself); else MK_EUNSUPPORTED.
+ *   cooperative   1: launch the persistent kernel cooperatively, so the runtime
+ *                 guarantees that all its workgroups are resident together
+ *                 (for callers that share the device with other streams); about
+ *                 15 us more per call.  0: an ordinary launch (see
+ *                 mk_dispatch_gemm).
+ *   ev_gemm_begin / ev_gemm_end: NULL, or hipEvent_t handles the library
+ *                 records on `stream` immediately before and after the launch
+ *                 that runs the expert GEMM, so a caller can time that kernel. */
+#define MK_MOVERS_STAGED (-1)
+#define MK_MOVERS_NONE (-2)
 typedef struct {
-    int32_t n_mover_wg, n_compute_wg, bm, bn, bk;
+    int32_t n_mover_wg, n_compute_wg, bm, bn, bk, cooperative;
     void *ev_gemm_begin;
     void *ev_gemm_end;
 } mk_tuning;
@@ -105,8 +129,11 @@ mk_status mk_route_topk(const void *x, const float *w_router, const float *bias,
                         int32_t *topk_ids, float *topk_w,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace mk_dispatch_gemm needs for this shape (0 on bad input). */
-size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src);
+/* Bytes of workspace mk_dispatch_gemm needs for this shape, sources and tuning
+ * (tune NULL = the per-shape table); 0 on bad input.  Paths that copy rows (a
+ * mover role or the staged launches) need room for the expert-contiguous row
+ * buffer, [T * min(k, E_local) + 256, d] bf16; the in-place path does not. */
+size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src, const mk_tuning *tune);
 
 /* Fused dispatch + expert GEMM, one persistent launch.
  * Steps (routing per mk_route_topk unless topk_ids_in is given):
@@ -127,12 +154,17 @@ size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src
  *   expert_offsets     [E_local + 1] int32
  *   topk_ids_out       NULL or [T, k] int32     topk_w_out NULL or [T, k] fp32
  *   row_token          NULL or [T * min(k, E_local)] int32 (first R written)
- *   workspace          mk_dispatch_gemm_workspace_bytes bytes, ZERO-FILLED ONCE before
- *                      its first use; it carries state between calls (barrier and
- *                      flag epochs), so two calls in flight must not share one.
+ *   workspace          mk_dispatch_gemm_workspace_bytes(s, src, tune) bytes, ZERO-FILLED
+ *                      ONCE before its first use; it carries state between calls (the
+ *                      call epoch from which grid-barrier targets derive), so two calls
+ *                      in flight must not share one.
  *   tune               NULL or all zeros = per-shape table
  * Device-side failures (a wait that timed out, bad topk_ids_in) are reported by
  * mk_poll_error after the stream is synchronised; outputs are then undefined.
+ * The workspace stays failed until mk_poll_error has read and cleared the error:
+ * every call through it before that stops early (outputs undefined).  After
+ * that it needs no re-zeroing: a failed call still ends its epoch, so barrier
+ * state it left behind cannot satisfy a later call's barriers.
  * The fused kernel runs one workgroup per resident slot of the device and
  * synchronises them with grid barriers: they must all become resident, so
  * work of other streams on the device only delays it, and a wait longer than
@@ -154,7 +186,7 @@ mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *
  * workspace: *offset bytes from its start, *n_wg records of *words uint64
  * each (record w = workgroup w).  Words, written by every fused call:
  *   0 start, 1 router logits done, 2 barrier A passed, 3 histogram done,
- *   4 barrier B passed, 5 scan done, 6 unused (0), 7 mover role
+ *   4 barrier B passed, 5 scan done, 6 barrier C passed (in-place path), 7 mover role
  *   done, 8 first GEMM task started, 9 workgroup done (wall-clock ticks,
  *   *ticks_per_us per microsecond); 10 GEMM tasks run, 11 ticks spent
  *   waiting for tiles, 12 hardware XCD id, 13 mover units copied, 14 ticks

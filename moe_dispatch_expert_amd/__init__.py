@@ -39,9 +39,17 @@ class MkSources(ctypes.Structure):
 
 class MkTuning(ctypes.Structure):
     _fields_ = [("n_mover_wg", _c_i32), ("n_compute_wg", _c_i32), ("bm", _c_i32), ("bn", _c_i32),
-                ("bk", _c_i32), ("ev_gemm_begin", _vp), ("ev_gemm_end", _vp)]
+                ("bk", _c_i32), ("cooperative", _c_i32), ("ev_gemm_begin", _vp), ("ev_gemm_end", _vp)]
 
-TUNING_INTS = ("n_mover_wg", "n_compute_wg", "bm", "bn", "bk")
+TUNING_INTS = ("n_mover_wg", "n_compute_wg", "bm", "bn", "bk", "cooperative")
+MK_MOVERS_STAGED, MK_MOVERS_NONE = -1, -2   # n_mover_wg: one launch per step; no mover role (rows read in place)
+
+
+def _tuning(tune: Optional[dict]):
+    if not tune:
+        return None
+    return MkTuning(*(int(tune.get(f, 0)) for f in TUNING_INTS), tune.get("ev_gemm_begin"),
+                    tune.get("ev_gemm_end"))
 
 
 class MkError(RuntimeError):
@@ -69,7 +77,7 @@ def load() -> ctypes.CDLL:
     lib.mk_route_topk.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
     lib.mk_route_topk.restype = _c_i32
-    lib.mk_dispatch_gemm_workspace_bytes.argtypes = [P(MkShape), P(MkSources)]
+    lib.mk_dispatch_gemm_workspace_bytes.argtypes = [P(MkShape), P(MkSources), P(MkTuning)]
     lib.mk_dispatch_gemm_workspace_bytes.restype = ctypes.c_size_t
     lib.mk_dispatch_gemm.argtypes = [P(MkShape), P(MkSources), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, ctypes.c_size_t, P(MkTuning), _vp]
@@ -163,15 +171,24 @@ def mk_route_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: Optiona
     return topk_ids, topk_w
 
 
-def mk_dispatch_gemm_workspace_bytes(T, d, E, k, e_begin, E_local, N, S=1) -> int:
+def mk_dispatch_gemm_workspace_bytes(T, d, E, k, e_begin, E_local, N, S=1, chunk_rows=0,
+                                     tune: Optional[dict] = None) -> int:
+    """Workspace bytes for this shape, number of sources, arrival chunking and tuning (None = the table)."""
     shape = _shape(T, d, E, k, e_begin, E_local, N)
-    src = MkSources(S, T // max(S, 1), None, 0, None, 0, None, None)
-    return int(load().mk_dispatch_gemm_workspace_bytes(ctypes.byref(shape), ctypes.byref(src)))
+    ptrs = (_vp * max(S, 1))(*([0x1000] * max(S, 1)))   # placeholders: only the count is inspected
+    src = MkSources(S, T // max(S, 1), ctypes.cast(ptrs, ctypes.POINTER(_vp)), int(chunk_rows),
+                    ctypes.c_void_p(0x1000) if chunk_rows else None, 0, None, None)
+    tu = _tuning(tune)
+    return int(load().mk_dispatch_gemm_workspace_bytes(ctypes.byref(shape), ctypes.byref(src),
+                                                       None if tu is None else ctypes.byref(tu)))
 
 
-def mk_select_tuning(T, d, E, k, e_begin, E_local, N) -> dict:
+def mk_select_tuning(T, d, E, k, e_begin, E_local, N, S=1, chunk_rows=0) -> dict:
+    """The per-shape table's tuning for this shape, number of sources and arrival chunking."""
     shape = _shape(T, d, E, k, e_begin, E_local, N)
-    src = MkSources(1, T, None, 0, None, 0, None, None)
+    ptrs = (_vp * max(S, 1))(*([0x1000] * max(S, 1)))
+    src = MkSources(S, T // max(S, 1), ctypes.cast(ptrs, ctypes.POINTER(_vp)), int(chunk_rows),
+                    ctypes.c_void_p(0x1000) if chunk_rows else None, 0, None, None)
     out = MkTuning()
     _check(load().mk_select_tuning(ctypes.byref(shape), ctypes.byref(src), ctypes.byref(out)), "mk_select_tuning")
     return {f: getattr(out, f) for f in TUNING_INTS}
@@ -241,15 +258,13 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
     o.setdefault("row_token", torch.empty(max(r_cap, 1), dtype=torch.int32, device=dev))
     shape = _shape(T, d, E, k, e_begin, E_local, N)
     srcs = _Sources(xs, chunk_rows, chunk_ready, epoch, sim_delay_us, sim_payload)
+    tu = _tuning(tune)
     if workspace is None:
-        nbytes = int(lib.mk_dispatch_gemm_workspace_bytes(ctypes.byref(shape), ctypes.byref(srcs.c)))
+        nbytes = int(lib.mk_dispatch_gemm_workspace_bytes(ctypes.byref(shape), ctypes.byref(srcs.c),
+                                                          None if tu is None else ctypes.byref(tu)))
         if nbytes == 0:
             _check(MK_EINVAL, "mk_dispatch_gemm_workspace_bytes")
         workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-    tu = None
-    if tune:
-        tu = MkTuning(*(int(tune.get(f, 0)) for f in TUNING_INTS), tune.get("ev_gemm_begin"),
-                      tune.get("ev_gemm_end"))
     st = lib.mk_dispatch_gemm(ctypes.byref(shape), ctypes.byref(srcs.c), _ptr(w_router), _ptr(bias),
                               _ptr(topk_ids_in), _ptr(w_experts), _ptr(o["y_perm"]), _ptr(o["slot_of"]),
                               _ptr(o["expert_offsets"]), _ptr(o["topk_ids"]), _ptr(o["topk_w"]),

@@ -86,105 +86,73 @@ int ticks_per_us()
     return v;
 }
 
-// The per-shape table.  Every co-resident workgroup starts as a mover when
-// all source rows are resident (the copy then takes a few microseconds and
-// every workgroup turns to the GEMM as soon as its share is moved); when rows
-// arrive from peers, 64 workgroups wait for arrivals and move while the rest
-// compute on the tiles that are complete.
+// The per-shape table.  One resident source (S = 1, no arrival flags): no mover role, the GEMM gathers
+// token rows straight from x through row_token (n_mover_wg = 0 in the table's answer); the x
+// matrix must fit one buffer resource (< 4 GiB).  Several resident sources: every co-resident
+// workgroup starts as a mover (the copy takes a few microseconds, then all compute).  Rows arriving
+// from peers: 64 workgroups wait for arrivals and move while the rest compute on the tiles that are
+// complete.
+bool gather_possible(const mk_shape *s, const mk_sources *src)
+{
+    return src && src->S == 1 && src->chunk_rows == 0 && (size_t)s->T * s->d * 2 <= 0xFFFFFFF0ull;
+}
+
 mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
 {
     mk_tuning t{};
     t.bm = 256;
     t.bn = 256;
-    t.bk = BigTile<256, 256>::BK;
-    t.n_mover_wg = (src && src->chunk_rows > 0) ? 64 : 256;
+    t.bk = Tiles<4>::M256::BK;
+    if (gather_possible(s, src)) t.n_mover_wg = MK_MOVERS_NONE;
+    else t.n_mover_wg = (src && src->chunk_rows > 0) ? 64 : 256;
     t.n_compute_wg = 0;   // 0: every co-resident workgroup
-    (void)s;
     return t;
 }
 
-}  // namespace
+enum class Path { kGather, kMove, kStaged };
 
-extern "C" {
+// How one call runs: the resolved tuning, the path, and the workspace layout it needs.
+struct Plan {
+    mk_tuning tu;
+    Path path;
+    WsLayout L;
+};
 
-const char *mk_status_str(mk_status st)
+mk_status plan_call(const mk_shape *s, const mk_sources *src, const mk_tuning *tune, Plan &p)
 {
-    switch (st) {
-    case MK_OK: return "ok";
-    case MK_EINVAL: return "invalid argument";
-    case MK_EUNSUPPORTED: return "unsupported shape or option";
-    case MK_EWORKSPACE: return "workspace too small";
-    case MK_EHIP: return "HIP runtime error";
-    case MK_ETIMEOUT: return "device wait timed out";
-    default: return "unknown status";
+    p.tu = table_tuning(s, src);
+    if (tune) {
+        if ((tune->bm && tune->bm != 256) || (tune->bn && tune->bn != 256) ||
+            (tune->bk && tune->bk != Tiles<4>::M256::BK))
+            return MK_EUNSUPPORTED;
+        if (tune->n_mover_wg < MK_MOVERS_NONE || tune->n_compute_wg < 0 || tune->cooperative < 0 ||
+            tune->cooperative > 1)
+            return MK_EINVAL;
+        if (tune->n_mover_wg) p.tu.n_mover_wg = tune->n_mover_wg;
+        p.tu.n_compute_wg = tune->n_compute_wg;
+        p.tu.cooperative = tune->cooperative;
     }
-}
-
-size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E)
-{
-    if (T < 0 || E < 1) return 0;
-    return align256((size_t)kRouterSegments * T * E * 4) + 256;
-}
-
-mk_status mk_route_topk(const void *x, const float *w_router, const float *bias, int32_t T, int32_t d, int32_t E,
-                        int32_t k, int32_t *topk_ids, float *topk_w, void *workspace, size_t workspace_bytes,
-                        void *stream)
-{
-    if (T < 0 || d <= 0 || E < 1 || k < 1 || k > E) return MK_EINVAL;
-    if (d % 8 != 0) return MK_EINVAL;
-    if (d % 128 != 0 || E > 1024 || k > kMaxK) return MK_EUNSUPPORTED;
-    if (T == 0) return MK_OK;
-    if (!x || !w_router || !topk_ids || !workspace) return MK_EINVAL;
-    if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(workspace) ||
-        (bias && !aligned16(bias)) || (topk_w && !aligned16(topk_w)))
-        return MK_EINVAL;
-    if (workspace_bytes < mk_route_topk_workspace_bytes(T, E)) return MK_EWORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
-    RouterArgs ra{};
-    ra.src.p[0] = (const uint16_t *)x;
-    ra.src.S = 1;
-    ra.src.rows_per_src = T;
-    ra.wr = w_router;
-    ra.part = (float *)workspace;
-    ra.T = T;
-    ra.d = d;
-    ra.E = E;
-    if (launch_router(ra, st) != hipSuccess) return MK_EHIP;
-    TopkArgs ta{};
-    ta.part = (const float *)workspace;
-    ta.bias = bias;
-    ta.ids = topk_ids;
-    ta.ids_user = nullptr;
-    ta.w_user = topk_w;
-    ta.T = T;
-    ta.E = E;
-    ta.k = k;
-    CountArgs ca{};
-    if (launch_topk(ta, ca, false, st) != hipSuccess) return MK_EHIP;
+    // Phase 3 of the fused kernel keeps nblk * E_local block counts in LDS.
+    const WsLayout L0 = ws_layout(s->T, s->d, s->E, s->k, s->E_local, false);
+    const bool fits_fused = (long)L0.nblk * s->E_local <= kMaxScanEntries;
+    if (p.tu.n_mover_wg == MK_MOVERS_STAGED || s->T == 0 || !fits_fused) {
+        if (src->chunk_rows > 0) return MK_EUNSUPPORTED;   // arrival flags need the fused kernel
+        p.path = Path::kStaged;
+    } else if (p.tu.n_mover_wg == MK_MOVERS_NONE) {
+        if (!gather_possible(s, src)) return MK_EUNSUPPORTED;
+        p.path = Path::kGather;
+    } else {
+        p.path = Path::kMove;
+    }
+    p.L = ws_layout(s->T, s->d, s->E, s->k, s->E_local, p.path != Path::kGather);
     return MK_OK;
 }
 
-size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src)
-{
-    (void)src;
-    if (check_shape(s) != MK_OK) return 0;
-    return ws_layout(s->T, s->d, s->E, s->k, s->E_local).total;
-}
-
-mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out)
-{
-    (void)src;
-    const mk_status st = check_shape(s);
-    if (st != MK_OK) return st;
-    if (!out) return MK_EINVAL;
-    *out = table_tuning(s, src);
-    return MK_OK;
-}
-
-mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
-                           const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
-                           int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
-                           void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream)
+// The dispatch call (the error words stay in the workspace for mk_poll_error).
+mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
+                        const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
+                        int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
+                        void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream)
 {
     mk_status st = check_shape(s);
     if (st != MK_OK) return st;
@@ -197,21 +165,14 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
                           topk_ids_out, topk_w_out, row_token, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return MK_EINVAL;
-    const WsLayout L = ws_layout(s->T, s->d, s->E, s->k, s->E_local);
+    Plan plan;
+    st = plan_call(s, src, tune, plan);
+    if (st != MK_OK) return st;
+    const WsLayout &L = plan.L;
     if (workspace_bytes < L.total) return MK_EWORKSPACE;
-
-    mk_tuning tu = table_tuning(s, src);
-    if (tune && (tune->bm || tune->bn || tune->bk || tune->n_mover_wg || tune->n_compute_wg)) {
-        if ((tune->bm && tune->bm != 256) || (tune->bn && tune->bn != 256) || (tune->bk && tune->bk != BigTile<256, 256>::BK))
-            return MK_EUNSUPPORTED;
-        if (tune->n_mover_wg) tu.n_mover_wg = tune->n_mover_wg;
-        tu.n_compute_wg = tune->n_compute_wg;
-    }
-    // The fused persistent kernel is the path; n_mover_wg < 0 asks for one launch per step instead
-    // (no overlap, for comparison).  Phase 3 keeps nblk * E_local block counts in LDS.
-    const bool fits_fused = (long)L.nblk * s->E_local <= kMaxScanEntries;
-    const bool staged = tu.n_mover_wg < 0 || s->T == 0 || !fits_fused;
-    if (staged && src->chunk_rows > 0) return MK_EUNSUPPORTED;
+    const mk_tuning &tu = plan.tu;
+    const bool staged = plan.path == Path::kStaged;
+    const bool gather = plan.path == Path::kGather;
     hipEvent_t ev_begin = tune ? (hipEvent_t)tune->ev_gemm_begin : nullptr;
     hipEvent_t ev_end = tune ? (hipEvent_t)tune->ev_gemm_end : nullptr;
 
@@ -230,8 +191,8 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     const SrcRows rows = make_src_rows(src);
 
     if (!staged) {
-        const int grid = fused_max_grid();
-        if (grid <= 0) return MK_EHIP;
+        const int resident = fused_max_grid();
+        if (resident <= 0) return MK_EHIP;
         FusedArgs fa{};
         fa.ra.src = rows;
         fa.ra.wr = w_router;
@@ -261,6 +222,11 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.ca.e_begin = s->e_begin;
         fa.ca.E_local = s->E_local;
         fa.ga.x_perm = x_perm;
+        if (gather) {
+            fa.ga.x_tok = rows.p[0];
+            fa.ga.row_token = row_token_ws;
+            fa.ga.T = s->T;
+        }
         fa.ga.w = (const uint16_t *)w_experts;
         fa.ga.y = (uint16_t *)y_perm;
         fa.ga.offsets = expert_offsets;
@@ -304,14 +270,22 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
         fa.bm = tu.bm;
         static_assert(256 % kMoveRows == 0, "mover units tile the GEMM row tiles");
         fa.has_sim = (src->chunk_rows > 0 && src->sim_delay_us) ? 1 : 0;
-        const int G = grid - fa.has_sim;
+        // Grid: every resident workgroup, or n_mover + n_compute of them (n_compute alone in the gather
+        // path); all of them must be resident together (grid barriers).
+        int G = resident - fa.has_sim;
+        if (tu.n_compute_wg > 0) {
+            G = tu.n_compute_wg + (gather ? 0 : tu.n_mover_wg);
+            if (G + fa.has_sim > resident) return MK_EUNSUPPORTED;
+        }
         if (G > kBarrierWGs) return MK_EUNSUPPORTED;
-        fa.n_mover = tu.n_mover_wg < 1 ? 1 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);
+        const int grid = G + fa.has_sim;
+        fa.gather = gather ? 1 : 0;
+        fa.n_mover = gather ? 0 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);
         fa.max_tiles = L.max_tiles;
         fa.ticks_per_us = (uint32_t)ticks_per_us();
         fa.trace = (uint64_t *)(ws + L.trace);
         if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
-        if (launch_fused(fa, grid, hs) != hipSuccess) return MK_EHIP;
+        if (launch_fused(fa, grid, tu.cooperative != 0, hs) != hipSuccess) return MK_EHIP;
         if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
         return MK_OK;
     }
@@ -402,14 +376,103 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     return MK_OK;
 }
 
+
+}  // namespace
+
+extern "C" {
+
+const char *mk_status_str(mk_status st)
+{
+    switch (st) {
+    case MK_OK: return "ok";
+    case MK_EINVAL: return "invalid argument";
+    case MK_EUNSUPPORTED: return "unsupported shape or option";
+    case MK_EWORKSPACE: return "workspace too small";
+    case MK_EHIP: return "HIP runtime error";
+    case MK_ETIMEOUT: return "device wait timed out";
+    default: return "unknown status";
+    }
+}
+
+size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E)
+{
+    if (T < 0 || E < 1) return 0;
+    return align256((size_t)kRouterSegments * T * E * 4) + 256;
+}
+
+mk_status mk_route_topk(const void *x, const float *w_router, const float *bias, int32_t T, int32_t d, int32_t E,
+                        int32_t k, int32_t *topk_ids, float *topk_w, void *workspace, size_t workspace_bytes,
+                        void *stream)
+{
+    if (T < 0 || d <= 0 || E < 1 || k < 1 || k > E) return MK_EINVAL;
+    if (d % 8 != 0) return MK_EINVAL;
+    if (d % 128 != 0 || E > 1024 || k > kMaxK) return MK_EUNSUPPORTED;
+    if (T == 0) return MK_OK;
+    if (!x || !w_router || !topk_ids || !workspace) return MK_EINVAL;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(workspace) ||
+        (bias && !aligned16(bias)) || (topk_w && !aligned16(topk_w)))
+        return MK_EINVAL;
+    if (workspace_bytes < mk_route_topk_workspace_bytes(T, E)) return MK_EWORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    RouterArgs ra{};
+    ra.src.p[0] = (const uint16_t *)x;
+    ra.src.S = 1;
+    ra.src.rows_per_src = T;
+    ra.wr = w_router;
+    ra.part = (float *)workspace;
+    ra.T = T;
+    ra.d = d;
+    ra.E = E;
+    if (launch_router(ra, st) != hipSuccess) return MK_EHIP;
+    TopkArgs ta{};
+    ta.part = (const float *)workspace;
+    ta.bias = bias;
+    ta.ids = topk_ids;
+    ta.ids_user = nullptr;
+    ta.w_user = topk_w;
+    ta.T = T;
+    ta.E = E;
+    ta.k = k;
+    CountArgs ca{};
+    if (launch_topk(ta, ca, false, st) != hipSuccess) return MK_EHIP;
+    return MK_OK;
+}
+
+size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src, const mk_tuning *tune)
+{
+    if (check_shape(s) != MK_OK || check_sources(s, src) != MK_OK) return 0;
+    Plan p;
+    if (plan_call(s, src, tune, p) != MK_OK) return 0;
+    return p.L.total;
+}
+
+mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out)
+{
+    mk_status st = check_shape(s);
+    if (st != MK_OK) return st;
+    st = check_sources(s, src);
+    if (st != MK_OK) return st;
+    if (!out) return MK_EINVAL;
+    *out = table_tuning(s, src);
+    return MK_OK;
+}
+
+mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
+                           const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
+                           int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
+                           void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream)
+{
+    return dispatch_impl(s, src, w_router, bias, topk_ids_in, w_experts, y_perm, slot_of, expert_offsets,
+                         topk_ids_out, topk_w_out, row_token, workspace, workspace_bytes, tune, stream);
+}
+
 mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,
                                   int32_t *words, int32_t *ticks_per_us_out)
 {
-    (void)src;
+    (void)src;   // the trace segment sits before the row buffer, at the same offset on every path
     const mk_status st = check_shape(s);
     if (st != MK_OK) return st;
-    const WsLayout L = ws_layout(s->T, s->d, s->E, s->k, s->E_local);
-    if (offset) *offset = L.trace;
+    if (offset) *offset = ws_layout(s->T, s->d, s->E, s->k, s->E_local, false).trace;
     if (n_wg) *n_wg = kTraceWGs;
     if (words) *words = kTraceWords;
     if (ticks_per_us_out) *ticks_per_us_out = ticks_per_us();

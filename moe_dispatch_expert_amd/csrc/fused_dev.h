@@ -58,7 +58,9 @@ struct FusedArgs {
     WsHeader *hdr;
     uint64_t spin_limit;
     int32_t T, d, E, k, e_begin, E_local, nblk, bm;
-    int32_t n_mover;             // workgroups that start as movers
+    int32_t n_mover;             // workgroups that start as movers (0: gather mode)
+    int32_t gather;              // 1: no mover role; the GEMM reads token rows through row_token (one resident
+                                 // source), after a third grid barrier that publishes row_token
     int32_t has_sim;             // last workgroup is the arrival simulator
     int32_t max_tiles;
     uint32_t ticks_per_us;       // wall-clock ticks per microsecond
@@ -79,24 +81,22 @@ __device__ __forceinline__ void trace_put(const FusedArgs &a, int word, uint64_t
 
 __device__ __forceinline__ int fused_participants(const FusedArgs &a) { return (int)gridDim.x - a.has_sim; }
 
+// Barrier targets of a call: barrier b (1, 2, 3) of the call with epoch c waits for the value 4 c + b.
+// Every workgroup reads the epoch at its start; the last workgroup to leave a call advances it
+// (fused_exit), so arrival words that a failed call left behind can never satisfy a barrier of a
+// later call.
+__device__ __forceinline__ uint32_t barrier_target(uint32_t call, int b) { return call * 4u + (uint32_t)b; }
+
 // Grid barrier over the participating workgroups (the simulator stays out).
-__device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detail)
+__device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t want, uint32_t detail)
 {
     // Arrival: each workgroup publishes its writes and then its own arrival word (release store, so
     // no two workgroups contend for one counter); workgroup 0 polls all the words, then releases
-    // the generation that the others wait for.  Every participant reads the generation before its
-    // arrival, so all agree on it; it does not change until all have arrived.
+    // the target value that the others wait for.
     wait_vmem_all();   // every wave's stores of the phase have reached L2
     __syncthreads();
-    __shared__ uint32_t g_shared;
     __shared__ int ok_shared;
-    if (threadIdx.x == 0) {
-        const uint32_t g = ld_relaxed(&a.hdr->bar_gen);
-        g_shared = g;
-        st_release(a.bar_flag + blockIdx.x, g + 1u);
-    }
-    __syncthreads();
-    const uint32_t want = g_shared + 1u;
+    if (threadIdx.x == 0) st_release(a.bar_flag + blockIdx.x, want);
     bool ok = true;
     if (blockIdx.x == 0) {
         const int G = fused_participants(a);
@@ -130,6 +130,30 @@ __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t detai
     if (threadIdx.x == 0) ok_shared = wait_flag_eq(&a.hdr->bar_gen, want, &a.hdr->err, a.spin_limit, detail) ? 1 : 0;
     __syncthreads();
     return ok_shared != 0;
+}
+
+// The epoch of the current call (uniform), read once at the start of every workgroup.
+__device__ __forceinline__ uint32_t fused_call_epoch(const FusedArgs &a)
+{
+    __shared__ uint32_t call_sh;
+    if (threadIdx.x == 0) call_sh = ld_relaxed(&a.hdr->call_epoch);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(call_sh);
+}
+
+// Every workgroup of the grid, on every path out of the call (also after a failed wait): count itself
+// out; the last one resets the count and advances the epoch.  No workgroup of this call reads the epoch
+// after that, and the next call on the stream starts after this one has ended.
+__device__ __forceinline__ void fused_exit(const FusedArgs &a, uint32_t call)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t n = __hip_atomic_fetch_add(&a.hdr->done_cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (n + 1u == gridDim.x) {
+            __hip_atomic_store(&a.hdr->done_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.hdr->call_epoch, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // Phase 3 in one workgroup: per-block exclusive bases for every local expert
@@ -342,8 +366,8 @@ __device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a)
 // addresses for the GEMM), also used by the earlier phases; off, toff, uoff:
 // LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
 template <class C>
-__device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *const (&st)[4], const LdsStages &ls, int32_t *off,
-                                  int32_t *toff, int32_t *uoff)
+__device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t call, char *const (&st)[4],
+                                                  const LdsStages &ls, int32_t *off, int32_t *toff, int32_t *uoff)
 {
     const int w = blockIdx.x;
     if (w < kTraceWGs && (int)threadIdx.x < kTraceWords) a.trace[w * kTraceWords + threadIdx.x] = 0;   // this call's record only
@@ -357,8 +381,6 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     }
     const int G = fused_participants(a);
 
-    // Every participant reads the barrier generation before its first arrival,
-    // so all of them agree on it; it does not change until all have arrived.
     if (w == 0 && threadIdx.x < 8) a.xcd_next[threadIdx.x] = 0u;
     for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x) a.tile_cnt[i] = 0u;
 
@@ -377,7 +399,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
         static_assert(4 * kRtLdsPerWave <= 4 * 32768, "router staging fits the stage arrays");
         for (int q = w * 4 + wave; q < tasks; q += G * 4) router_task(a.ra, q, rlds);
         trace_put(a, kTrRouted, now_ticks());
-        if (!fused_barrier(a, 0x01000000u)) return;
+        if (!fused_barrier(a, barrier_target(call, 1), 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
     }
     // ---- phase 2: top-k, histogram and ranks.  Routing inside: the selection
@@ -389,7 +411,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
         topk_wave_loop(a.ta, w, G);
         trace_put(a, kTrSelected, now_ticks());
         trace_put(a, kTrCounted, now_ticks());
-        if (!fused_barrier(a, 0x04000000u)) return;
+        if (!fused_barrier(a, barrier_target(call, 2), 0x04000000u)) return;
         trace_put(a, kTrBarB, now_ticks());
     } else {
         int32_t *ids_lds = (int32_t *)st[1];                          // 8 KiB
@@ -409,7 +431,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
             count_block(a.ca, blk, ids_lds, cnt_lds, mask_lds);
         }
         trace_put(a, kTrCounted, now_ticks());
-        if (!fused_barrier(a, 0x02000000u)) return;
+        if (!fused_barrier(a, barrier_target(call, 2), 0x02000000u)) return;
         trace_put(a, kTrBarB, now_ticks());
     }
 
@@ -454,11 +476,15 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
         }
     }
     trace_put(a, kTrSlots, now_ticks());
+    if (a.gather) {   // the GEMM reads row_token of every tile: wait for all of it
+        if (!fused_barrier(a, barrier_target(call, 3), 0x08000000u)) return;
+        trace_put(a, kTrBarC, now_ticks());
+    }
 
     // ---- movers: unit u = kMoveRows ranks of one expert (tile-major, since bm % kMoveRows == 0),
     // dealt round-robin over the movers
     uint64_t n_units = 0, copy_ticks = 0, release_ticks = 0;
-    if (w < a.n_mover) {
+    if (!a.gather && w < a.n_mover) {
         int32_t *tok_lds = (int32_t *)st[2] + 256;   // kMoveRows ints after the scan's partials
         const int n_units_all = uoff[a.E_local];
         // The arrival counter of unit u's tile.
@@ -555,6 +581,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     // Blocking: wait until all rows of t are moved (false: give up, the error word is set).
     auto wait = [&](const TileJob &t) -> bool {
         if (n_done == 0) trace_put(a, kTrFirstTask, now_ticks());
+        if (a.gather) return true;   // rows are read in place; row_token was published by barrier 3
         const uint64_t tw0 = now_ticks();
         if (threadIdx.x == 0)
             // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
@@ -569,7 +596,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, char *cons
     auto claim_job = [&]() { return job_of(claim()); };
     auto done = [&]() { ++n_done; };
     LambdaSched<decltype(claim_job), decltype(wait), decltype(done)> sc{claim_job, wait, done};
-    gemm_run(g, sc, ls);
+    gemm_run<C::NW>(g, sc, ls);
     trace_put(a, kTrDone, now_ticks());
     trace_put(a, kTrTasks, n_done);
     trace_put(a, kTrWaitTicks, wait_ticks);

@@ -7,24 +7,29 @@
 // design; the one here is written for CDNA4:
 //   - a workgroup of 4 waves owns a BN x BM tile of y^T (W rows x token rows);
 //     each wave a (BN/2) x (BM/2) quadrant made of 32x32 v_mfma bf16 blocks
-//     with K = 16 per instruction;
-//   - both operands are K-contiguous in HBM.  K runs in slabs of 64: each
-//     wave loads its share of a slab as whole 128-byte lines (8 rows x 128 B
-//     per buffer_load_dwordx4) into registers two slabs ahead, and writes the
-//     slab into one of two LDS buffers one slab ahead.  Streaming is latency
-//     bound per CU, so what counts is the bytes in flight: registers hold two
-//     slabs (128 KiB per workgroup) on top of the two LDS buffers;
+//     with K = 16 per instruction (one wave per SIMD);
+//   - both operands are K-contiguous in HBM.  K runs in slabs of 64 (one
+//     128-byte segment per tile row).  Slabs go from global memory straight
+//     into LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at byte
+//     16 l of a 1 KiB block), two stages, the loads of slab j + 2 issued while
+//     slab j is computed, so the waves issue no LDS writes and hold no staging
+//     registers: a wave's LDS issue rate (about 24 bytes per clock at one
+//     wave per SIMD, measured) then serves the fragment reads alone;
 //   - the 16-byte chunk index of each 128-byte LDS row is XOR-swizzled by
-//     (row >> 1) & 7, so both the slab writes and the fragment reads are
-//     conflict-free on the 64-bank LDS;
+//     (row >> 1) & 7, so the fragment reads are conflict-free on the 64-bank
+//     LDS; a load lane fetches the chunk that belongs at its LDS position;
 //   - fragment reads of the next K = 16 step are interleaved with the MFMAs
 //     of the current one (sched_group_barrier), and the one barrier per slab
-//     sits before the last step, so the next slab's first reads overlap it;
+//     sits before the last step, so the next slab's first reads and the next
+//     loads overlap it;
+//   - token rows come from an expert-contiguous row buffer, or straight from
+//     the token matrix through the slot -> token map (a gather in the loads,
+//     no copy);
 //   - W is the MFMA "A" operand, so each lane ends with 4 consecutive output
 //     columns of one row; the epilogue stages the bf16 tile in LDS and stores
 //     whole 512-byte row segments (16 bytes per lane);
-//   - ragged tails: tile rows past the expert's count read padding or the next
-//     expert's rows and are never stored; W rows past N are clamped.
+//   - ragged tails: tile rows past the expert's count read 0 (or the next
+//     expert's rows) and are never stored; W rows past N likewise.
 #pragma once
 
 #include "mk_args.h"
@@ -49,7 +54,10 @@ __device__ __forceinline__ lds_char_t *stage_at(const LdsStages &ls, int k)
 }
 
 struct GemmArgs {
-    const uint16_t *x_perm;      // [x_perm_rows, d]
+    const uint16_t *x_perm;      // [x_perm_rows, d] expert-contiguous rows (row mode)
+    const uint16_t *x_tok;       // [T, d] token matrix (gather mode: row r is token row_token[r]), or nullptr
+    const int32_t *row_token;    // [R_cap] slot -> token (gather mode)
+    int32_t T;                   // rows of x_tok
     const uint16_t *w;           // [E_local, N, d]
     uint16_t *y;                 // [R_cap, N]
     const int32_t *offsets;      // [E_local + 1]
@@ -61,22 +69,31 @@ struct GemmArgs {
     int32_t F;
 };
 
-template <int BM_, int BN_, int WN_ = 2>
+// A tile of BM token rows x BN W rows computed by NW waves, WN of them along N
+// and NW / WN along M.  A slab (K = 64) of an operand is BN / 8 (or BM / 8)
+// blocks of 8 rows x 128 bytes, one 1 KiB global -> LDS load each; wave w
+// loads blocks w, w + NW, w + 2 NW, ...: WS slots of W blocks, then XS slots of
+// x blocks (when NW does not divide BM / 8, the last slot of some waves holds
+// rows past the tile, which read 0 into a block the tile does not use).
+template <int BM_, int BN_, int WN_, int NW_>
 struct BigTile {
     static constexpr int BM = BM_;         // token rows per tile
     static constexpr int BN = BN_;         // W rows (output columns) per tile
-    static constexpr int WN = WN_;         // waves along N (the other 4 / WN along M)
-    static constexpr int WM = 4 / WN_;
+    static constexpr int NW = NW_;         // waves per workgroup
+    static constexpr int WN = WN_;         // waves along N (the other NW / WN along M)
+    static constexpr int WM = NW_ / WN_;
     static constexpr int BK = 64;          // K per slab: one 128-byte LDS row per tile row
     static constexpr int NI = BN / WN / 32;   // 32-wide blocks per wave along N
     static constexpr int MI = BM / WM / 32;   // 32-wide blocks per wave along M
-    static constexpr int WL = BN / 32;     // W loads per wave per slab (8 rows x 128 B each)
-    static constexpr int XL = BM / 32;     // x loads per wave per slab
-    static constexpr int STAGE = BN * BK * 2;   // bytes of one LDS array (W or x half of a slab buffer)
-    static constexpr int THREADS = 256;
-    static_assert(NI >= 1 && MI >= 1 && XL <= WL, "tile shape");
+    static constexpr int WB = BN / 8;      // W blocks per slab
+    static constexpr int XB = BM / 8;      // x blocks per slab
+    static constexpr int WS = WB / NW;     // W load slots per wave
+    static constexpr int XS = (XB + NW - 1) / NW;   // x load slots per wave
+    static constexpr int NS = WS + XS;
+    static constexpr int STAGE = 256 * BK * 2;   // bytes of one LDS array (the W or x half of a stage)
+    static constexpr int THREADS = 64 * NW;
+    static_assert(NI >= 1 && MI >= 1 && WB % NW == 0 && NW % 2 == 0 && BN <= 256 && BM <= 256, "tile shape");
 };
-static_assert(BigTile<256, 256>::STAGE == 32768, "an LDS array is 32 KiB");
 
 typedef int32_t v4i_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i_t lds_v4i_t;
@@ -93,46 +110,67 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, si
     return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
 }
 
-// One wave's share of a slab in registers: load i < WL is W, the rest x;
-// load i covers tile rows (4 (i % WL) + wave) * 8 + lane / 8, 16 bytes at
-// chunk lane % 8.
-template <class C>
-struct SlabRegs {
-    static constexpr int N = C::WL + C::XL;
-    v4i_t v[N];
-};
-
-// Loads [I0, I1) of slab `slab`.  The row part of each offset is in the
-// per-lane offset (voff[i] = row * row_bytes + chunk * 16), which the buffer
-// range check covers, so rows past the end of a resource read 0 without a
-// memory access; the K part (slab * 128 bytes, always inside the row) is the
-// scalar offset.  SwiGLU tiles (SW): voff[i >= WL / 2] carry the up rows' skip (slab_offsets<true>);
-// the x loads that share those offsets take it off again.
-template <class C, int I0, int I1, bool SW = false>
-__device__ __forceinline__ void load_part(__amdgpu_buffer_rsrc_t wsrc, __amdgpu_buffer_rsrc_t xsrc,
-                                          const uint32_t (&voff)[C::WL], int slab, SlabRegs<C> &r,
-                                          uint32_t up_skip = 0)
+// The same resource as four scalar dwords (base, stride 0, records, flags), for the slab loads below.
+typedef uint32_t rsrc4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc4_t make_rsrc4(const void *base, size_t bytes)
 {
-    const uint32_t k0 = (uint32_t)slab * C::BK * 2;
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        const int vi = i < C::WL ? i : i - C::WL;
-        const uint32_t vo = (SW && i >= C::WL && vi >= C::WL / 2) ? voff[vi] - up_skip : voff[vi];
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < C::WL ? wsrc : xsrc, vo, k0, 0);
-    }
+    const uint64_t b = (uint64_t)base;
+    return rsrc4_t{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)bytes),
+                   0x00020000u};
 }
 
-// Writes [I0, I1) of a slab from registers into an LDS buffer (128 B per row,
-// chunk p of row r at position p ^ ((r >> 1) & 7)).  st_off: this lane's byte
-// offset inside a block of 8 rows (the swizzle of row (4 i + wave) * 8 +
-// lane / 8 depends on the lane and the wave's parity only).
+// One global -> LDS load: 16 bytes per lane from rsrc + voff (range-checked) + soff land at LDS byte
+// lds_addr + 16 lane.  Written as an instruction of its own rather than the compiler builtin: for the
+// builtin the compiler cannot tell that the fragment reads of the other stage do not alias the loads
+// in flight, and waits for every load before each such read.  The loads have no register results; the
+// caller waits for them (s_waitcnt vmcnt) before a barrier, and the compiler's own vmcnt waits only
+// grow with loads it does not count.  M0 (the LDS address) is written by the compiler as an input;
+// the s_nop covers the M0 -> LDS-load hazard.
+__device__ __forceinline__ void lds_load16(rsrc4_t rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "{m0}"(lds_addr));
+}
+
+
+// Global -> LDS load slot i of slab `slab` into one stage: slot i < WS is W
+// block wave + NW i, the rest x block wave + NW (i - WS); block b covers
+// operand rows 8 b .. 8 b + 7, i.e. LDS bytes [1024 b, 1024 b + 1024) of the
+// stage array, lane l's 16 bytes at 1024 b + 16 l.  wo / xo: the lane's byte
+// offsets of its row and chunk (the row part is range-checked: rows past the
+// resource read 0); the K part (slab * 128 bytes) is the scalar offset.
+template <class C>
+__device__ __forceinline__ void dma_one(rsrc4_t wsrc, rsrc4_t xsrc, const uint32_t *wo, const uint32_t *xo, int i,
+                                        int slab, lds_char_t *wbuf, lds_char_t *xbuf, int wave)
+{
+    const uint32_t k0 = __builtin_amdgcn_readfirstlane((uint32_t)slab * C::BK * 2);
+    const bool isw = i < C::WS;
+    const int vi = isw ? i : i - C::WS;
+    // Every wave issues the same number of loads per slab, so that a wave's vmcnt waits (which count
+    // its own loads) cover the slab: an x slot past the tile's XB blocks (32-row tiles of eight waves)
+    // still loads, its rows lie past the tile's valid rows and read 0, and it lands in an LDS block the
+    // tile never reads (block b < 8 of the 32-block x array).
+    const int b = wave + C::NW * vi;
+    lds_char_t *dst = (isw ? wbuf : xbuf) + b * 1024;
+    lds_load16(isw ? wsrc : xsrc, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst), isw ? wo[vi] : xo[vi], k0);
+}
+
 template <class C, int I0, int I1>
-__device__ __forceinline__ void store_part(const SlabRegs<C> &r, lds_char_t *wbuf, lds_char_t *xbuf, int wave,
-                                           uint32_t st_off)
+__device__ __forceinline__ void dma_part(rsrc4_t wsrc, rsrc4_t xsrc, const uint32_t *wo, const uint32_t *xo,
+                                         int slab, lds_char_t *wbuf, lds_char_t *xbuf, int wave)
 {
 #pragma unroll
-    for (int i = I0; i < I1; ++i)
-        *(lds_v4i_t *)((i < C::WL ? wbuf : xbuf) + (4 * (i < C::WL ? i : i - C::WL) + wave) * 1024 + st_off) = r.v[i];
+    for (int i = I0; i < I1; ++i) dma_one<C>(wsrc, xsrc, wo, xo, i, slab, wbuf, xbuf, wave);
+}
+
+// The chunk a load lane fetches: LDS position lane % 8 of row 8 b + lane / 8 holds chunk
+// (lane % 8) ^ ((row >> 1) & 7), and (row >> 1) & 7 = (4 (b % 2) + lane / 16) & 7 with b % 2 = wave % 2
+// for every slot (NW is even).
+__device__ __forceinline__ uint32_t dma_chunk_bytes(int wave, int lane)
+{
+    return (uint32_t)(((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7)) << 4);
 }
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -155,53 +193,50 @@ __device__ __forceinline__ void wait_vmem()
 }
 __device__ __forceinline__ void wait_vmem_all() { wait_vmem<0>(); }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMFMA = 0x008, kSchedVMEMRead = 0x020, kSchedDSRead = 0x100, kSchedDSWrite = 0x200;
 
-template <class C>
-__device__ __forceinline__ void load_frags(const lds_char_t *wbuf, const lds_char_t *xbuf, int wn, int wm, int off,
-                                           bf16x8_t (&fa)[C::NI], bf16x8_t (&fb)[C::MI])
+// Fragment q of a K = 16 step (q < NI: W block q of the wave's N range;
+// else x block q - NI of its M range) from stage B: the LDS address is the
+// lane's precomputed base for the step (row lane % 32 of the block's first
+// row, chunk 2 kk + lane / 32 after the swizzle) plus immediates.
+template <class C, int B>
+__device__ __forceinline__ void read_frag(const lds_char_t *aw, const lds_char_t *ax, int q, bf16x8_t (&fa)[C::NI],
+                                          bf16x8_t (&fb)[C::MI])
 {
     typedef __attribute__((address_space(3))) const bf16x8_t lds_frag_t;
-    const lds_char_t *wt = wbuf + (wn * (C::BN / C::WN)) * 128;
-    const lds_char_t *xt = xbuf + (wm * (C::BM / C::WM)) * 128;
-#pragma unroll
-    for (int i = 0; i < C::NI; ++i) fa[i] = *(lds_frag_t *)(wt + i * 32 * 128 + off);
-#pragma unroll
-    for (int j = 0; j < C::MI; ++j) fb[j] = *(lds_frag_t *)(xt + j * 32 * 128 + off);
+    if (q < C::NI) fa[q] = *(lds_frag_t *)(aw + B * C::STAGE + q * 32 * 128);
+    else fb[q - C::NI] = *(lds_frag_t *)(ax + B * C::STAGE + (q - C::NI) * 32 * 128);
 }
 
+// The order in which a step's fragments are read: the one the next step's MFMA (0, 0) needs first,
+// then the x fragments (MFMAs (0, j)), then the remaining W fragments.
 template <class C>
-__device__ __forceinline__ void mfma_block(const bf16x8_t (&fa)[C::NI], const bf16x8_t (&fb)[C::MI],
-                                           f32x16_t (&acc)[C::NI][C::MI])
+__device__ __forceinline__ constexpr int frag_order(int r)
 {
-#pragma unroll
-    for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::MI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    return r == 0 ? 0 : (r <= C::MI ? C::NI + r - 1 : r - C::MI);
 }
 
-// Order the K = 16 step just emitted: NR fragment reads, then NW slab writes
-// each followed by a slab load, one after each MFMA; the rest of the MFMAs
-// after them.
-template <class C, int NR, int NW>
-__device__ __forceinline__ void sched_step()
+// One K = 16 step: the NI x MI MFMAs on (fa, fb) in order (i, j) row-major;
+// after MFMA q, slab load q (q < NLD, ld(q)) and fragment read frag_order(q)
+// of the next step (q < NRD, rd(...)).  The order is pinned: the reads and
+// loads are spread over the MFMAs instead of bunching at one end.
+template <class C, int NRD, int NLD, class RD, class LD>
+__device__ __forceinline__ void mfma_step(const bf16x8_t (&fa)[C::NI], const bf16x8_t (&fb)[C::MI],
+                                          f32x16_t (&acc)[C::NI][C::MI], RD &&rd, LD &&ld)
 {
-    constexpr int NM = C::NI * C::MI;
-    if (NR + NW > NM) return;   // too few MFMAs to pair with: the compiler's own order
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+    for (int q = 0; q < C::NI * C::MI; ++q) {
+        const int i = q / C::MI, j = q % C::MI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        if (q < NLD) ld(q);
+        if (q < NRD) rd(frag_order<C>(q));
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // a step with fewer MFMAs than loads or reads issues the rest after them
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSWrite, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVMEMRead, 1, 0);
+    for (int q = C::NI * C::MI; q < NLD || q < NRD; ++q) {
+        if (q < NLD) ld(q);
+        if (q < NRD) rd(frag_order<C>(q));
     }
-    if (NM - NR - NW > 0) __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NM - NR - NW, 0);
 }
 
 // Epilogue, first half: the tile's bf16 outputs go into LDS, so that the
@@ -246,7 +281,7 @@ __device__ __forceinline__ void stage_tile(const f32x16_t (&acc)[C::NI][C::MI], 
 }
 
 // Second half of the epilogue: after a barrier that follows stage_tile, wave
-// w stores rows [w * BM / 4, (w + 1) * BM / 4) of the staged tile.
+// w stores rows [w * BM / NW, (w + 1) * BM / NW) of the staged tile.
 template <class C>
 __device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, int rows_valid, int n0,
                                                   const LdsStages &ls, int wave, int lane)
@@ -256,7 +291,7 @@ __device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, i
     int lo_ = lane;
     asm volatile("" : "+v"(lo_));
     lane = lo_;
-    constexpr int RPW = C::BM / 4;
+    constexpr int RPW = C::BM / C::NW;
     constexpr int NS = RPW / 2, BATCH = NS < 8 ? NS : 8;
     static_assert(RPW % 2 == 0 && NS % BATCH == 0, "rows per wave");
     const int c = lane & 31;
@@ -294,7 +329,7 @@ __device__ __forceinline__ void store_staged_swiglu(const GemmArgs &a, int row0,
     int lo_ = lane;
     asm volatile("" : "+v"(lo_));
     lane = lo_;
-    constexpr int RPW = C::BM / 4;
+    constexpr int RPW = C::BM / C::NW;
     static_assert(RPW % 4 == 0, "rows per wave");
     const int c = lane & 15;
     const bool col_ok = f0 + c * 8 < a.F;   // F % 8 == 0
@@ -321,14 +356,18 @@ __device__ __forceinline__ void store_staged_swiglu(const GemmArgs &a, int row0,
     __syncthreads();   // the stage arrays are free again for the next tile
 }
 
-// The tile heights in use: full row tiles are 256 rows; the last (ragged)
-// row tile of an expert takes the smallest height that covers its rows, so a
-// tail of a few rows (and every tile of a decode-sized batch) costs a fraction
-// of a full tile's matrix work.
-typedef BigTile<256, 256, 2> TileM256;
-typedef BigTile<128, 256, 2> TileM128;
-typedef BigTile<64, 256, 4> TileM64;
-typedef BigTile<32, 256, 4> TileM32;
+// The tile heights in use for NW waves: full row tiles are 256 rows; the last
+// (ragged) row tile of an expert takes the smallest height that covers its
+// rows, so a tail of a few rows (and every tile of a decode-sized batch) costs
+// a fraction of a full tile's matrix work.  Eight waves (two per SIMD): each
+// wave owns 128 x 64 of a full tile; four waves: 128 x 128.
+template <int NW>
+struct Tiles {
+    typedef BigTile<256, 256, 2, NW> M256;
+    typedef BigTile<128, 256, 2, NW> M128;
+    typedef BigTile<64, 256, 4, NW> M64;
+    typedef BigTile<32, 256, NW == 8 ? 8 : 4, NW> M32;
+};
 
 // One GEMM task: token rows [row0, row0 + BM) of x_perm (rows_valid of them
 // readable and stored), W rows [n0, n0 + BN) of expert e.  rows_valid <= 0:
@@ -337,41 +376,74 @@ struct TileJob {
     int e, row0, rows_valid, n0;
 };
 
+// The lane's byte offsets of a tile's x rows: slot i covers tile row
+// (wave + NW i) * 8 + lane / 8 (the same rows for every tile height; a
+// shorter tile uses the first slots), plus its chunk.  Computed for the next task while the current one stores its
+// outputs, so the slot -> token reads of the gather mode are off the critical path.
+template <int NW>
+struct XOffsets {
+    uint32_t v[Tiles<NW>::M256::XS];
+};
+
+template <int NW>
+__device__ __forceinline__ XOffsets<NW> x_offsets(const GemmArgs &a, const TileJob &t, int wave, int lane)
+{
+    XOffsets<NW> o;
+    const uint32_t row_bytes = (uint32_t)a.d * 2;
+    const uint32_t ch = dma_chunk_bytes(wave, lane);
+#pragma unroll
+    for (int i = 0; i < Tiles<NW>::M256::XS; ++i) {
+        const int m = (wave + NW * i) * 8 + (lane >> 3);
+        if (a.x_tok) {
+            // Gather: row m of the tile is token row_token[row0 + m] of the token matrix; rows past the
+            // tile's valid rows point past the end of the resource and read 0 without a memory access.
+            const int tok = (t.rows_valid > 0 && m < t.rows_valid) ? a.row_token[t.row0 + m] : a.T;
+            o.v[i] = (uint32_t)tok * row_bytes + ch;
+        } else {
+            o.v[i] = (uint32_t)m * row_bytes + ch;
+        }
+    }
+    return o;
+}
+
 // The W and x buffer resources of a tile.
 struct TileSrc {
-    __amdgpu_buffer_rsrc_t w, x;
+    rsrc4_t w, x;
 };
 
 __device__ __forceinline__ TileSrc tile_src(const GemmArgs &a, const TileJob &t)
 {
     TileSrc s;
     const size_t w_first = (size_t)t.e * a.N + t.n0;
-    s.w = make_rsrc(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
-    // Only the tile's valid rows are readable: rows past a ragged end return 0 without a memory access
-    // (they may belong to a tile that is not yet moved).
-    s.x = make_rsrc(a.x_perm + (size_t)t.row0 * a.d, (size_t)t.rows_valid * a.d * 2);
+    s.w = make_rsrc4(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
+    if (a.x_tok) s.x = make_rsrc4(a.x_tok, (size_t)a.T * a.d * 2);
+    // Row mode: only the tile's valid rows are readable: rows past a ragged end return 0 without a
+    // memory access (they may belong to a tile that is not yet moved).
+    else s.x = make_rsrc4(a.x_perm + (size_t)t.row0 * a.d, (size_t)t.rows_valid * a.d * 2);
     return s;
 }
 
-// Per-lane byte offsets of the slab loads (the same for every tile of a
-// launch): load i covers tile rows (4 i + wave) * 8 + lane / 8, 16 bytes at
-// chunk lane % 8 of the row's 128-byte slab segment.
+// Per-lane byte offsets of the W loads (the same for every tile of a launch):
+// slot i covers W tile rows (wave + NW i) * 8 + lane / 8.
+template <int NW>
 struct SlabOffsets {
-    uint32_t v[TileM256::WL];
+    uint32_t v[Tiles<NW>::M256::WS];
 };
 
 // SwiGLU tiles (SW): tile rows 0..127 are gate rows f0.., rows 128..255 the up rows F + f0.., so the
-// W loads of the second half (i >= WL / 2: rows >= 128) skip F - 128 rows.
-template <bool SW = false>
-__device__ __forceinline__ SlabOffsets slab_offsets(const GemmArgs &a, int wave, int lane)
+// W loads of blocks 16.. (rows >= 128) skip F - 128 rows.
+template <int NW, bool SW = false>
+__device__ __forceinline__ SlabOffsets<NW> slab_offsets(const GemmArgs &a, int wave, int lane)
 {
-    SlabOffsets o;
+    SlabOffsets<NW> o;
     const uint32_t row_bytes = (uint32_t)a.d * 2;
     const uint32_t up_skip = SW ? (uint32_t)(a.F - 128) * row_bytes : 0u;
+    const uint32_t ch = dma_chunk_bytes(wave, lane);
 #pragma unroll
-    for (int i = 0; i < TileM256::WL; ++i)
-        o.v[i] = (uint32_t)((4 * i + wave) * 8 + (lane >> 3)) * row_bytes + (uint32_t)(lane & 7) * 16u +
-                 (i >= TileM256::WL / 2 ? up_skip : 0u);
+    for (int i = 0; i < Tiles<NW>::M256::WS; ++i) {
+        const int b = wave + NW * i;
+        o.v[i] = (uint32_t)(b * 8 + (lane >> 3)) * row_bytes + ch + (b >= 16 ? up_skip : 0u);
+    }
     return o;
 }
 
@@ -379,32 +451,37 @@ __device__ __forceinline__ SlabOffsets slab_offsets(const GemmArgs &a, int wave,
 // (sc.claim() into `next`; not earlier, so that no workgroup holds a second
 // task while others still look for their first), then runs the epilogue.
 //
-// Slab j (K = 64 j .. 64 j + 63) is computed from LDS buffer j % 2 (W in
-// ls.p[2 (j % 2)], x in ls.p[2 (j % 2) + 1]) in four K = 16 steps, with the
-// fragments of step s + 1 read during the MFMAs of step s.  Between steps 2
-// and 3: write slab j + 1 from registers into the other buffer (its old slab
-// j - 1 was last read before the previous barrier), load slab j + 3 into the
-// registers just freed, barrier, then read step 0 of slab j + 1 during step 3.
-// Slab s lives in register set s % 2, loaded two slabs before it is written.
+// Slab j (K = 64 j .. 64 j + 63) sits in stage j % 2 (W in ls.p[2 (j % 2)],
+// x in ls.p[2 (j % 2) + 1]) and is computed in four K = 16 steps, the
+// fragments of step s + 1 read during the MFMAs of step s.  Before step 3:
+// wait for this wave's loads of slab j + 1 and for its fragment reads of step
+// 3, then one barrier (every wave's slab j + 1 has landed, and no wave reads
+// stage j % 2 any more); during step 3, issue the loads of slab j + 2 into
+// stage j % 2 and read step 0 of slab j + 1.
 template <class C, bool SW, class Sched>
-__device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &job, TileJob &next, Sched &sc,
-                                              const LdsStages &ls, const SlabOffsets &so)
+__device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &job, const XOffsets<C::NW> &xoff,
+                                              TileJob &next, XOffsets<C::NW> &xoff_next, Sched &sc,
+                                              const LdsStages &ls, const SlabOffsets<C::NW> &so)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // uniform: keeps soffsets scalar
     const int lane = threadIdx.x % kWave;
     const int wn = wave % C::WN, wm = wave / C::WN;
     const TileSrc src = tile_src(a, job);
-    const uint32_t(&voff)[TileM256::WL] = so.v;
-    // Loads of slabs past the end go to empty resources: they read 0 without a memory access, and
-    // keep the number of loads in flight the same on every path.
-    const __amdgpu_buffer_rsrc_t wnone = make_rsrc(a.w, 0), xnone = make_rsrc(a.x_perm, 0);
-    const uint32_t st_off = (uint32_t)(lane >> 3) * 128u + (uint32_t)(((lane & 7) ^ ((lane >> 4) + 4 * (wave & 1))) << 4);
+    const uint32_t *wo = so.v;
+    const uint32_t *xo = xoff.v;
     const int KK = __builtin_amdgcn_readfirstlane(a.d / C::BK);   // even (d % 128 == 0); uniform
 
-    int frag_off[4];   // row (lane & 31) of a 32-row block, chunk 2 kk + lane / 32
+    // LDS: W of stage 0 and 1 in ls.p[0], ls.p[1]; x of stage 0 and 1 in ls.p[2], ls.p[3] (consecutive
+    // 32 KiB arrays, so a stage is an immediate offset).  The lane's fragment bases, one per K = 16
+    // step kk of a slab: row (lane & 31), chunk 2 kk + lane / 32 after the swizzle.
+    const lds_char_t *aw[4], *ax[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        frag_off[kk] = (lane & 31) * 128 + (((2 * kk + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) << 4);
+    for (int kk = 0; kk < 4; ++kk) {
+        int fo = (lane & 31) * 128 + (((2 * kk + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) << 4);
+        asm volatile("" : "+v"(fo));   // computed once, kept in a register (no re-adds in the loop)
+        aw[kk] = ls.p[0] + wn * (C::BN / C::WN) * 128 + fo;
+        ax[kk] = ls.p[2] + wm * (C::BM / C::WM) * 128 + fo;
+    }
 
     f32x16_t acc[C::NI][C::MI];
 #pragma unroll
@@ -414,74 +491,47 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    lds_char_t *const wb[2] = {ls.p[0], ls.p[2]};
-    lds_char_t *const xb[2] = {ls.p[1], ls.p[3]};
-    constexpr int NL = SlabRegs<C>::N;
-    constexpr int P1 = (NL + 2) / 3, P2 = (2 * NL + 2) / 3;   // the slab write in three parts
-    constexpr int NR = C::NI + C::MI;
-    SlabRegs<C> r0, r1;
-    const uint32_t up_skip = SW ? (uint32_t)__builtin_amdgcn_readfirstlane((a.F - 128) * a.d * 2) : 0u;
-    load_part<C, 0, NL, SW>(src.w, src.x, voff, 0, r0, up_skip);
-    load_part<C, 0, NL, SW>(src.w, src.x, voff, 1, r1, up_skip);
-    store_part<C, 0, NL>(r0, wb[0], xb[0], wave, st_off);
-    load_part<C, 0, NL, SW>(KK > 2 ? src.w : wnone, KK > 2 ? src.x : xnone, voff, 2, r0, up_skip);
-    __syncthreads();
+    lds_char_t *const wb[2] = {ls.p[0], ls.p[1]};
+    lds_char_t *const xb[2] = {ls.p[2], ls.p[3]};
+    constexpr int NL = C::NS;           // load slots per wave per slab
+    constexpr int NR = C::NI + C::MI;   // fragment reads per wave per K = 16 step
+    dma_part<C, 0, NL>(src.w, src.x, wo, xo, 0, wb[0], xb[0], wave);
+    dma_part<C, 0, NL>(src.w, src.x, wo, xo, 1, wb[1], xb[1], wave);
+    wait_vmem<NL>();   // this wave's slab 0 has landed
+    __syncthreads();   // every wave's
     bf16x8_t fa0[C::NI], fb0[C::MI], fa1[C::NI], fb1[C::MI];
-    load_frags<C>(wb[0], xb[0], wn, wm, frag_off[0], fa0, fb0);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) read_frag<C, 0>(aw[0], ax[0], q, fa0, fb0);
 
-    // Slab J from buffer B; RN: the register set holding slab J + 1; NEXT
-    // (compile-time): slab J + 1 exists.  During steps 0..2, slab J + 1 is
-    // written from RN into the other buffer, a third per step, and each
-    // register is refilled with slab J + 3 right after it is written (from
-    // the empty resources if slab J + 3 does not exist).
-#define MK_GEMM_SLAB(B, RN, J, NEXT)                                                                   \
-    do {                                                                                               \
-        const bool ahead_ = __builtin_amdgcn_readfirstlane((J) + 3 < KK);                              \
-        const __amdgpu_buffer_rsrc_t wl_ = ahead_ ? src.w : wnone, xl_ = ahead_ ? src.x : xnone;       \
-        lds_char_t *const wo_ = wb[1 - (B)];                                                           \
-        lds_char_t *const xo_ = xb[1 - (B)];                                                           \
-        load_frags<C>(wb[B], xb[B], wn, wm, frag_off[1], fa1, fb1);                                    \
-        mfma_block<C>(fa0, fb0, acc);                                                                  \
-        if (NEXT) {                                                                                    \
-            store_part<C, 0, P1>(RN, wo_, xo_, wave, st_off);                                          \
-            load_part<C, 0, P1, SW>(wl_, xl_, voff, (J) + 3, RN, up_skip);                                 \
-            sched_step<C, NR, P1>();                                                                   \
-        } else {                                                                                       \
-            sched_step<C, NR, 0>();                                                                    \
-        }                                                                                              \
-        load_frags<C>(wb[B], xb[B], wn, wm, frag_off[2], fa0, fb0);                                    \
-        mfma_block<C>(fa1, fb1, acc);                                                                  \
-        if (NEXT) {                                                                                    \
-            store_part<C, P1, P2>(RN, wo_, xo_, wave, st_off);                                         \
-            load_part<C, P1, P2, SW>(wl_, xl_, voff, (J) + 3, RN, up_skip);                                \
-            sched_step<C, NR, P2 - P1>();                                                              \
-        } else {                                                                                       \
-            sched_step<C, NR, 0>();                                                                    \
-        }                                                                                              \
-        load_frags<C>(wb[B], xb[B], wn, wm, frag_off[3], fa1, fb1);                                    \
-        mfma_block<C>(fa0, fb0, acc);                                                                  \
-        if (NEXT) {                                                                                    \
-            store_part<C, P2, NL>(RN, wo_, xo_, wave, st_off);                                         \
-            load_part<C, P2, NL, SW>(wl_, xl_, voff, (J) + 3, RN, up_skip);                                \
-            sched_step<C, NR, NL - P2>();                                                              \
-            __builtin_amdgcn_sched_barrier(0);                                                         \
-            __syncthreads();                                                                           \
-            load_frags<C>(wo_, xo_, wn, wm, frag_off[0], fa0, fb0);                                    \
-        } else {                                                                                       \
-            sched_step<C, NR, 0>();                                                                    \
-        }                                                                                              \
-        mfma_block<C>(fa1, fb1, acc);                                                                  \
-        if (NEXT) sched_step<C, NR, 0>();                                                              \
-        else sched_step<C, 0, 0>();                                                                    \
+    auto none = [](int) {};
+    // Slab J from stage B.  MODE (compile-time): 2 = slab J + 1 exists and slab J + 2 is loaded into
+    // stage B during step 3; 1 = slab J + 1 exists, nothing more to load; 0 = the last slab.
+#define MK_GEMM_SLAB(B, J, MODE)                                                                         \
+    do {                                                                                                \
+        mfma_step<C, NR, 0>(fa0, fb0, acc, [&](int q) { read_frag<C, B>(aw[1], ax[1], q, fa1, fb1); }, none); \
+        mfma_step<C, NR, 0>(fa1, fb1, acc, [&](int q) { read_frag<C, B>(aw[2], ax[2], q, fa0, fb0); }, none); \
+        mfma_step<C, NR, 0>(fa0, fb0, acc, [&](int q) { read_frag<C, B>(aw[3], ax[3], q, fa1, fb1); }, none); \
+        if constexpr ((MODE) > 0) {                                                                     \
+            __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0): slab J + 1 and step 3 here */   \
+            __syncthreads();                                                                            \
+            mfma_step<C, NR, (MODE) == 2 ? NL : 0>(                                                     \
+                fa1, fb1, acc, [&](int q) { read_frag<C, 1 - (B)>(aw[0], ax[0], q, fa0, fb0); },        \
+                [&](int q) {                                                                            \
+                    if constexpr ((MODE) == 2)                                                          \
+                        dma_one<C>(src.w, src.x, wo, xo, q, (J) + 2, wb[B], xb[B], wave);           \
+                });                                                                                     \
+        } else {                                                                                        \
+            mfma_step<C, 0, 0>(fa1, fb1, acc, none, none);                                              \
+        }                                                                                               \
     } while (0)
 
     int j = 0;
     for (; j + 2 < KK; j += 2) {
-        MK_GEMM_SLAB(0, r1, j, true);
-        MK_GEMM_SLAB(1, r0, j + 1, true);
+        MK_GEMM_SLAB(0, j, 2);
+        MK_GEMM_SLAB(1, j + 1, 2);
     }
-    MK_GEMM_SLAB(0, r1, j, true);
-    MK_GEMM_SLAB(1, r0, j + 1, false);
+    MK_GEMM_SLAB(0, j, 1);
+    MK_GEMM_SLAB(1, j + 1, 0);
 #undef MK_GEMM_SLAB
 
     // Distance between the last MFMA and the first read of its accumulators.  The compiler pads that
@@ -501,6 +551,7 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
     __syncthreads();   // every wave is done with the stages before the epilogue reuses them
     stage_tile<C>(acc, ls, wave, lane);
     next = sc.claim();
+    xoff_next = x_offsets<C::NW>(a, next, wave, lane);
     __syncthreads();   // the staged tile is complete
     if constexpr (SW) store_staged_swiglu<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
     else store_staged_tile<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
@@ -521,20 +572,25 @@ struct LambdaSched {
 // this workgroup (rows_valid <= 0: none left); wait(job) -> false if the
 // workgroup must stop (a failed wait for the job's rows); done() after each
 // tile.
-template <bool SW = false, class Sched>
+template <int NW, bool SW = false, class Sched>
 __device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const LdsStages &ls)
 {
-    const SlabOffsets so = slab_offsets<SW>(a, __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), threadIdx.x % kWave);
+    typedef Tiles<NW> T;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const SlabOffsets<NW> so = slab_offsets<NW, SW>(a, wave, lane);
     TileJob job = sc.claim();
+    XOffsets<NW> xo = x_offsets<NW>(a, job, wave, lane);
     while (job.rows_valid > 0) {
         if (!sc.wait(job)) return;
         TileJob next;
-        if (job.rows_valid > 128) gemm_tile_big<TileM256, SW>(a, job, next, sc, ls, so);
-        else if (job.rows_valid > 64) gemm_tile_big<TileM128, SW>(a, job, next, sc, ls, so);
-        else if (job.rows_valid > 32) gemm_tile_big<TileM64, SW>(a, job, next, sc, ls, so);
-        else gemm_tile_big<TileM32, SW>(a, job, next, sc, ls, so);
+        XOffsets<NW> xo_next;
+        if (job.rows_valid > 128) gemm_tile_big<typename T::M256, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        else if (job.rows_valid > 64) gemm_tile_big<typename T::M128, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        else if (job.rows_valid > 32) gemm_tile_big<typename T::M64, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        else gemm_tile_big<typename T::M32, SW>(a, job, xo, next, xo_next, sc, ls, so);
         sc.done();
         job = next;
+        xo = xo_next;
     }
 }
 
@@ -584,7 +640,7 @@ __device__ __forceinline__ void gemm_worker(const GemmArgs &a, int w, int G, con
     };
     const int NB = SW ? (a.F + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
     Sched sc{a, NB, (int)a.hdr->n_tiles * NB, (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w, G};
-    gemm_run<SW>(a, sc, ls);
+    gemm_run<C::NW, SW>(a, sc, ls);
 }
 
 }  // namespace mk

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_move(SrcRows src, const int32_t *row_to
 }
 
 template <class C, bool SW = false>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
+__global__ __launch_bounds__(C::THREADS, 1) void k_gemm(GemmArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
     LdsStages ls;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a)
 }
 
 template <class C>
-__global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
+__global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
     __shared__ int32_t off[1025], toff[1025], uoff[1025];
@@ -85,7 +85,9 @@ __global__ __launch_bounds__(256, 1) void k_fused(FusedArgs a)
         st[k] = stg + k * C::STAGE;
         ls.p[k] = (lds_char_t *)st[k];
     }
-    fused_kernel_body<C>(a, st, ls, off, toff, uoff);
+    const uint32_t call = fused_call_epoch(a);
+    fused_kernel_body<C>(a, call, st, ls, off, toff, uoff);
+    fused_exit(a, call);
 }
 
 // Combine: wave task q = (token q / nc, 512-column chunk q % nc); the lane owns
@@ -244,12 +246,13 @@ hipError_t launch_tiles(const int32_t *offsets, int32_t E_local, int32_t bm, int
     return hipGetLastError();
 }
 
-typedef BigTile<256, 256> Tile256;
+typedef Tiles<8>::M256 Tile256;       // the grouped GEMM launches: eight waves per workgroup
+typedef Tiles<4>::M256 FusedTile;     // the fused kernel: four waves per workgroup
 
 hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s)
 {
     if (bm == 256 && bn == 256) {
-        hipLaunchKernelGGL((k_gemm<Tile256>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<Tile256>), dim3(grid), dim3(Tile256::THREADS), 0, s, a);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;
@@ -257,7 +260,7 @@ hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t 
 
 hipError_t launch_gemm_swiglu(const GemmArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_gemm<Tile256, true>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<Tile256, true>), dim3(grid), dim3(Tile256::THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -267,21 +270,28 @@ int gemm_max_grid(int bm, int bn)
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (bm == 256 && bn == 256) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemm<Tile256>, 256, 0) !=
-            hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemm<Tile256>, Tile256::THREADS,
+                                                         0) != hipSuccess)
             return 0;
     }
     return cus * per_cu;
 }
 
-// An ordinary launch of as many workgroups as the device holds at once (a
-// cooperative launch measured ~15 us more per call).  The grid barriers need
-// every workgroup resident together: with the device's CUs free of other work
-// the dispatcher places them all; work of other streams only delays the late
-// ones, and a wait that outlasts the bound ends the call with MK_ETIMEOUT.
-hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s)
+// An ordinary launch of at most as many workgroups as the device holds at
+// once, or (cooperative) a cooperative launch, which costs ~15 us more per
+// call.  The grid barriers need every workgroup resident together: with the
+// device's CUs free of other work the dispatcher places them all; work of
+// other streams only delays the late ones, and a wait that outlasts the bound
+// ends the call with MK_ETIMEOUT.  A cooperative launch has the runtime
+// guarantee co-residency instead.
+hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_fused<Tile256>, dim3(grid), dim3(256), 0, s, a);
+    if (cooperative) {   // the runtime guarantees co-residency (or refuses the launch)
+        void *args[] = {(void *)&a};
+        return hipLaunchCooperativeKernel((const void *)k_fused<FusedTile>, dim3(grid), dim3(FusedTile::THREADS), args,
+                                          0, s);
+    }
+    hipLaunchKernelGGL(k_fused<FusedTile>, dim3(grid), dim3(FusedTile::THREADS), 0, s, a);
     return hipGetLastError();
 }
 
@@ -293,7 +303,8 @@ int fused_max_grid()
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev >= 0 && dev < kMaxDevices && cached[dev] > 0) return cached[dev];
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<Tile256>, 256, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<FusedTile>, FusedTile::THREADS,
+                                                     0) != hipSuccess)
         return 0;
     if (dev >= 0 && dev < kMaxDevices) cached[dev] = cus * per_cu;
     return cus * per_cu;

@@ -35,11 +35,11 @@ struct SrcFlags {
 struct WsHeader {
     uint32_t err;          // 0 or an mk_status code
     uint32_t err_detail;
-    uint32_t bar_spare;    // unused
-    uint32_t bar_gen;      // grid barrier generation (grows by one per barrier)
+    uint32_t done_cnt;     // fused kernel: workgroups that have left the current call (0 between calls)
+    uint32_t bar_gen;      // grid barrier: the last target value released by workgroup 0
     uint32_t n_tiles;      // GEMM row tiles of the current call
     uint32_t R;            // routed local rows of the current call
-    uint32_t call_epoch;   // spare
+    uint32_t call_epoch;   // fused kernel: calls completed through this workspace (barrier targets derive from it)
     uint32_t xcd_next[8];  // fused kernel: per-XCD GEMM task counters
     uint32_t pad[49];
 };
@@ -57,13 +57,15 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_local)
+// with_x_perm: the call copies rows into the expert-contiguous row buffer (mover role or staged path);
+// the gather path reads rows in place and needs no such buffer.
+inline WsLayout ws_layout(int32_t T, int32_t d, int32_t E, int32_t k, int32_t E_local, bool with_x_perm)
 {
     WsLayout L{};
     L.nblk = (T + kTokBlock - 1) / kTokBlock;
     L.r_cap = T * (k < E_local ? k : E_local);
     L.max_tiles = L.r_cap / kMinBM + E_local + 1;
-    L.x_perm_rows = L.r_cap + 256;   // a full tile past the last row stays in bounds
+    L.x_perm_rows = with_x_perm ? L.r_cap + 256 : 0;   // a full tile past the last row stays in bounds
     size_t o = 0;
     L.hdr = o;       o += align256(sizeof(WsHeader));
     L.bar_flag = o;  o += align256((size_t)kBarrierWGs * 4);

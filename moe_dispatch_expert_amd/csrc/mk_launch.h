@@ -42,7 +42,7 @@ hipError_t launch_gemm_swiglu(const GemmArgs &a, int grid, hipStream_t s);
 int gemm_max_grid(int bm, int bn);
 // The persistent fused kernel: one workgroup per resident slot of the device (its grid barriers need them all
 // resident together).
-hipError_t launch_fused(const FusedArgs &a, int grid, hipStream_t s);
+hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s);
 int fused_max_grid();
 
 }  // namespace mk

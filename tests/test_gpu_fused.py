@@ -193,3 +193,35 @@ def test_withheld_arrival_flag_times_out():
             os.environ["MK_TIMEOUT_US"] = old
     assert st == mk.MK_ETIMEOUT
     assert detail == (0x20000000 | (n_chunks // 2))
+
+
+def test_workspace_reusable_after_timeout():
+    """After a call that ended in MK_ETIMEOUT (a withheld arrival flag: movers, tile waits and grid state
+    left mid-call), mk_poll_error and then a call with every chunk released through the same workspace
+    give the same bits as a fresh workspace."""
+    wl = _ep_small()
+    inp, dev, ids_in = _ep_inputs(wl, 43)
+    ref, st, _, _ = _ep_run(wl, inp, dev, ids_in, pre_release=True)
+    assert st == mk.MK_OK
+    n_chunks = wl.S * (wl.rows_per_src // wl.chunk_rows)
+    ready = torch.ones(n_chunks, dtype=torch.int32, device="cuda")
+    ready[3] = 0
+    ws = torch.zeros_like(ref["workspace"])
+    old = os.environ.get("MK_TIMEOUT_US")
+    os.environ["MK_TIMEOUT_US"] = "20000"
+    try:
+        mk.mk_dispatch_gemm(dev["x"], dev["w_experts"], wl.k, topk_ids_in=ids_in, E=wl.E, e_begin=wl.e_begin,
+                            chunk_rows=wl.chunk_rows, chunk_ready=ready, epoch=1, workspace=ws)
+        st, _ = mk.mk_poll_error(ws)
+    finally:
+        if old is None:
+            del os.environ["MK_TIMEOUT_US"]
+        else:
+            os.environ["MK_TIMEOUT_US"] = old
+    assert st == mk.MK_ETIMEOUT
+    ready.fill_(1)
+    out = mk.mk_dispatch_gemm(dev["x"], dev["w_experts"], wl.k, topk_ids_in=ids_in, E=wl.E, e_begin=wl.e_begin,
+                              chunk_rows=wl.chunk_rows, chunk_ready=ready, epoch=1, workspace=ws)
+    st, detail = mk.mk_poll_error(ws)
+    assert st == mk.MK_OK, (mk.mk_status_str(st), detail)
+    _same(ref, out)

@@ -251,3 +251,23 @@ def test_bad_source_ids_reported():
     out = mk.mk_dispatch_gemm(dev["x"], dev["w_experts"], wl.k, topk_ids_in=ids.cuda(), E=wl.E)
     st, detail = mk.mk_poll_error(out["workspace"])
     assert st == mk.MK_EINVAL and detail == 17
+
+
+def test_workspace_reusable_after_device_error():
+    """A call that fails on the device leaves its grid barrier half passed: bad source ids raise MK_EINVAL
+    while the workgroups arrive at the barrier after the histogram, and they give up there.  After
+    mk_poll_error, a valid call through the same workspace must not pass that barrier early on the words
+    the failed call left behind; its result is checked in full against the oracle."""
+    wl = W.scaled(W.WORKLOADS["tiny"], T=64, N=64)
+    inp = W.make_inputs(wl, 12)
+    dev = to_dev(inp)
+    ws = torch.zeros(mk.mk_dispatch_gemm_workspace_bytes(wl.T, wl.d, wl.E, wl.k, 0, wl.E_local, wl.N),
+                     dtype=torch.uint8, device="cuda")
+    ids = torch.tensor([[0, 1]] * 64, dtype=torch.int32)
+    ids[5] = torch.tensor([2, 200])
+    mk.mk_dispatch_gemm(dev["x"], dev["w_experts"], wl.k, topk_ids_in=ids.cuda(), E=wl.E, workspace=ws)
+    st, detail = mk.mk_poll_error(ws)
+    assert st == mk.MK_EINVAL and detail == 5
+    for _ in range(2):
+        out = _run(inp, dev, workspace=ws)
+        full_check(inp, out, what="after a failed call")
