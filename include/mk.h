@@ -179,6 +179,30 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src,
                            void *workspace, size_t workspace_bytes,
                            const mk_tuning *tune, void *stream);
 
+/* mk_dispatch_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, inputs and outputs, with the workspace replaced by the
+ * library's own device array of MK_STATIC_SCRATCH_BYTES (one per GPU, held
+ * until the process ends).  The call allocates nothing.
+ *   status   [2] int32 (out, device): the call's device status (an mk_status:
+ *            MK_OK, MK_ETIMEOUT or MK_EINVAL) and its detail, written when the
+ *            call ends on the stream (read it after a sync); it takes the
+ *            place of mk_poll_error for this entry point.
+ * A shape, sources and tuning whose workspace (mk_dispatch_gemm_workspace_bytes)
+ * exceeds MK_STATIC_SCRATCH_BYTES is refused with MK_EWORKSPACE before any
+ * device work; paths that copy rows into the expert-contiguous buffer need it
+ * for the rows, so in practice this is the in-place path (one resident source).
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race and give undefined results. */
+#define MK_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+mk_status mk_dispatch_gemm_static(const mk_shape *s, const mk_sources *src,
+                                  const float *w_router, const float *bias,
+                                  const int32_t *topk_ids_in,
+                                  const void *w_experts,
+                                  void *y_perm, int32_t *slot_of, int32_t *expert_offsets,
+                                  int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
+                                  int32_t *status, const mk_tuning *tune, void *stream);
+
 /* The tuning the per-shape table picks (what a NULL/zero `tune` means). */
 mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out);
 

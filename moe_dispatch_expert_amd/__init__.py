@@ -82,6 +82,9 @@ def load() -> ctypes.CDLL:
     lib.mk_dispatch_gemm.argtypes = [P(MkShape), P(MkSources), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, ctypes.c_size_t, P(MkTuning), _vp]
     lib.mk_dispatch_gemm.restype = _c_i32
+    lib.mk_dispatch_gemm_static.argtypes = [P(MkShape), P(MkSources), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, P(MkTuning), _vp]
+    lib.mk_dispatch_gemm_static.restype = _c_i32
     lib.mk_select_tuning.argtypes = [P(MkShape), P(MkSources), P(MkTuning)]
     lib.mk_select_tuning.restype = _c_i32
     lib.mk_poll_error.argtypes = [_vp, P(_c_i32)]
@@ -274,6 +277,29 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
     o["workspace"] = workspace
     o["_sources"] = srcs
     return o
+
+
+def mk_dispatch_gemm_static(x: torch.Tensor, w_experts: torch.Tensor, k: int, out: dict, status: torch.Tensor, *,
+                            w_router: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                            topk_ids_in: Optional[torch.Tensor] = None, E: Optional[int] = None, e_begin: int = 0,
+                            tune: Optional[dict] = None, stream=None) -> None:
+    """mk_dispatch_gemm_static: the dispatch with the library's own device scratch instead of a workspace.
+    Every output must be given in `out` (y_perm, slot_of, expert_offsets, and optionally topk_ids, topk_w,
+    row_token); status is a device int32 tensor of at least 2 elements receiving (status, detail)."""
+    lib = load()
+    T, d = x.shape
+    E_local, N, _ = w_experts.shape
+    if E is None:
+        E = w_router.shape[1] if w_router is not None else E_local
+    shape = _shape(T, d, E, k, e_begin, E_local, N)
+    srcs = _Sources([x])
+    tu = _tuning(tune)
+    st = lib.mk_dispatch_gemm_static(ctypes.byref(shape), ctypes.byref(srcs.c), _ptr(w_router), _ptr(bias),
+                                     _ptr(topk_ids_in), _ptr(w_experts), _ptr(out["y_perm"]), _ptr(out["slot_of"]),
+                                     _ptr(out["expert_offsets"]), _ptr(out.get("topk_ids")), _ptr(out.get("topk_w")),
+                                     _ptr(out.get("row_token")), _ptr(status),
+                                     None if tu is None else ctypes.byref(tu), _stream(stream))
+    _check(st, "mk_dispatch_gemm_static")
 
 
 def mk_combine(y_perm: torch.Tensor, slot_of: torch.Tensor, topk_w: torch.Tensor, rows: Optional[int] = None,

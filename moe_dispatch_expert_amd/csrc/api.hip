@@ -4,6 +4,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/mk.h"
 #include "fused_dev.h"
@@ -12,6 +13,8 @@
 #include "mk_args.h"
 #include "mk_launch.h"
 #include "route_dev.h"
+
+static __device__ __align__(256) char scratch[MK_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -148,11 +151,13 @@ mk_status plan_call(const mk_shape *s, const mk_sources *src, const mk_tuning *t
     return MK_OK;
 }
 
-// The dispatch call (the error words stay in the workspace for mk_poll_error).
+// The dispatch call; status_out (device [2], or nullptr) receives the call's device status at its end
+// (no-allocation entry point), else the error words stay in the workspace for mk_poll_error.
 mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
                         const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
                         int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
-                        void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream)
+                        void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream,
+                        int32_t *status_out, const Plan *pre_plan)
 {
     mk_status st = check_shape(s);
     if (st != MK_OK) return st;
@@ -166,8 +171,12 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return MK_EINVAL;
     Plan plan;
-    st = plan_call(s, src, tune, plan);
-    if (st != MK_OK) return st;
+    if (pre_plan) {
+        plan = *pre_plan;
+    } else {
+        st = plan_call(s, src, tune, plan);
+        if (st != MK_OK) return st;
+    }
     const WsLayout &L = plan.L;
     if (workspace_bytes < L.total) return MK_EWORKSPACE;
     const mk_tuning &tu = plan.tu;
@@ -284,6 +293,7 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
         fa.max_tiles = L.max_tiles;
         fa.ticks_per_us = (uint32_t)ticks_per_us();
         fa.trace = (uint64_t *)(ws + L.trace);
+        fa.status_out = status_out;
         if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
         if (launch_fused(fa, grid, tu.cooperative != 0, hs) != hipSuccess) return MK_EHIP;
         if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
@@ -338,7 +348,7 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
     sa.E_local = s->E_local;
     sa.bm = tu.bm;
     if (launch_scan(sa, hs) != hipSuccess) return MK_EHIP;
-    if (s->T == 0) return MK_OK;
+    if (s->T == 0) return (status_out && launch_status(hdr, status_out, hs) != hipSuccess) ? MK_EHIP : MK_OK;
 
     SlotArgs sl{};
     sl.ids = ids;
@@ -373,9 +383,19 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
     if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
     if (launch_gemm(ga, tu.bm, tu.bn, grid, hs) != hipSuccess) return MK_EHIP;
     if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
+    if (status_out && launch_status(hdr, status_out, hs) != hipSuccess) return MK_EHIP;
     return MK_OK;
 }
 
+
+// ---------------------------------------------------------------- the library's own scratch
+
+// Device memory of the no-allocation entry point: one array per GPU the library runs on, held until the
+// process ends.  Host code never uses this name as an address (in host code it is a stand-in): it takes
+// the device address once per device from hipGetSymbolAddress and keeps that.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];
 
 }  // namespace
 
@@ -463,7 +483,42 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
                            void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream)
 {
     return dispatch_impl(s, src, w_router, bias, topk_ids_in, w_experts, y_perm, slot_of, expert_offsets,
-                         topk_ids_out, topk_w_out, row_token, workspace, workspace_bytes, tune, stream);
+                         topk_ids_out, topk_w_out, row_token, workspace, workspace_bytes, tune, stream, nullptr,
+                         nullptr);
+}
+
+mk_status mk_dispatch_gemm_static(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
+                                  const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
+                                  int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out,
+                                  int32_t *row_token, int32_t *status, const mk_tuning *tune, void *stream)
+{
+    mk_status st = check_shape(s);
+    if (st != MK_OK) return st;
+    st = check_sources(s, src);
+    if (st != MK_OK) return st;
+    if (!status || !aligned16(status)) return MK_EINVAL;
+    Plan plan;
+    st = plan_call(s, src, tune, plan);
+    if (st != MK_OK) return st;
+    if (plan.L.total > MK_STATIC_SCRATCH_BYTES) return MK_EWORKSPACE;   // before any HIP call
+    // The scratch address of the current device, taken once; at that time its barrier and error words
+    // are zeroed by a kernel on the caller's stream (the rest of the workspace is rewritten by every call).
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MK_EHIP;
+    void *ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_dev[dev]) {
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MK_EHIP;
+            if (launch_zero(ptr, plan.L.part, (hipStream_t)stream) != hipSuccess) return MK_EHIP;
+            g_scratch_dev[dev] = ptr;
+        }
+        ws = g_scratch_dev[dev];
+    }
+    return dispatch_impl(s, src, w_router, bias, topk_ids_in, w_experts, y_perm, slot_of, expert_offsets,
+                         topk_ids_out, topk_w_out, row_token, ws, MK_STATIC_SCRATCH_BYTES, tune, stream, status,
+                         &plan);
 }
 
 mk_status mk_dispatch_gemm_trace(const mk_shape *s, const mk_sources *src, size_t *offset, int32_t *n_wg,

@@ -65,6 +65,8 @@ struct FusedArgs {
     int32_t max_tiles;
     uint32_t ticks_per_us;       // wall-clock ticks per microsecond
     uint64_t *trace;             // [kTraceWGs][kTraceWords] per-workgroup phase stamps
+    int32_t *status_out;         // nullptr, or [2]: the call's (error code, detail), written by the last
+                                 // workgroup out, which then clears the workspace's error words
 };
 
 // Trace record words (wall-clock ticks unless noted), written by thread 0.
@@ -152,6 +154,12 @@ __device__ __forceinline__ void fused_exit(const FusedArgs &a, uint32_t call)
         if (n + 1u == gridDim.x) {
             __hip_atomic_store(&a.hdr->done_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.hdr->call_epoch, call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (a.status_out) {   // the acq_rel count above ordered every workgroup's error write before this
+                a.status_out[0] = (int32_t)ld_relaxed(&a.hdr->err);
+                a.status_out[1] = (int32_t)ld_relaxed(&a.hdr->err_detail);
+                __hip_atomic_store(&a.hdr->err_detail, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.hdr->err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
 }

@@ -174,7 +174,39 @@ __global__ void k_tiles(const int32_t *offsets, int32_t E_local, int32_t bm, int
     hdr->R = (uint32_t)offsets[E_local];
 }
 
+// The call status of a staged call into status[2] (error code, detail), then the workspace's error
+// words cleared (one thread); and a zero fill of n16 16-byte words (a kernel, so that a caller's graph
+// capture records no memset node).
+__global__ void k_status(WsHeader *hdr, int32_t *status)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    status[0] = (int32_t)hdr->err;
+    status[1] = (int32_t)hdr->err_detail;
+    hdr->err = 0u;
+    hdr->err_detail = 0u;
+}
+
+__global__ void k_zero(uint4 *p, size_t n16)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 // ---------------------------------------------------------------- wrappers
+
+hipError_t launch_status(WsHeader *hdr, int32_t *status, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_status, dim3(1), dim3(64), 0, s, hdr, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    const int grid = (int)std::min<size_t>((n16 + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_zero, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, (uint4 *)p, n16);
+    return hipGetLastError();
+}
 
 hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 {

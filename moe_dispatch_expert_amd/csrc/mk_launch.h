@@ -44,5 +44,8 @@ int gemm_max_grid(int bm, int bn);
 // resident together).
 hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s);
 int fused_max_grid();
+// A staged call's status into status[2], then the error words cleared; a zero fill of bytes (% 16 == 0).
+hipError_t launch_status(WsHeader *hdr, int32_t *status, hipStream_t s);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 }  // namespace mk
