@@ -35,6 +35,7 @@ namespace mk {
 constexpr int kMoveRows = 32;          // rows per mover work unit
 constexpr int kScanHalf = 8192;       // ints per LDS array in phase 3
 constexpr int kMaxScanEntries = 2 * kScanHalf; // nblk * E_local held in LDS by phase 3
+constexpr int kBaseTab = 4096;        // nblk * E_local bases kept through the GEMM (in-place path, no 3rd barrier)
 
 struct FusedArgs {
     RouterArgs ra;
@@ -168,7 +169,7 @@ __device__ __forceinline__ void fused_exit(const FusedArgs &a, uint32_t call)
 // (into LDS and, for the blocks this workgroup owns, into the workspace),
 // expert offsets and tile prefix (LDS).  The nblk*E_local counts live in two
 // LDS arrays of kScanHalf ints (entry i in cnt0[i] or cnt1[i - kScanHalf]);
-// part: 256 ints; off/toff/uoff: E_local+1 ints each.
+// part: blockDim.x ints; off/toff/uoff: E_local+1 ints each.
 struct ScanLds {
     int32_t *cnt0, *cnt1;
     __device__ __forceinline__ int32_t &operator[](int i) const
@@ -314,9 +315,11 @@ __device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, const ScanLd
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x % kWave;
     const int cpr = a.d / 8;
-    if (cpr <= 4 * kWave) move_rows<4, 8>(a, tok_lds, off[le] + q0, nrows, wave, lane);
-    else if (cpr <= 8 * kWave) move_rows<8, 4>(a, tok_lds, off[le] + q0, nrows, wave, lane);
-    else if (cpr <= 16 * kWave) move_rows<16, 2>(a, tok_lds, off[le] + q0, nrows, wave, lane);
+    // 64 registers of row data in flight per lane (eight waves per workgroup, two per SIMD: the GEMM's
+    // 128 accumulators leave 128 registers for the rest)
+    if (cpr <= 4 * kWave) move_rows<4, 4>(a, tok_lds, off[le] + q0, nrows, wave, lane);
+    else if (cpr <= 8 * kWave) move_rows<8, 2>(a, tok_lds, off[le] + q0, nrows, wave, lane);
+    else if (cpr <= 16 * kWave) move_rows<16, 1>(a, tok_lds, off[le] + q0, nrows, wave, lane);
     else
         for (int r = wave; r < nrows; r += (int)blockDim.x / kWave) {
             const int t = tok_lds[r];
@@ -375,7 +378,8 @@ __device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a)
 // LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
 template <class C>
 __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t call, char *const (&st)[4],
-                                                  const LdsStages &ls, int32_t *off, int32_t *toff, int32_t *uoff)
+                                                  const LdsStages &ls, int32_t *off, int32_t *toff, int32_t *uoff,
+                                                  int32_t *basetab)
 {
     const int w = blockIdx.x;
     if (w < kTraceWGs && (int)threadIdx.x < kTraceWords) a.trace[w * kTraceWords + threadIdx.x] = 0;   // this call's record only
@@ -403,9 +407,12 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     if (!a.ids_in) {
         const int tasks = router_tasks(a.T, a.E);
         const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-        lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * kRtLdsPerWave;   // the stage arrays are consecutive
-        static_assert(4 * kRtLdsPerWave <= 4 * 32768, "router staging fits the stage arrays");
-        for (int q = w * 4 + wave; q < tasks; q += G * 4) router_task(a.ra, q, rlds);
+        constexpr int RL = RtStage<kRtKCFused>::LDS_PER_WAVE;
+        lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * RL;   // the stage arrays are consecutive
+        static_assert(C::NW * RL <= 4 * 32768, "router staging fits the stage arrays");
+        // Task q runs on workgroup q % G, wave q / G: with at most 4 G tasks every SIMD holds one chain (a
+        // task is a chain of d / 8 dependent MFMAs, so two on one SIMD take about twice as long).
+        for (int q = wave * G + w; q < tasks; q += G * C::NW) router_task<kRtKCFused>(a.ra, q, rlds);
         trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, barrier_target(call, 1), 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
@@ -447,7 +454,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     // need no barrier after it: they find the tokens of their rows from the
     // block masks and the bases, which every workgroup holds in LDS.
     const ScanLds cnt{(int32_t *)st[0], (int32_t *)st[1]};   // nblk * E_local (<= 64 KiB)
-    int32_t *part = (int32_t *)st[2];                         // 256
+    int32_t *part = (int32_t *)st[2];                         // blockDim.x ints
     fused_scan(a, cnt, part, off, toff, uoff, wave_topk);
     if (w == 0) {
         for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
@@ -484,16 +491,31 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         }
     }
     trace_put(a, kTrSlots, now_ticks());
-    if (a.gather) {   // the GEMM reads row_token of every tile: wait for all of it
-        if (!fused_barrier(a, barrier_target(call, 3), 0x08000000u)) return;
-        trace_put(a, kTrBarC, now_ticks());
+    // The GEMM's row tokens: with a small block table each workgroup keeps the per-block bases it
+    // scanned (the stage arrays that hold them now are reused by the GEMM) and finds the tokens of its
+    // tiles from them and the block masks; otherwise it reads row_token after a barrier that publishes
+    // every workgroup's slots.
+    GemmArgs g = a.ga;
+    if (a.gather) {
+        const int nb = a.nblk * a.E_local;
+        if (nb <= kBaseTab) {
+            for (int i = threadIdx.x; i < nb; i += blockDim.x) basetab[i] = cnt[i];
+            __syncthreads();
+            g.tok_mask = a.ca.blkmask;
+            g.tok_base = basetab;
+            g.tok_off = off;
+            g.tok_nblk = a.nblk;
+        } else {
+            if (!fused_barrier(a, barrier_target(call, 3), 0x08000000u)) return;
+            trace_put(a, kTrBarC, now_ticks());
+        }
     }
 
     // ---- movers: unit u = kMoveRows ranks of one expert (tile-major, since bm % kMoveRows == 0),
     // dealt round-robin over the movers
     uint64_t n_units = 0, copy_ticks = 0, release_ticks = 0;
     if (!a.gather && w < a.n_mover) {
-        int32_t *tok_lds = (int32_t *)st[2] + 256;   // kMoveRows ints after the scan's partials
+        int32_t *tok_lds = (int32_t *)st[2] + 1024;   // kMoveRows ints after the scan's partials
         const int n_units_all = uoff[a.E_local];
         // The arrival counter of unit u's tile.
         auto unit_tile = [&](int u, int &e, int &q0, int &q1) {
@@ -542,7 +564,6 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     uint64_t n_done = 0, wait_ticks = 0;
 
     // ---- compute: per-XCD queues over chunks of CH consecutive tasks
-    const GemmArgs &g = a.ga;
     const int NB = (g.N + C::BN - 1) / C::BN;
     const int n_tasks = toff[a.E_local] * NB;
     const int xcd = w % 8;

@@ -58,6 +58,13 @@ struct GemmArgs {
     const uint16_t *x_tok;       // [T, d] token matrix (gather mode: row r is token row_token[r]), or nullptr
     const int32_t *row_token;    // [R_cap] slot -> token (gather mode)
     int32_t T;                   // rows of x_tok
+    // Gather mode with the tokens derived in place of row_token (nullptr: read row_token): the
+    // per-64-token-block expert masks [nblk, E_local], the per-block exclusive bases of every expert
+    // (LDS, same layout) and the expert offsets (LDS).
+    const uint64_t *tok_mask;
+    const int32_t *tok_base;
+    const int32_t *tok_off;
+    int32_t tok_nblk;
     const uint16_t *w;           // [E_local, N, d]
     uint16_t *y;                 // [R_cap, N]
     const int32_t *offsets;      // [E_local + 1]
@@ -385,6 +392,32 @@ struct XOffsets {
     uint32_t v[Tiles<NW>::M256::XS];
 };
 
+// The token of rank q among expert e's rows: the last block b whose base is <= q holds it (bases grow
+// by the block's count, so that block has more than q - base bits), at the (q - base)-th set bit of the
+// block's mask.
+__device__ __forceinline__ int token_of_rank(const GemmArgs &a, int e, int q)
+{
+    const int E = a.E_local;
+    int lo = 0, hi = a.tok_nblk;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tok_base[mid * E + e] <= q) lo = mid; else hi = mid;
+    }
+    uint64_t m = a.tok_mask[(size_t)lo * E + e];
+    int j = q - a.tok_base[lo * E + e];
+    int pos = 0;
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {   // select the j-th set bit: halve the window each step
+        const int c = __popcll(m & ((1ull << w) - 1ull));
+        if (j >= c) {
+            j -= c;
+            m >>= w;
+            pos += w;
+        }
+    }
+    return lo * 64 + pos;
+}
+
 template <int NW>
 __device__ __forceinline__ XOffsets<NW> x_offsets(const GemmArgs &a, const TileJob &t, int wave, int lane)
 {
@@ -397,7 +430,9 @@ __device__ __forceinline__ XOffsets<NW> x_offsets(const GemmArgs &a, const TileJ
         if (a.x_tok) {
             // Gather: row m of the tile is token row_token[row0 + m] of the token matrix; rows past the
             // tile's valid rows point past the end of the resource and read 0 without a memory access.
-            const int tok = (t.rows_valid > 0 && m < t.rows_valid) ? a.row_token[t.row0 + m] : a.T;
+            int tok = a.T;
+            if (t.rows_valid > 0 && m < t.rows_valid)
+                tok = a.tok_base ? token_of_rank(a, t.e, t.row0 - a.tok_off[t.e] + m) : a.row_token[t.row0 + m];
             o.v[i] = (uint32_t)tok * row_bytes + ch;
         } else {
             o.v[i] = (uint32_t)m * row_bytes + ch;
@@ -557,6 +592,113 @@ __device__ __forceinline__ void gemm_tile_big(const GemmArgs &a, const TileJob &
     else store_staged_tile<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
 }
 
+// Short tiles (BM <= 64: the ragged tail of an expert, every tile of a
+// decode-sized batch) do little matrix work per slab and are bound by how
+// fast a CU streams its W tile, i.e. by the bytes it has in flight.  They run
+// three stages, two slabs ahead: W of stage s in ls.p[s], x of stage s at
+// ls.p[3] + s * XSTAGE.  Otherwise the same step structure as gemm_tile_big
+// (one barrier per slab, before its last step), with the stage index held at
+// run time.  Loads of slabs past the end go to empty resources (no memory
+// access; every wave keeps the same load count), and all loads are waited for
+// before the epilogue reuses the stage arrays.
+template <class C, bool SW, class Sched>
+__device__ __forceinline__ void gemm_tile_stream(const GemmArgs &a, const TileJob &job, const XOffsets<C::NW> &xoff,
+                                                 TileJob &next, XOffsets<C::NW> &xoff_next, Sched &sc,
+                                                 const LdsStages &ls, const SlabOffsets<C::NW> &so)
+{
+    static_assert(C::BM <= 64, "three stages of x fit one 32 KiB array");
+    constexpr int S = 3;
+    constexpr int XSTAGE = (C::XB > C::XS * C::NW ? C::XB : C::XS * C::NW) * 1024;   // empty slots land inside
+    static_assert(S * XSTAGE <= 32768, "x stages");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int wn = wave % C::WN, wm = wave / C::WN;
+    const TileSrc src = tile_src(a, job);
+    const TileSrc none{make_rsrc4(a.w, 0), make_rsrc4(a.w, 0)};
+    const uint32_t *wo = so.v;
+    const uint32_t *xo = xoff.v;
+    const int KK = __builtin_amdgcn_readfirstlane(a.d / C::BK);
+
+    const lds_char_t *aw[4], *ax[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        int fo = (lane & 31) * 128 + (((2 * kk + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) << 4);
+        asm volatile("" : "+v"(fo));
+        aw[kk] = ls.p[0] + wn * (C::BN / C::WN) * 128 + fo;
+        ax[kk] = ls.p[3] + wm * (C::BM / C::WM) * 128 + fo;
+    }
+    f32x16_t acc[C::NI][C::MI];
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::MI; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    constexpr int NL = C::NS;
+    constexpr int NR = C::NI + C::MI;
+    // stage st: W at ls.p[0] + st * 32768, x at ls.p[3] + st * XSTAGE
+    auto issue = [&](int slab, int st, int i) {
+        const bool real = slab < KK;
+        dma_one<C>(real ? src.w : none.w, real ? src.x : none.x, wo, xo, i, real ? slab : 0,
+                   ls.p[0] + st * 32768, ls.p[3] + st * XSTAGE, wave);
+    };
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) issue(sl, sl, i);
+    wait_vmem<(S - 1) * NL>();   // this wave's slab 0 has landed
+    __syncthreads();
+    bf16x8_t fa0[C::NI], fb0[C::MI], fa1[C::NI], fb1[C::MI];
+    typedef __attribute__((address_space(3))) const bf16x8_t lds_frag_t;
+    // fragment q of step kk from the stage at byte offsets (wst, xst)
+    auto rd = [&](int kk, int q, int wst, int xst, bf16x8_t (&fa)[C::NI], bf16x8_t (&fb)[C::MI]) {
+        if (q < C::NI) fa[q] = *(lds_frag_t *)(aw[kk] + wst + q * 32 * 128);
+        else fb[q - C::NI] = *(lds_frag_t *)(ax[kk] + xst + (q - C::NI) * 32 * 128);
+    };
+#pragma unroll
+    for (int q = 0; q < NR; ++q) rd(0, q, 0, 0, fa0, fb0);
+    auto none_ld = [](int) {};
+    int st = 0;
+    for (int j = 0; j < KK; ++j) {
+        const int wst = __builtin_amdgcn_readfirstlane(st * 32768), xst = __builtin_amdgcn_readfirstlane(st * XSTAGE);
+        const int st1 = st == S - 1 ? 0 : st + 1;
+        mfma_step<C, NR, 0>(fa0, fb0, acc, [&](int q) { rd(1, q, wst, xst, fa1, fb1); }, none_ld);
+        mfma_step<C, NR, 0>(fa1, fb1, acc, [&](int q) { rd(2, q, wst, xst, fa0, fb0); }, none_ld);
+        mfma_step<C, NR, 0>(fa0, fb0, acc, [&](int q) { rd(3, q, wst, xst, fa1, fb1); }, none_ld);
+        if (j + 1 < KK) {
+            // slab j + 1 has landed (slab j + 2 may still be in flight) and this wave's reads of stage st are done
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((NL & 15) | ((NL >> 4) << 14) | 0x0070);   // vmcnt(NL) lgkmcnt(0)
+            __syncthreads();
+            const int wst1 = __builtin_amdgcn_readfirstlane(st1 * 32768);
+            const int xst1 = __builtin_amdgcn_readfirstlane(st1 * XSTAGE);
+            mfma_step<C, NR, NL>(fa1, fb1, acc, [&](int q) { rd(0, q, wst1, xst1, fa0, fb0); },
+                                 [&](int i) { issue(j + S, st, i); });
+        } else {
+            mfma_step<C, 0, 0>(fa1, fb1, acc, none_ld, none_ld);
+        }
+        st = st1;
+    }
+    wait_vmem_all();   // the loads past the end land in the stages the epilogue reuses
+
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::MI; ++j) asm volatile("" : "+a"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
+
+    __syncthreads();
+    stage_tile<C>(acc, ls, wave, lane);
+    next = sc.claim();
+    xoff_next = x_offsets<C::NW>(a, next, wave, lane);
+    __syncthreads();
+    if constexpr (SW) store_staged_swiglu<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
+    else store_staged_tile<C>(a, job.row0, job.rows_valid, job.n0, ls, wave, lane);
+}
+
 // A Sched made of three callables.
 template <class Cl, class Wa, class Do>
 struct LambdaSched {
@@ -586,8 +728,8 @@ __device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const Lds
         XOffsets<NW> xo_next;
         if (job.rows_valid > 128) gemm_tile_big<typename T::M256, SW>(a, job, xo, next, xo_next, sc, ls, so);
         else if (job.rows_valid > 64) gemm_tile_big<typename T::M128, SW>(a, job, xo, next, xo_next, sc, ls, so);
-        else if (job.rows_valid > 32) gemm_tile_big<typename T::M64, SW>(a, job, xo, next, xo_next, sc, ls, so);
-        else gemm_tile_big<typename T::M32, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        else if (job.rows_valid > 32) gemm_tile_stream<typename T::M64, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        else gemm_tile_stream<typename T::M32, SW>(a, job, xo, next, xo_next, sc, ls, so);
         sc.done();
         job = next;
         xo = xo_next;

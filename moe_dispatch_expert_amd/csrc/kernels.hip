@@ -78,7 +78,7 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
-    __shared__ int32_t off[1025], toff[1025], uoff[1025];
+    __shared__ int32_t off[1025], toff[1025], uoff[1025], basetab[kBaseTab];
     LdsStages ls;
     char *st[4];   // filled one by one: a constant initializer would become a static one
     for (int k = 0; k < 4; ++k) {
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
         ls.p[k] = (lds_char_t *)st[k];
     }
     const uint32_t call = fused_call_epoch(a);
-    fused_kernel_body<C>(a, call, st, ls, off, toff, uoff);
+    fused_kernel_body<C>(a, call, st, ls, off, toff, uoff, basetab);
     fused_exit(a, call);
 }
 
@@ -217,7 +217,7 @@ hipError_t launch_router(const RouterArgs &a, hipStream_t s)
 hipError_t launch_topk(const TopkArgs &ta, const CountArgs &ca, bool do_count, hipStream_t s)
 {
     // token-parallel selection, then the per-block histogram from the ids it wrote
-    hipLaunchKernelGGL(k_topk_wave, dim3(topk_wave_units(ta.T)), dim3(256), 0, s, ta);
+    hipLaunchKernelGGL(k_topk_wave, dim3(topk_wave_units(ta.T, 4)), dim3(256), 0, s, ta);
     if (!do_count) return hipGetLastError();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -279,7 +279,7 @@ hipError_t launch_tiles(const int32_t *offsets, int32_t E_local, int32_t bm, int
 }
 
 typedef Tiles<8>::M256 Tile256;       // the grouped GEMM launches: eight waves per workgroup
-typedef Tiles<4>::M256 FusedTile;     // the fused kernel: four waves per workgroup
+typedef Tiles<8>::M256 FusedTile;     // the fused kernel: eight waves per workgroup
 
 hipError_t launch_gemm(const GemmArgs &a, int bm, int bn, int grid, hipStream_t s)
 {

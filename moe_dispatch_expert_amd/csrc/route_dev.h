@@ -78,12 +78,20 @@ __device__ __forceinline__ void unpack8(const u32x4_t v, float (&f)[8])
 // of its column at a time).
 constexpr int kRtTok = 32;                    // tokens per wave task
 constexpr int kRtExp = 8;                     // experts per wave task
-constexpr int kRtKC = 128;                    // K steps per staged chunk
-constexpr int kRtWS = kRtKC + 4;              // LDS row stride of the staged weights (floats)
-constexpr int kRtXS = kRtKC + 8;              // LDS row stride of the staged x rows (bf16)
-constexpr int kRtWBuf = kRtExp * kRtWS * 4;   // bytes of one weight buffer
-constexpr int kRtXBuf = kRtTok * kRtXS * 2;   // bytes of one x buffer
-constexpr int kRtLdsPerWave = 2 * (kRtWBuf + kRtXBuf);
+
+// Staging geometry for KC K steps per chunk (128 in the router's own launch, 64 in the fused kernel,
+// whose eight waves share the GEMM's 128 KiB of stage arrays).
+template <int KC>
+struct RtStage {
+    static constexpr int WS = KC + 4;                 // LDS row stride of the staged weights (floats)
+    static constexpr int XS = KC + 8;                 // LDS row stride of the staged x rows (bf16)
+    static constexpr int WBUF = kRtExp * WS * 4;      // bytes of one weight buffer
+    static constexpr int XBUF = kRtTok * XS * 2;      // bytes of one x buffer
+    static constexpr int LDS_PER_WAVE = 2 * (WBUF + XBUF);
+};
+constexpr int kRtKC = 128;                    // K steps per staged chunk of the router launch
+constexpr int kRtKCFused = 64;                // ... of the fused kernel
+constexpr int kRtLdsPerWave = RtStage<kRtKC>::LDS_PER_WAVE;
 
 __host__ __device__ inline int router_tasks(int T, int E)
 {
@@ -95,35 +103,41 @@ typedef __attribute__((address_space(3))) char lds_byte_t;
 
 // FULL: the 8 columns exist and E % 4 == 0 (16-byte weight loads); otherwise
 // one load per column, columns past E repeating the last (never stored).
-// lds: this wave's kRtLdsPerWave bytes.
-template <bool FULL>
+// lds: this wave's RtStage<KC>::LDS_PER_WAVE bytes.
+template <bool FULL, int KC>
 __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int tb, int e0, lds_byte_t *lds)
 {
+    constexpr int kRtKC = KC;
+    constexpr int kRtWS = RtStage<KC>::WS, kRtXS = RtStage<KC>::XS;
+    constexpr int kRtWBuf = RtStage<KC>::WBUF, kRtXBuf = RtStage<KC>::XBUF;
     typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
     typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
     const int lane = threadIdx.x % kWave;
     const int seg = a.d / kRouterSegments;   // a multiple of 16 (d % 128 == 0)
     const int nch = (seg + kRtKC - 1) / kRtKC;
     const int eb = 4 * (lane >> 5) + (lane & 3);   // this lane's B column in the group
-    // x staging: lane l loads rows 4 i + l / 16 (i < 8), 16 bytes at piece l % 16 of the chunk's 256 bytes.
-    const uint16_t *xrow[8];
+    // x staging: a chunk row is KC / 8 pieces of 16 bytes; lane l loads rows XR i + l / XP (i < 32 / XR),
+    // piece l % XP, with XP = KC / 8 pieces per row and XR = 64 / XP rows per load.
+    constexpr int XP = kRtKC / 8, XR = kWave / XP, XI = kRtTok / XR;
+    const uint16_t *xrow[XI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        xrow[i] = token_row(a.src, min(tb * kRtTok + 4 * i + (lane >> 4), a.T - 1), a.d) + (size_t)s * seg +
-                  8 * (lane & 15);
-    // Weight staging: lane l loads rows (l / 2) + 32 i (i < 4) of a chunk, columns 4 (l % 2) .. + 3.
+    for (int i = 0; i < XI; ++i)
+        xrow[i] = token_row(a.src, min(tb * kRtTok + XR * i + lane / XP, a.T - 1), a.d) + (size_t)s * seg +
+                  8 * (lane % XP);
+    // Weight staging: lane l loads rows (l / 2) + 32 i (i < KC / 32) of a chunk, columns 4 (l % 2) .. + 3.
     const int c0 = min(4 * (lane & 1), a.E - 1 - e0);
     const int clast = a.E - 1 - e0 - c0;
     const float *wsrc = a.wr + (size_t)s * seg * a.E + e0 + c0;
+    constexpr int WI = kRtKC / 32;
     struct Regs {
-        u32x4_t x[8];
-        f32x4_t w[4];
+        u32x4_t x[XI];
+        f32x4_t w[WI];
     };
     // Chunk c into registers (past the end: the last chunk again; steps past the segment: clamped).
     auto fetch = [&](int c, Regs &r) {
         const int cc = min(c, nch - 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < WI; ++i) {
             const int row = min(cc * kRtKC + (lane >> 1) + 32 * i, seg - 1);
             const float *q = wsrc + (size_t)row * a.E;
             if (FULL) {
@@ -133,22 +147,22 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
                 for (int j = 0; j < 4; ++j) r.w[i][j] = q[min(j, clast)];
             }
         }
-        const int k0 = min(cc * kRtKC + 8 * (lane & 15), seg - 8) - 8 * (lane & 15);
+        const int k0 = min(cc * kRtKC + 8 * (lane % XP), seg - 8) - 8 * (lane % XP);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r.x[i] = *(const u32x4_t *)(xrow[i] + k0);
+        for (int i = 0; i < XI; ++i) r.x[i] = *(const u32x4_t *)(xrow[i] + k0);
     };
     auto wbuf = [&](int c) { return (lds_float_t *)(lds + (c & 1) * kRtWBuf); };
     auto xbuf = [&](int c) { return lds + 2 * kRtWBuf + (c & 1) * kRtXBuf; };
     auto stash = [&](const Regs &r, int c) {
         lds_float_t *wb = wbuf(c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WI; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) wb[(4 * (lane & 1) + j) * kRtWS + (lane >> 1) + 32 * i] = r.w[i][j];
         lds_byte_t *xb = xbuf(c);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *(lds_u32x4_t *)(xb + ((4 * i + (lane >> 4)) * kRtXS + 8 * (lane & 15)) * 2) = r.x[i];
+        for (int i = 0; i < XI; ++i)
+            *(lds_u32x4_t *)(xb + ((XR * i + lane / XP) * kRtXS + 8 * (lane % XP)) * 2) = r.x[i];
     };
     Regs r;
     fetch(0, r);
@@ -193,6 +207,7 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
 
 // Wave task q (< router_tasks(T, E)); q uniform over the wave.  Task numbers
 // run expert group fastest, so the waves of a workgroup share token rows.
+template <int KC = kRtKC>
 __device__ __forceinline__ void router_task(const RouterArgs &a, int q, lds_byte_t *lds)
 {
     const int neg = (a.E + kRtExp - 1) / kRtExp;
@@ -200,8 +215,8 @@ __device__ __forceinline__ void router_task(const RouterArgs &a, int q, lds_byte
     const int eg = __builtin_amdgcn_readfirstlane(q % neg);
     const int tb = __builtin_amdgcn_readfirstlane((q / neg) % ntb);
     const int s = __builtin_amdgcn_readfirstlane(q / (neg * ntb));
-    if (a.E % 4 == 0 && eg * kRtExp + kRtExp <= a.E) router_task_body<true>(a, s, tb, eg * kRtExp, lds);
-    else router_task_body<false>(a, s, tb, eg * kRtExp, lds);
+    if (a.E % 4 == 0 && eg * kRtExp + kRtExp <= a.E) router_task_body<true, KC>(a, s, tb, eg * kRtExp, lds);
+    else router_task_body<false, KC>(a, s, tb, eg * kRtExp, lds);
 }
 
 struct TopkArgs {
@@ -294,28 +309,40 @@ __device__ __forceinline__ void topk_select(const TopkArgs &a, int t, const Topk
     }
 }
 
-// Token-per-wave top-k: workgroup unit u covers tokens 4u .. 4u+3, one per wave.
-__host__ __device__ inline int topk_wave_units(int T) { return (T + 3) / 4; }
+// Token-per-wave top-k: workgroup unit u of W waves covers tokens W u .. W u + W - 1, one per wave.
+__host__ __device__ inline int topk_wave_units(int T, int waves) { return (T + waves - 1) / waves; }
 
-// Units u0, u0 + stride, ... (< topk_wave_units(T)) of one workgroup, the next
-// token's partials in flight while the current one is selected.
+// Units u0, u0 + stride, ... (< topk_wave_units(T, W)) of one workgroup.  For E <= 256 the next
+// token's partials are in flight while the current one is selected; larger E holds one token's
+// partials only (their registers would not leave room for a second wave per SIMD in the fused kernel).
 template <int NV>
 __device__ __forceinline__ void topk_wave_units_nv(const TopkArgs &a, int u0, int stride)
 {
+    const int W = (int)blockDim.x / kWave;
     const int wave = (int)threadIdx.x / kWave;
-    const int units = topk_wave_units(a.T);
-    int t = u0 * 4 + wave;
+    const int units = topk_wave_units(a.T, W);
+    int t = u0 * W + wave;
     if (u0 >= units || t >= a.T) return;
-    TopkPartials<NV> cur, nxt;
-    topk_load<NV>(a, t, cur);
-    for (int u = u0; u < units; u += stride) {
-        const int tn = (u + stride) * 4 + wave;
-        const bool more = u + stride < units && tn < a.T;
-        if (more) topk_load<NV>(a, tn, nxt);
-        topk_select<NV>(a, t, cur);
-        if (!more) break;
-        cur = nxt;
-        t = tn;
+    if constexpr (NV <= 4) {
+        TopkPartials<NV> cur, nxt;
+        topk_load<NV>(a, t, cur);
+        for (int u = u0; u < units; u += stride) {
+            const int tn = (u + stride) * W + wave;
+            const bool more = u + stride < units && tn < a.T;
+            if (more) topk_load<NV>(a, tn, nxt);
+            topk_select<NV>(a, t, cur);
+            if (!more) break;
+            cur = nxt;
+            t = tn;
+        }
+    } else {
+        for (int u = u0; u < units; u += stride) {
+            const int tt = u * W + wave;
+            if (tt >= a.T) break;
+            TopkPartials<NV> cur;
+            topk_load<NV>(a, tt, cur);
+            topk_select<NV>(a, tt, cur);
+        }
     }
 }
 
