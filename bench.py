@@ -4,7 +4,11 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral] [--seed
 
 One step = one mk_dispatch_gemm call over one batch of synthetic input
 (routing, histogram, offsets, slots, row scatter, grouped GEMM), inputs
-resident in HBM before the timed region.  Prints one JSON line:
+resident in HBM before the timed region.  Prints one JSON line for the named
+workload (default the Mixtral-shaped one) with, on the default run, two
+sub-records of the same form: "decode" (the weight-streaming bound share,
+roofline in HBM GB/s) and "wide_ep" (rows arriving from eight simulated peers,
+with the overlap efficiency against the serial sum).  Fields:
   value          whole-step TFLOP/s, 2*R*d*N flops per step (R = routed local rows)
   roofline       the dominant kernel's launch (the fused kernel, or with
                  --staged the grouped GEMM), timed with HIP events the library
@@ -230,26 +234,31 @@ def time_combine(bufs: dict, R: int, steps: int, warmup: int) -> dict:
             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int, x_dev, w_experts) -> dict:
-    """The expert FFN after the step, its y_perm read as [gate | up] (F = N / 2): mk_swiglu, then the
-    down-projection mk_grouped_gemm with a seeded W_down [E_local, d, F] ~ N(0, 1/F).  Also the gate|up
-    GEMM over the permuted rows both ways: mk_grouped_gemm + mk_swiglu, and mk_grouped_gemm_swiglu
-    (SwiGLU in the GEMM's epilogue).  Each timed K times between two events on the current stream."""
+def time_ffn(case, R: int, steps: int, warmup: int, ms_step: float) -> dict:
+    """The expert FFN over the dispatch's own layout, the workload's expert weights read as [gate | up]
+    (F = N / 2), each part timed K times between two events on the current stream:
+      dispatch_swiglu       mk_dispatch_gemm_swiglu: the whole step with SwiGLU in the GEMM epilogue, h [R, F]
+      dispatch_then_swiglu  the step (mk_dispatch_gemm, timed above) plus mk_swiglu over its y_perm
+      swiglu                mk_swiglu alone
+      down                  the down-projection mk_grouped_gemm over h, seeded W_down [E_local, d, F] ~ N(0, 1/F)"""
     import torch
     import moe_dispatch_expert_amd as mk
-    y = bufs["y_perm"]
+    wl = case.wl
+    y = case.bufs["y_perm"]
     F = wl.N // 2
-    if wl.N % 2 or F % 128:
-        return {"skipped": f"F = N / 2 = {wl.N / 2} is not a multiple of 128"}
-    g = torch.Generator().manual_seed(seed * 1000 + 5)
+    if wl.N % 16:
+        return {"skipped": f"F = N / 2 = {wl.N / 2} is not a multiple of 8"}
+    g = torch.Generator().manual_seed(case.seed * 1000 + 5)
     wd = torch.empty(wl.E_local, wl.d, F, dtype=torch.bfloat16)
     for e in range(wl.E_local):
         wd[e] = (torch.randn(wl.d, F, generator=g) / F ** 0.5).to(torch.bfloat16)
     wd = wd.to(y.device)
     h = torch.empty(y.shape[0], F, dtype=torch.bfloat16, device=y.device)
+    h2 = torch.empty_like(h)
     z = torch.empty(y.shape[0], wl.d, dtype=torch.bfloat16, device=y.device)
-    ws = torch.empty(mk.mk_grouped_gemm_workspace_bytes(wl.E_local), dtype=torch.uint8, device=y.device)
-    off = bufs["expert_offsets"]
+    gws = torch.empty(mk.mk_grouped_gemm_workspace_bytes(wl.E_local), dtype=torch.uint8, device=y.device)
+    off = case.bufs["expert_offsets"]
+    out_h = dict(case.bufs, y_perm=h)
 
     def timed(fn):
         for _ in range(warmup):
@@ -263,30 +272,27 @@ def time_ffn(bufs: dict, R: int, wl, seed: int, steps: int, warmup: int, x_dev, 
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    ms_act = timed(lambda: mk.mk_swiglu(y, rows=R, out=h))
-    ms_down = timed(lambda: mk.mk_grouped_gemm(h, off, wd, out=z, workspace=ws))
-    a = x_dev[bufs["row_token"][:R].long()].contiguous()   # the permuted rows (gathered outside the timing)
-    gu = torch.empty(R, wl.N, dtype=torch.bfloat16, device=y.device)
-    h2 = torch.empty(R, F, dtype=torch.bfloat16, device=y.device)
-    ms_sep = timed(lambda: (mk.mk_grouped_gemm(a, off, w_experts, out=gu, workspace=ws),
-                            mk.mk_swiglu(gu, rows=R, out=h2)))
-    ms_fused = timed(lambda: mk.mk_grouped_gemm_swiglu(a, off, w_experts, out=h2, workspace=ws))
+    ms_dsw = timed(lambda: case.call(out=out_h, swiglu=True))
+    st, detail = mk.mk_poll_error(case.ws)
+    if st != mk.MK_OK:
+        raise SystemExit(f"device error {mk.mk_status_str(st)} ({detail})")
+    ms_act = timed(lambda: mk.mk_swiglu(y, rows=R, out=h2))
+    ms_down = timed(lambda: mk.mk_grouped_gemm(h, off, wd, out=z, workspace=gws))
     gu_flops = 2.0 * R * wl.d * wl.N
     act_bytes = R * 3 * F * 2
-    flops = 2.0 * R * F * wl.d
+    down_flops = 2.0 * R * F * wl.d
+    tf = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 2)
     return {"F": F,
+            "dispatch_swiglu": {"kernel": "k_fused (SwiGLU epilogue)", "ms": round(ms_dsw, 4), "flops": gu_flops,
+                                "TFLOP/s": tf(gu_flops, ms_dsw),
+                                "frac": round(tf(gu_flops, ms_dsw) / PEAK_BF16_TFLOPS, 4)},
+            "dispatch_then_swiglu": {"kernels": "k_fused + k_swiglu", "ms": round(ms_step + ms_act, 4),
+                                     "TFLOP/s": tf(gu_flops, ms_step + ms_act)},
             "swiglu": {"kernel": "k_swiglu", "ms": round(ms_act, 4), "alg_bytes": act_bytes,
                        "achieved": round(act_bytes / (ms_act * 1e-3) / 1e9, 1), "unit": "GB/s",
                        "frac": round(act_bytes / (ms_act * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "down": {"kernel": "k_gemm", "ms": round(ms_down, 4), "flops": flops,
-                     "achieved": round(flops / (ms_down * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                     "frac": round(flops / (ms_down * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-            "gate_up_then_swiglu": {"kernels": "k_gemm + k_swiglu", "ms": round(ms_sep, 4), "flops": gu_flops,
-                                    "achieved": round(gu_flops / (ms_sep * 1e-3) / 1e12, 2), "unit": "TFLOP/s"},
-            "gate_up_swiglu_fused": {"kernel": "k_gemm (SwiGLU epilogue)", "ms": round(ms_fused, 4),
-                                     "flops": gu_flops,
-                                     "achieved": round(gu_flops / (ms_fused * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                                     "frac": round(gu_flops / (ms_fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+            "down": {"kernel": "k_gemm", "ms": round(ms_down, 4), "flops": down_flops,
+                     "TFLOP/s": tf(down_flops, ms_down), "frac": round(tf(down_flops, ms_down) / PEAK_BF16_TFLOPS, 4)}}
 
 
 def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
@@ -316,6 +322,175 @@ def cpu_baseline(inp, R_gpu: int, budget_s: float = 12.0) -> dict:
             "routed_rows_per_s": R / t_full, "matches_gpu_R": R == R_gpu}
 
 
+def _roofline(flops: float, alg_bytes: float, launch_all, kernel: str, traffic) -> dict:
+    """Roofline record of one launch kind: which roof bounds it (flops per algorithmic byte against the ridge
+    point), what it achieved over the mean event-timed launch, and the spread of launch times."""
+    ms = float(np.mean(launch_all))
+    if flops / max(alg_bytes, 1) >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        tf = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    else:
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel": kernel, "launch_ms": round(ms, 4),
+                 "launch_ms_p10_p50_p90": [round(float(v), 4) for v in np.percentile(launch_all, [10, 50, 90])],
+                 "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes})
+    return roof
+
+
+class Case:
+    """One workload resident on the GPU: inputs, outputs, workspace, and a timed loop of mk_dispatch_gemm."""
+
+    def __init__(self, wl, seed: int, base_tune: dict, inp=None):
+        import torch
+        import moe_dispatch_expert_amd as mk
+        import workloads as W
+        self.wl, self.mk, self.torch, self.seed = wl, mk, torch, seed
+        self.inp = inp if inp is not None else W.make_inputs(wl, seed)
+        dev = self.dev = torch.device("cuda:0")
+        x = self.inp["x"]
+        self.xs = ([x[s * wl.rows_per_src:(s + 1) * wl.rows_per_src].contiguous().to(dev) for s in range(wl.S)]
+                   if wl.S > 1 else x.to(dev))
+        self.wr = self.inp["w_router"].to(dev)
+        self.bias = None if self.inp["bias"] is None else self.inp["bias"].to(dev)
+        self.we = self.inp["w_experts"].to(dev)
+        self.ids_in = None
+        if wl.route_outside:   # the sources route their own tokens before the payload arrives (untimed)
+            parts = [mk.mk_route_topk(self.xs[s], self.wr, wl.k)[0] for s in range(wl.S)]
+            self.ids_in = torch.cat(parts).contiguous()
+        self.base_tune = dict(base_tune)
+        self.arrivals = None
+        self.ws = torch.zeros(mk.mk_dispatch_gemm_workspace_bytes(
+            wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, wl.S, tune=self.base_tune), dtype=torch.uint8,
+            device=dev)
+        out = self._call(None, None)
+        self.bufs = {k: out[k] for k in ("y_perm", "slot_of", "expert_offsets", "topk_ids", "topk_w", "row_token")}
+        self.epoch = 1
+
+    def with_arrivals(self, delays_us):
+        """From now on every call models arriving rows: chunk flags released by the kernel's arrival simulator
+        sim_delay_us[c] microseconds after the launch starts (flags only: the rows are already resident).
+        Each call uses the next epoch, so no flag needs clearing between calls."""
+        torch, wl = self.torch, self.wl
+        n = wl.S * (-(-wl.rows_per_src // wl.chunk_rows))
+        self.arrivals = {"ready": torch.zeros(n, dtype=torch.int32, device=self.dev),
+                         "delays": delays_us.to(self.dev)}
+        tu = dict(self.base_tune)
+        self.ws = torch.zeros(self.mk.mk_dispatch_gemm_workspace_bytes(
+            wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, wl.S, chunk_rows=wl.chunk_rows, tune=tu),
+            dtype=torch.uint8, device=self.dev)
+        return self
+
+    def _call(self, ev_begin, ev_end, out=None, swiglu=False):
+        wl, mk = self.wl, self.mk
+        tune = dict(self.base_tune)
+        if ev_begin is not None:
+            tune.update({"ev_gemm_begin": ev_begin, "ev_gemm_end": ev_end})
+        kw = {}
+        if self.arrivals is not None:
+            self.epoch += 1
+            kw = dict(chunk_rows=wl.chunk_rows, chunk_ready=self.arrivals["ready"], epoch=self.epoch,
+                      sim_delay_us=self.arrivals["delays"])
+        return mk.mk_dispatch_gemm(self.xs, self.we, wl.k, w_router=self.wr, bias=self.bias, topk_ids_in=self.ids_in,
+                                   E=wl.E, e_begin=wl.e_begin, workspace=self.ws,
+                                   out=out if out is not None else getattr(self, "bufs", None), tune=tune,
+                                   swiglu=swiglu, **kw)
+
+    def call(self, out=None, swiglu=False):
+        """One untimed call (out: other output buffers; swiglu: the gate|up reading of the weights)."""
+        return self._call(None, None, out, swiglu)
+
+    def run(self, steps: int, warmup: int, evict_mall: bool = False) -> dict:
+        """W untimed calls, then K timed calls between two events (step time), each call's GEMM launch also
+        between the library's own events on its stream (launch time)."""
+        torch, mk = self.torch, self.mk
+        hip = _hip()
+        evs = _events(hip, 2 * steps)
+        for _ in range(warmup):
+            self._call(None, None)
+        torch.cuda.synchronize()
+        st, detail = mk.mk_poll_error(self.ws)
+        if st != mk.MK_OK:
+            raise SystemExit(f"device error {mk.mk_status_str(st)} ({detail})")
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        scratch = torch.ones(1 << 30, dtype=torch.uint8, device=self.dev) if evict_mall else None
+        torch.cuda.synchronize()
+        t_start.record()
+        for i in range(steps):
+            if scratch is not None:   # read, not write: evicted lines are clean, so no write-back lands in the step
+                scratch.sum(dtype=torch.int64)
+            self._call(evs[2 * i], evs[2 * i + 1])
+        t_end.record()
+        torch.cuda.synchronize()
+        st, detail = mk.mk_poll_error(self.ws)
+        if st != mk.MK_OK:
+            raise SystemExit(f"device error {mk.mk_status_str(st)} ({detail})")
+        launch_all = [_elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+        for e in evs:
+            hip.hipEventDestroy(e)
+        ms_step = t_start.elapsed_time(t_end) / steps
+        if scratch is not None:   # the evicting reads sit between the steps: time the launches only
+            ms_step = float(np.mean(launch_all))
+        wl = self.wl
+        R = int(self.bufs["expert_offsets"][-1].item())
+        hit = int((torch.diff(self.bufs["expert_offsets"]) > 0).sum())
+        alg_bytes = (hit * wl.N * wl.d * 2 + R * wl.N * 2      # weights of hit experts, y_perm
+                     + wl.T * wl.d * 2 + (0 if self.ids_in is not None else wl.d * wl.E * 4))
+        return {"ms_step": ms_step, "launch_all": launch_all, "R": R, "flops": 2.0 * R * wl.d * wl.N,
+                "alg_bytes": alg_bytes}
+
+
+def decode_record(seed: int, steps: int, warmup: int) -> dict:
+    """Decode-shaped share (T=128, d=7168, 32 local of 256 experts, top-8, N=2048), routing inside the step:
+    weight-streaming bound, so its roofline is HBM bytes (weights of the hit experts, x, router weights,
+    y_perm) over the event-timed fused launch."""
+    import workloads as W
+    c = Case(W.WORKLOADS["decode"], seed, {})
+    m = c.run(steps, warmup)
+    roof = _roofline(m["flops"], m["alg_bytes"], m["launch_all"], "fused dispatch+GEMM (k_fused)",
+                     _traffic("fused", "decode"))
+    return {"workload": "decode", "R": m["R"], "ms_per_step": round(m["ms_step"], 4),
+            "tokens_per_s": c.wl.T / (m["ms_step"] * 1e-3), "roofline": roof}
+
+
+def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
+    """One GPU's share of a wide EP layer (8 sources x 2048 rows, d=7168, 32 local of 256 experts, top-8,
+    N=2048), ids routed by the sources (untimed), rows arriving in chunks of 128 whose ready flags the
+    kernel's arrival simulator releases at seeded U[0, 100] us delays.  Overlap efficiency = (last arrival
+    + the grouped GEMM alone on the same layout) / the fused launch: above 1 when the GEMM runs while rows
+    are still arriving."""
+    import workloads as W
+    wl = W.WORKLOADS["wide_ep"]
+    inp = W.make_inputs(wl, seed)
+    delays = inp["delays_us"]
+    fused = Case(wl, seed, {}, inp=inp).with_arrivals(delays)
+    mf = fused.run(steps, warmup)
+    del fused
+    resident = Case(wl, seed, {}, inp=inp)
+    mr = resident.run(steps, warmup)
+    del resident
+    staged = Case(wl, seed, {"n_mover_wg": -1}, inp=inp)
+    ms = staged.run(steps, warmup)
+    del staged
+    fused_ms = float(np.mean(mf["launch_all"]))
+    gemm_ms = float(np.mean(ms["launch_all"]))
+    arrival_ms = float(delays.max()) * 1e-3
+    roof = _roofline(mf["flops"], mf["alg_bytes"], mf["launch_all"], "fused dispatch+GEMM (k_fused), arrivals",
+                     _traffic("fused", "wide_ep"))
+    return {"workload": "wide_ep", "R": mf["R"], "ms_per_step": round(mf["ms_step"], 4),
+            "tflops_step": round(mf["flops"] / (mf["ms_step"] * 1e-3) / 1e12, 2),
+            "arrivals": f"{delays.numel()} chunks of {wl.chunk_rows} rows, flags released at seeded U[0,100] us "
+                        f"(last at {float(delays.max()):.0f} us), rows already resident",
+            "roofline": roof,
+            "fused_all_resident_launch_ms": round(float(np.mean(mr["launch_all"])), 4),
+            "gemm_alone_launch_ms": round(gemm_ms, 4),
+            "last_arrival_ms": round(arrival_ms, 4),
+            "serial_sum_ms": round(arrival_ms + gemm_ms, 4),
+            "overlap_efficiency": round((arrival_ms + gemm_ms) / fused_ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,9 +499,12 @@ def main():
     ap.add_argument("--workload", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="time the named workload only (no decode / wide_ep sub-records)")
     ap.add_argument("--trace", action="store_true", help="add the fused kernel's phase timeline of the last step")
     ap.add_argument("--staged", action="store_true", help="one launch per step instead of the fused kernel")
     ap.add_argument("--movers", type=int, default=0, help="override the per-shape mover count")
+    ap.add_argument("--compute-wg", type=int, default=0, help="override the per-shape compute workgroup count")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     ap.add_argument("--write-traffic", default="", metavar="DIR",
@@ -336,8 +514,9 @@ def main():
                     help="read 1 GiB before every step (outside the launch events) so no input is left in the "
                          "256 MiB Infinity Cache; value and roofline then come from the launch events")
     ap.add_argument("--ffn", action="store_true",
-                    help="also time the expert FFN after the step (its y_perm read as [gate | up], F = N / 2): "
-                         "mk_swiglu and the down-projection mk_grouped_gemm (reported apart, not in value)")
+                    help="also time the expert FFN over the step's layout (the expert weights read as [gate | up], "
+                         "F = N / 2): mk_dispatch_gemm_swiglu, mk_swiglu, and the down-projection mk_grouped_gemm "
+                         "(reported apart, not in value)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time the dense library GEMM (torch linear) of the workload's expert shape and exit")
     ap.add_argument("--combine", action="store_true",
@@ -362,115 +541,60 @@ def main():
     if args.library_gemm:
         library_gemm(wl, args.steps, args.warmup)
         return
-    inp = W.make_inputs(wl, args.seed)
-    dev = torch.device("cuda:0")
-    x = inp["x"]
-    xs = ([x[s * wl.rows_per_src:(s + 1) * wl.rows_per_src].contiguous().to(dev) for s in range(wl.S)]
-          if wl.S > 1 else x.to(dev))
-    wr = inp["w_router"].to(dev)
-    bias = None if inp["bias"] is None else inp["bias"].to(dev)
-    we = inp["w_experts"].to(dev)
-    ids_in = None
-    if wl.route_outside:   # the sources route their own tokens before the payload arrives (untimed)
-        parts = [mk.mk_route_topk(xs[s], wr, wl.k)[0] for s in range(wl.S)]
-        ids_in = torch.cat(parts).contiguous()
     base_tune = {}
     if args.staged:
         base_tune["n_mover_wg"] = mk.MK_MOVERS_STAGED
     elif args.movers:
         base_tune["n_mover_wg"] = args.movers
-    ws = torch.zeros(mk.mk_dispatch_gemm_workspace_bytes(wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N,
-                                                         wl.S, tune=base_tune), dtype=torch.uint8, device=dev)
-    out = mk.mk_dispatch_gemm(xs, we, wl.k, w_router=wr, bias=bias, topk_ids_in=ids_in, E=wl.E,
-                              e_begin=wl.e_begin, workspace=ws, tune=base_tune)
-    bufs = {k: out[k] for k in ("y_perm", "slot_of", "expert_offsets", "topk_ids", "topk_w", "row_token")}
-    hip = _hip()
-    evs = _events(hip, 2 * args.steps)
-
-    def step(i=None):
-        tune = dict(base_tune)
-        if i is not None:
-            tune.update({"ev_gemm_begin": evs[2 * i], "ev_gemm_end": evs[2 * i + 1]})
-        mk.mk_dispatch_gemm(xs, we, wl.k, w_router=wr, bias=bias, topk_ids_in=ids_in, E=wl.E,
-                            e_begin=wl.e_begin, workspace=ws, out=bufs, tune=tune)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    st, detail = mk.mk_poll_error(ws)
-    if st != mk.MK_OK:
-        raise SystemExit(f"device error {mk.mk_status_str(st)} ({detail})")
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    scratch = torch.ones(1 << 30, dtype=torch.uint8, device=dev) if args.evict_mall else None
-    t_start.record()
-    for i in range(args.steps):
-        if scratch is not None:   # read, not write: evicted lines are clean, so no write-back lands in the step
-            scratch.sum(dtype=torch.int64)
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    launch_all = [_elapsed_ms(hip, evs[2 * i], evs[2 * i + 1]) for i in range(args.steps)]
-    gemm_ms = float(np.mean(launch_all))
-    if scratch is not None:   # the evicting writes sit between the steps: time the launches only
-        ms_step = gemm_ms
-        del scratch
-    for e in evs:
-        hip.hipEventDestroy(e)
-
-    R = int(bufs["expert_offsets"][-1].item())
-    flops = 2.0 * R * wl.d * wl.N
+    if args.compute_wg:
+        base_tune["n_compute_wg"] = args.compute_wg
+    case = Case(wl, args.seed, base_tune)
+    if wl.chunk_rows > 0 and not args.staged:   # rows arriving in chunks, flags released at seeded delays
+        case.with_arrivals(case.inp["delays_us"])
+    m = case.run(args.steps, args.warmup, args.evict_mall)
+    ms_step, R, flops = m["ms_step"], m["R"], m["flops"]
     tflops = flops / (ms_step * 1e-3) / 1e12
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    counts = torch.diff(bufs["expert_offsets"]).cpu()
-    hit = int((counts > 0).sum())
-    alg_bytes = (hit * wl.N * wl.d * 2 + R * wl.N * 2      # weights of hit experts, y_perm
-                 + wl.T * wl.d * 2 + (0 if ids_in is not None else wl.d * wl.E * 4))
     kernel = "gemm" if args.staged else "fused"
-    traffic = _traffic(kernel, args.workload) if not args.movers else None
-    # Which roof bounds the GEMM launch: flops per algorithmic byte against the ridge point.
-    if flops / max(alg_bytes, 1) >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)}
-    else:
-        gbs = alg_bytes / (gemm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": traffic,
-                 "kernel": "grouped expert GEMM (k_gemm)" if args.staged else "fused dispatch+GEMM (k_fused)",
-                 "launch_ms": round(gemm_ms, 4),
-                 "launch_ms_p10_p50_p90": [round(float(v), 4) for v in np.percentile(launch_all, [10, 50, 90])],
-                 "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes})
+    traffic = _traffic(kernel, args.workload) if not (args.movers or args.compute_wg) else None
+    roof = _roofline(flops, m["alg_bytes"], m["launch_all"],
+                     "grouped expert GEMM (k_gemm)" if args.staged else "fused dispatch+GEMM (k_fused)", traffic)
     rec = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "T": wl.T, "d": wl.d, "E": wl.E, "k": wl.k, "N": wl.N,
                    "E_local": wl.E_local, "e_begin": wl.e_begin, "sources": wl.S, "R": R, "seed": args.seed,
-                   "routing": "by the sources (untimed)" if ids_in is not None else "inside the step"},
+                   "routing": "by the sources (untimed)" if case.ids_in is not None else "inside the step",
+                   "arrivals": ("chunk flags at seeded U[0,100] us delays" if case.arrivals is not None
+                                else "all rows resident")},
         "mfma_frac_step": round(tflops / PEAK_BF16_TFLOPS, 4),
         "routed_rows_per_s": R / (ms_step * 1e-3), "tokens_per_s": wl.T / (ms_step * 1e-3),
-        "hbm_GBs_step_alg": alg_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_GBs_step_alg": m["alg_bytes"] / (ms_step * 1e-3) / 1e9,
         "roofline": roof,
         "torch": torch.__version__,
     }
-    if args.staged or args.movers:
-        rec["config"]["path"] = "staged" if args.staged else f"fused, {args.movers} movers"
+    if args.staged or args.movers or args.compute_wg:
+        rec["config"]["path"] = ("staged" if args.staged else "fused") + (
+            f", {args.movers} movers" if args.movers else "") + (
+            f", {args.compute_wg} compute workgroups" if args.compute_wg else "")
     if args.evict_mall:
         rec["config"]["mall"] = "1 GiB read before every step; step time = launch time"
     if args.trace and not args.staged:
-        rec["trace"] = trace_summary(mk.mk_dispatch_gemm_trace(ws, wl.T, wl.d, wl.E, wl.k, wl.e_begin,
+        rec["trace"] = trace_summary(mk.mk_dispatch_gemm_trace(case.ws, wl.T, wl.d, wl.E, wl.k, wl.e_begin,
                                                                wl.E_local, wl.N, wl.S))
     if args.combine:
-        rec["combine"] = time_combine(bufs, R, args.steps, args.warmup)
+        rec["combine"] = time_combine(case.bufs, R, args.steps, args.warmup)
     if args.ffn:
-        rec["ffn"] = time_ffn(bufs, R, wl, args.seed, args.steps, args.warmup,
-                              xs if wl.S == 1 else torch.cat(xs), we)
+        rec["ffn"] = time_ffn(case, R, args.steps, args.warmup, ms_step)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, R)
+        rec["cpu_baseline"] = cpu_baseline(case.inp, R)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)
+    del case
+    if not args.no_sub and not (args.staged or args.movers or args.compute_wg) and args.workload == "mixtral":
+        torch.cuda.empty_cache()
+        rec["decode"] = decode_record(args.seed, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        rec["wide_ep"] = wide_ep_record(args.seed, args.steps, args.warmup)
     print(json.dumps(rec), flush=True)
 
 

@@ -68,7 +68,9 @@ typedef struct {
      * If sim_payload is also non-NULL (HOST array of S device pointers, same
      * shape as x), that workgroup first copies the chunk from sim_payload[s]
      * into x[s] (which must then be writable), so a read before the release
-     * sees whatever x held before the call. */
+     * sees whatever x held before the call.  The simulator holds at most
+     * 16384 chunks (S * ceil(rows_per_src / chunk_rows)); more is
+     * MK_EUNSUPPORTED. */
     const uint32_t *sim_delay_us;
     const void *const *sim_payload;
 } mk_sources;
@@ -121,12 +123,14 @@ typedef struct {
  * this library's readings.
  *   x         [T, d] bf16          w_router [d, E] fp32     bias [E] fp32 or NULL
  *   topk_ids  [T, k] int32 (out)   topk_w   [T, k] fp32 (out, may be NULL)
+ *   logits    [T, E] fp32 (out, may be NULL): every logit as it entered the
+ *             selection (the ordered sum above, bias included), for checking
  *   workspace mk_route_topk_workspace_bytes(T, E) bytes, any contents.
  * T == 0 is a no-op returning MK_OK. */
 size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E);
 mk_status mk_route_topk(const void *x, const float *w_router, const float *bias,
                         int32_t T, int32_t d, int32_t E, int32_t k,
-                        int32_t *topk_ids, float *topk_w,
+                        int32_t *topk_ids, float *topk_w, float *logits,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace mk_dispatch_gemm needs for this shape, sources and tuning
@@ -178,6 +182,29 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src,
                            int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
                            void *workspace, size_t workspace_bytes,
                            const mk_tuning *tune, void *stream);
+
+/* mk_dispatch_gemm with the expert FFN's gate|up weights and the SwiGLU of
+ * mk_swiglu in the GEMM's epilogue, so the first half of the expert FFN runs
+ * over the dispatch's own layout in the same launch.  The pages name the MoE
+ * Dispatch+GEMM kernel (zubnet.ai, paragraph 2), whose experts in MoE models
+ * are gated FFNs; the gated form is this library's reading, as for mk_swiglu.
+ * Everything is as for mk_dispatch_gemm (routing, layout, outputs other than
+ * y_perm, workspace and its size, tuning, errors) with s->N = 2F and:
+ *   w_gate_up [E_local, 2F, d] bf16 (F gate rows, then F up rows; d contiguous)
+ *   h_perm    [T * min(k, E_local), F] bf16 (out; rows >= R are not written):
+ *             h_perm[r, f] = bf16_rne( silu(g) * u ), g and u the bf16 outputs
+ *             of mk_dispatch_gemm with w_experts = w_gate_up at columns f and
+ *             F + f, i.e. bit for bit mk_dispatch_gemm followed by mk_swiglu.
+ * Requires F % 8 == 0 (s->N % 16 == 0, else MK_EINVAL) and
+ * (2F + 256) * d * 2 < 2^31 (else MK_EUNSUPPORTED). */
+mk_status mk_dispatch_gemm_swiglu(const mk_shape *s, const mk_sources *src,
+                                  const float *w_router, const float *bias,
+                                  const int32_t *topk_ids_in,
+                                  const void *w_gate_up,
+                                  void *h_perm, int32_t *slot_of, int32_t *expert_offsets,
+                                  int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
+                                  void *workspace, size_t workspace_bytes,
+                                  const mk_tuning *tune, void *stream);
 
 /* mk_dispatch_gemm for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

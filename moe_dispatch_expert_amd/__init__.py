@@ -74,7 +74,7 @@ def load() -> ctypes.CDLL:
     lib.mk_status_str.restype = ctypes.c_char_p
     lib.mk_route_topk_workspace_bytes.argtypes = [_c_i32, _c_i32]
     lib.mk_route_topk_workspace_bytes.restype = ctypes.c_size_t
-    lib.mk_route_topk.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp,
+    lib.mk_route_topk.argtypes = [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _vp,
                                   ctypes.c_size_t, _vp]
     lib.mk_route_topk.restype = _c_i32
     lib.mk_dispatch_gemm_workspace_bytes.argtypes = [P(MkShape), P(MkSources), P(MkTuning)]
@@ -82,6 +82,8 @@ def load() -> ctypes.CDLL:
     lib.mk_dispatch_gemm.argtypes = [P(MkShape), P(MkSources), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, ctypes.c_size_t, P(MkTuning), _vp]
     lib.mk_dispatch_gemm.restype = _c_i32
+    lib.mk_dispatch_gemm_swiglu.argtypes = lib.mk_dispatch_gemm.argtypes
+    lib.mk_dispatch_gemm_swiglu.restype = _c_i32
     lib.mk_dispatch_gemm_static.argtypes = [P(MkShape), P(MkSources), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp, P(MkTuning), _vp]
     lib.mk_dispatch_gemm_static.restype = _c_i32
@@ -156,8 +158,9 @@ def mk_route_topk_workspace_bytes(T: int, E: int) -> int:
 
 def mk_route_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None,
                   topk_ids: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
-    """Router logits, top-k and softmax gate (mk_route_topk).  Returns (topk_ids, topk_w)."""
+                  workspace: Optional[torch.Tensor] = None, stream=None, logits: Optional[torch.Tensor] = None):
+    """Router logits, top-k and softmax gate (mk_route_topk).  Returns (topk_ids, topk_w).  If `logits`
+    ([T, E] fp32) is given, every logit as it entered the selection is written there too."""
     lib = load()
     T, d = x.shape
     E = w_router.shape[1]
@@ -169,7 +172,7 @@ def mk_route_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: Optiona
     if workspace is None:
         workspace = torch.empty(mk_route_topk_workspace_bytes(T, E), dtype=torch.uint8, device=dev)
     st = lib.mk_route_topk(_ptr(x), _ptr(w_router), _ptr(bias), T, d, E, k, _ptr(topk_ids), _ptr(topk_w),
-                           _ptr(workspace), workspace.numel(), _stream(stream))
+                           _ptr(logits), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "mk_route_topk")
     return topk_ids, topk_w
 
@@ -232,11 +235,14 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
                      E: Optional[int] = None, e_begin: int = 0, workspace: Optional[torch.Tensor] = None,
                      out: Optional[dict] = None, tune: Optional[dict] = None, chunk_rows: int = 0,
                      chunk_ready: Optional[torch.Tensor] = None, epoch: int = 0,
-                     sim_delay_us: Optional[torch.Tensor] = None, sim_payload=None, stream=None) -> dict:
-    """Fused dispatch + expert GEMM (mk_dispatch_gemm).
+                     sim_delay_us: Optional[torch.Tensor] = None, sim_payload=None, stream=None,
+                     swiglu: bool = False) -> dict:
+    """Fused dispatch + expert GEMM (mk_dispatch_gemm; with swiglu=True mk_dispatch_gemm_swiglu).
 
     x: [T, d] bf16 tensor, or a list of S shards [T/S, d] (token t = s*(T/S) + r).
     w_experts: [E_local, N, d] bf16.  Routing uses w_router/bias unless topk_ids_in is given.
+    swiglu: w_experts holds the gate|up weights (N = 2F: F gate rows, then F up rows) and y_perm
+    receives h = silu(gate) * up, [R_cap, F].
     workspace: a zero-filled uint8 tensor of mk_dispatch_gemm_workspace_bytes bytes, reused
     across calls (allocated and zero-filled here if None).
     Returns dict(y_perm, slot_of, expert_offsets, topk_ids, topk_w, row_token, workspace).
@@ -253,7 +259,7 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
     dev = w_experts.device
     r_cap = T * min(k, E_local)
     o = {} if out is None else dict(out)
-    o.setdefault("y_perm", torch.empty(max(r_cap, 1), N, dtype=torch.bfloat16, device=dev))
+    o.setdefault("y_perm", torch.empty(max(r_cap, 1), N // 2 if swiglu else N, dtype=torch.bfloat16, device=dev))
     o.setdefault("slot_of", torch.empty(T, k, dtype=torch.int32, device=dev))
     o.setdefault("expert_offsets", torch.empty(E_local + 1, dtype=torch.int32, device=dev))
     o.setdefault("topk_ids", torch.empty(T, k, dtype=torch.int32, device=dev))
@@ -268,12 +274,13 @@ def mk_dispatch_gemm(x, w_experts: torch.Tensor, k: int, *, w_router: Optional[t
         if nbytes == 0:
             _check(MK_EINVAL, "mk_dispatch_gemm_workspace_bytes")
         workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-    st = lib.mk_dispatch_gemm(ctypes.byref(shape), ctypes.byref(srcs.c), _ptr(w_router), _ptr(bias),
-                              _ptr(topk_ids_in), _ptr(w_experts), _ptr(o["y_perm"]), _ptr(o["slot_of"]),
-                              _ptr(o["expert_offsets"]), _ptr(o["topk_ids"]), _ptr(o["topk_w"]),
-                              _ptr(o["row_token"]), _ptr(workspace), workspace.numel(),
-                              None if tu is None else ctypes.byref(tu), _stream(stream))
-    _check(st, "mk_dispatch_gemm")
+    fn = lib.mk_dispatch_gemm_swiglu if swiglu else lib.mk_dispatch_gemm
+    st = fn(ctypes.byref(shape), ctypes.byref(srcs.c), _ptr(w_router), _ptr(bias),
+            _ptr(topk_ids_in), _ptr(w_experts), _ptr(o["y_perm"]), _ptr(o["slot_of"]),
+            _ptr(o["expert_offsets"]), _ptr(o["topk_ids"]), _ptr(o["topk_w"]),
+            _ptr(o["row_token"]), _ptr(workspace), workspace.numel(),
+            None if tu is None else ctypes.byref(tu), _stream(stream))
+    _check(st, "mk_dispatch_gemm_swiglu" if swiglu else "mk_dispatch_gemm")
     o["workspace"] = workspace
     o["_sources"] = srcs
     return o

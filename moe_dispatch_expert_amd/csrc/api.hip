@@ -2,6 +2,7 @@
 // workspace layout, per-shape tuning and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -57,6 +58,9 @@ mk_status check_sources(const mk_shape *s, const mk_sources *src)
     if (src->chunk_rows > 0) {
         if (!src->chunk_ready || !aligned16(src->chunk_ready)) return MK_EINVAL;
         if (src->sim_delay_us && !aligned16(src->sim_delay_us)) return MK_EINVAL;
+        // the simulator holds every chunk's delay in LDS
+        const long n_chunks = (long)src->S * ((src->rows_per_src + src->chunk_rows - 1) / src->chunk_rows);
+        if (src->sim_delay_us && n_chunks > kSimMaxChunks) return MK_EUNSUPPORTED;
         if (src->sim_payload) {
             if (!src->sim_delay_us) return MK_EINVAL;
             for (int i = 0; i < src->S; ++i)
@@ -91,10 +95,12 @@ int ticks_per_us()
 
 // The per-shape table.  One resident source (S = 1, no arrival flags): no mover role, the GEMM gathers
 // token rows straight from x through row_token (n_mover_wg = 0 in the table's answer); the x
-// matrix must fit one buffer resource (< 4 GiB).  Several resident sources: every co-resident
-// workgroup starts as a mover (the copy takes a few microseconds, then all compute).  Rows arriving
-// from peers: 64 workgroups wait for arrivals and move while the rest compute on the tiles that are
-// complete.
+// matrix must fit one buffer resource (< 4 GiB).  Several sources, resident or arriving from peers:
+// every co-resident workgroup starts as a mover, then computes (on the one-GPU share of a wide EP
+// layer, 8 sources x 2048 rows, d = 7168, 32 local experts, rows arriving in 128-row chunks at
+// U[0, 100] us, the launch took 0.78 / 0.77 / 0.76 / 0.75 ms with 32 / 64 / 128 / 256 movers: every
+// expert tile holds rows of most chunks, so no tile is complete much before the last arrival, and
+// more movers finish the copy sooner).
 bool gather_possible(const mk_shape *s, const mk_sources *src)
 {
     return src && src->S == 1 && src->chunk_rows == 0 && (size_t)s->T * s->d * 2 <= 0xFFFFFFF0ull;
@@ -107,7 +113,7 @@ mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
     t.bn = 256;
     t.bk = Tiles<4>::M256::BK;
     if (gather_possible(s, src)) t.n_mover_wg = MK_MOVERS_NONE;
-    else t.n_mover_wg = (src && src->chunk_rows > 0) ? 64 : 256;
+    else t.n_mover_wg = 256;
     t.n_compute_wg = 0;   // 0: every co-resident workgroup
     return t;
 }
@@ -157,10 +163,14 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
                         const int32_t *topk_ids_in, const void *w_experts, void *y_perm, int32_t *slot_of,
                         int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
                         void *workspace, size_t workspace_bytes, const mk_tuning *tune, void *stream,
-                        int32_t *status_out, const Plan *pre_plan)
+                        int32_t *status_out, const Plan *pre_plan, bool swiglu = false)
 {
     mk_status st = check_shape(s);
     if (st != MK_OK) return st;
+    // SwiGLU: w_experts holds 2F = N rows per expert (F gate rows, then F up rows), y_perm is [R_cap, F]
+    if (swiglu && s->N % 16 != 0) return MK_EINVAL;
+    // (the SwiGLU tiles' W row offsets are 32-bit: N + 256 rows of d bf16 stay below 2 GiB)
+    if (swiglu && (int64_t)(s->N + 256) * s->d * 2 >= ((int64_t)1 << 31)) return MK_EUNSUPPORTED;
     st = check_sources(s, src);
     if (st != MK_OK) return st;
     if (!w_experts || !expert_offsets || !workspace) return MK_EINVAL;
@@ -243,6 +253,7 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
         fa.ga.hdr = hdr;
         fa.ga.d = s->d;
         fa.ga.N = s->N;
+        fa.ga.F = swiglu ? s->N / 2 : 0;
         fa.ga.E_local = s->E_local;
         fa.src = rows;
         if (src->chunk_rows > 0) {
@@ -374,6 +385,7 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
     ga.hdr = hdr;
     ga.d = s->d;
     ga.N = s->N;
+    ga.F = swiglu ? s->N / 2 : 0;
     ga.E_local = s->E_local;
     int grid = gemm_max_grid(tu.bm, tu.bn);
     if (grid <= 0) return MK_EHIP;
@@ -381,7 +393,8 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
     grid -= grid % 8;
     if (grid < 8) grid = 8;
     if (ev_begin && hipEventRecord(ev_begin, hs) != hipSuccess) return MK_EHIP;
-    if (launch_gemm(ga, tu.bm, tu.bn, grid, hs) != hipSuccess) return MK_EHIP;
+    if ((swiglu ? launch_gemm_swiglu(ga, grid, hs) : launch_gemm(ga, tu.bm, tu.bn, grid, hs)) != hipSuccess)
+        return MK_EHIP;
     if (ev_end && hipEventRecord(ev_end, hs) != hipSuccess) return MK_EHIP;
     if (status_out && launch_status(hdr, status_out, hs) != hipSuccess) return MK_EHIP;
     return MK_OK;
@@ -421,8 +434,8 @@ size_t mk_route_topk_workspace_bytes(int32_t T, int32_t E)
 }
 
 mk_status mk_route_topk(const void *x, const float *w_router, const float *bias, int32_t T, int32_t d, int32_t E,
-                        int32_t k, int32_t *topk_ids, float *topk_w, void *workspace, size_t workspace_bytes,
-                        void *stream)
+                        int32_t k, int32_t *topk_ids, float *topk_w, float *logits, void *workspace,
+                        size_t workspace_bytes, void *stream)
 {
     if (T < 0 || d <= 0 || E < 1 || k < 1 || k > E) return MK_EINVAL;
     if (d % 8 != 0) return MK_EINVAL;
@@ -430,7 +443,7 @@ mk_status mk_route_topk(const void *x, const float *w_router, const float *bias,
     if (T == 0) return MK_OK;
     if (!x || !w_router || !topk_ids || !workspace) return MK_EINVAL;
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(workspace) ||
-        (bias && !aligned16(bias)) || (topk_w && !aligned16(topk_w)))
+        (bias && !aligned16(bias)) || (topk_w && !aligned16(topk_w)) || (logits && !aligned16(logits)))
         return MK_EINVAL;
     if (workspace_bytes < mk_route_topk_workspace_bytes(T, E)) return MK_EWORKSPACE;
     hipStream_t st = (hipStream_t)stream;
@@ -450,6 +463,7 @@ mk_status mk_route_topk(const void *x, const float *w_router, const float *bias,
     ta.ids = topk_ids;
     ta.ids_user = nullptr;
     ta.w_user = topk_w;
+    ta.logits_user = logits;
     ta.T = T;
     ta.E = E;
     ta.k = k;
@@ -485,6 +499,17 @@ mk_status mk_dispatch_gemm(const mk_shape *s, const mk_sources *src, const float
     return dispatch_impl(s, src, w_router, bias, topk_ids_in, w_experts, y_perm, slot_of, expert_offsets,
                          topk_ids_out, topk_w_out, row_token, workspace, workspace_bytes, tune, stream, nullptr,
                          nullptr);
+}
+
+mk_status mk_dispatch_gemm_swiglu(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,
+                                  const int32_t *topk_ids_in, const void *w_gate_up, void *h_perm, int32_t *slot_of,
+                                  int32_t *expert_offsets, int32_t *topk_ids_out, float *topk_w_out,
+                                  int32_t *row_token, void *workspace, size_t workspace_bytes, const mk_tuning *tune,
+                                  void *stream)
+{
+    return dispatch_impl(s, src, w_router, bias, topk_ids_in, w_gate_up, h_perm, slot_of, expert_offsets,
+                         topk_ids_out, topk_w_out, row_token, workspace, workspace_bytes, tune, stream, nullptr,
+                         nullptr, true);
 }
 
 mk_status mk_dispatch_gemm_static(const mk_shape *s, const mk_sources *src, const float *w_router, const float *bias,

@@ -294,21 +294,36 @@ __device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, const ScanLd
     __syncthreads();
     const int nrows = q1 - q0;
     __shared__ int ok_sh;
-    if (threadIdx.x == 0) {
-        int ok = 1, waited = -1;
+    if (threadIdx.x < kWave) {
+        // Rows from peers: lane i checks the ready flag of row i's source chunk, all lanes at once
+        // (one load latency for the unit); while some are not ready, lane 0 waits for the first of them
+        // and the lanes check again.
+        int ok = 1;
+        static_assert(kMoveRows <= kWave, "one lane per row of a unit");
         if (a.fl.chunk_rows > 0) {
-            for (int i = 0; i < nrows && ok; ++i) {   // rows are in token order, so chunks ascend
+            const int i = threadIdx.x;
+            int c = -1;
+            if (i < nrows && tok_lds[i] >= 0) {
                 const int t = tok_lds[i];
-                if (t < 0) continue;
                 const int sh = t / a.src.rows_per_src;
-                const int c = sh * a.fl.chunks_per_src + (t - sh * a.src.rows_per_src) / a.fl.chunk_rows;
-                if (c == waited) continue;
-                ok = wait_flag_eq(a.fl.ready + c, a.fl.epoch, &a.hdr->err, a.spin_limit,
-                                  0x20000000u | (uint32_t)c) ? 1 : 0;
-                waited = c;
+                c = sh * a.fl.chunks_per_src + (t - sh * a.src.rows_per_src) / a.fl.chunk_rows;
             }
+            for (;;) {
+                const bool pending = c >= 0 && ld_relaxed(a.fl.ready + c) != a.fl.epoch;
+                const uint64_t pend = __ballot(pending);
+                if (pend == 0ull) break;
+                const int cw = __shfl(c, __ffsll((unsigned long long)pend) - 1);
+                int r = 1;
+                if (i == 0) r = wait_flag_eq(a.fl.ready + cw, a.fl.epoch, &a.hdr->err, a.spin_limit,
+                                             0x20000000u | (uint32_t)cw) ? 1 : 0;
+                if (!__shfl(r, 0)) {
+                    ok = 0;
+                    break;
+                }
+            }
+            fence_acquire_agent();   // the rows' payload is read after the flags
         }
-        ok_sh = ok;
+        if (threadIdx.x == 0) ok_sh = ok;
     }
     __syncthreads();
     if (!ok_sh) return false;
@@ -329,46 +344,76 @@ __device__ __forceinline__ bool fused_move_unit(const FusedArgs &a, const ScanLd
     return true;
 }
 
-// The arrival simulator: releases chunk c at start + delay[c] microseconds,
-// copying the chunk's payload into the source buffer first if one is given.
-__device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a)
+// The arrival simulator: releases chunk c at start + delay[c] microseconds, copying the chunk's
+// payload into the source buffer first if one is given.  Its state lives in LDS (the workgroup's
+// stage arrays, which it has no other use for): every chunk's delay and a released bit.  Each round
+// the workgroup collects the chunks that are due, copies their payloads together, then releases
+// them with one release fence and a flag store each, so a round costs about one LDS pass and no
+// round trip to memory per chunk.  Chunks that already hold the epoch count as released.
+constexpr int kSimMaxChunks = 16384;   // chunks the simulator can hold (S * chunks_per_src)
+constexpr int kSimList = 256;          // chunks released per round at most
+
+__device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a, char *lds)
 {
-    const int n_chunks = a.src.S * a.fl.chunks_per_src;
-    const uint64_t per_us = a.ticks_per_us;
+    const int n_chunks = a.src.S * a.fl.chunks_per_src;   // <= kSimMaxChunks (checked by the host)
+    uint32_t *delay = (uint32_t *)lds;                    // [kSimMaxChunks] microseconds
+    uint32_t *done = delay + kSimMaxChunks;               // [kSimMaxChunks / 32] released bits
+    int32_t *list = (int32_t *)(done + kSimMaxChunks / 32);   // [kSimList] due this round
+    __shared__ int n_due_sh, left_sh;
     __shared__ uint64_t t0_sh;
-    __shared__ int next_sh;
-    if (threadIdx.x == 0) t0_sh = now_ticks();
+    if (threadIdx.x == 0) {
+        t0_sh = now_ticks();
+        left_sh = n_chunks;
+    }
+    for (int c = threadIdx.x; c < n_chunks; c += blockDim.x) delay[c] = a.fl.sim_delay_us[c];
+    for (int i = threadIdx.x; i < (n_chunks + 31) / 32; i += blockDim.x) done[i] = 0u;
+    __syncthreads();
+    for (int c = threadIdx.x; c < n_chunks; c += blockDim.x)
+        if (ld_relaxed(a.fl.ready + c) == a.fl.epoch) {
+            atomicOr(done + c / 32, 1u << (c % 32));
+            atomicSub(&left_sh, 1);
+        }
     __syncthreads();
     const uint64_t t0 = t0_sh;
-    // release in order of due time; ties in chunk order
-    for (int released = 0; released < n_chunks; ++released) {
-        if (threadIdx.x == 0) {
-            int best = -1;
-            uint64_t best_due = ~0ull;
-            for (int c = 0; c < n_chunks; ++c) {
-                if (ld_relaxed(a.fl.ready + c) == a.fl.epoch) continue;
-                const uint64_t due = (uint64_t)a.fl.sim_delay_us[c] * per_us;
-                if (due < best_due) { best_due = due; best = c; }
+    while (left_sh > 0) {   // uniform: read after a barrier
+        // past the wait bound every chunk is due (the readers' own bounds report the delay)
+        const uint64_t el = now_ticks() - t0;
+        const bool late = el >= a.spin_limit;
+        const uint64_t now_us = el / a.ticks_per_us;
+        if (threadIdx.x == 0) n_due_sh = 0;
+        __syncthreads();
+        for (int c = threadIdx.x; c < n_chunks; c += blockDim.x)
+            if (!((done[c / 32] >> (c % 32)) & 1u) && (late || delay[c] <= now_us)) {
+                const int i = atomicAdd(&n_due_sh, 1);
+                if (i < kSimList) list[i] = c;
             }
-            const uint64_t lim = a.spin_limit;
-            while (best >= 0 && now_ticks() - t0 < best_due && now_ticks() - t0 < lim)
-                __builtin_amdgcn_s_sleep(8);
-            next_sh = best;
-        }
         __syncthreads();
-        const int c = next_sh;
-        if (c < 0) break;
-        if (a.fl.has_payload) {
-            const int sh = c / a.fl.chunks_per_src;
-            const int r0 = (c % a.fl.chunks_per_src) * a.fl.chunk_rows;
-            const int r1 = min(a.src.rows_per_src, r0 + a.fl.chunk_rows);
-            const uint4 *s = (const uint4 *)(a.fl.sim_payload[sh] + (size_t)r0 * a.d);
-            uint4 *dst = (uint4 *)(a.src.p[sh] + (size_t)r0 * a.d);
-            const int n16 = (r1 - r0) * a.d / 8;
-            for (int i = threadIdx.x; i < n16; i += blockDim.x) dst[i] = s[i];
+        const int n = min(n_due_sh, kSimList);
+        if (n == 0) {
+            __builtin_amdgcn_s_sleep(2);
+        } else {
+            if (a.fl.has_payload) {
+                for (int i = 0; i < n; ++i) {
+                    const int c = list[i];
+                    const int sh = c / a.fl.chunks_per_src;
+                    const int r0 = (c % a.fl.chunks_per_src) * a.fl.chunk_rows;
+                    const int r1 = min(a.src.rows_per_src, r0 + a.fl.chunk_rows);
+                    const uint4 *src = (const uint4 *)(a.fl.sim_payload[sh] + (size_t)r0 * a.d);
+                    uint4 *dst = (uint4 *)(a.src.p[sh] + (size_t)r0 * a.d);
+                    const int n16 = (r1 - r0) * a.d / 8;
+                    for (int q = threadIdx.x; q < n16; q += blockDim.x) dst[q] = src[q];
+                }
+                wait_vmem_all();   // every wave's copies have reached L2 before the release below
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                for (int i = 0; i < n; ++i)
+                    __hip_atomic_store(a.fl.ready + list[i], a.fl.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                left_sh -= n;
+            }
+            for (int i = threadIdx.x; i < n; i += blockDim.x) atomicOr(done + list[i] / 32, 1u << (list[i] % 32));
         }
-        __syncthreads();
-        if (threadIdx.x == 0) st_release(a.fl.ready + c, a.fl.epoch);
         __syncthreads();
     }
 }
@@ -376,7 +421,7 @@ __device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a)
 // st / ls: the four GEMM stage arrays (32 KiB each; ls holds their LDS-space
 // addresses for the GEMM), also used by the earlier phases; off, toff, uoff:
 // LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
-template <class C>
+template <class C, bool SW>
 __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t call, char *const (&st)[4],
                                                   const LdsStages &ls, int32_t *off, int32_t *toff, int32_t *uoff,
                                                   int32_t *basetab)
@@ -387,7 +432,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     trace_put(a, kTrStart, now_ticks());
     trace_put(a, kTrXcc, (uint64_t)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & 0xF));
     if (a.has_sim && w == (int)gridDim.x - 1) {
-        fused_arrival_sim(a);
+        fused_arrival_sim(a, st[0]);   // the stage arrays are consecutive: 128 KiB
         trace_put(a, kTrDone, now_ticks());
         return;
     }
@@ -407,12 +452,18 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     if (!a.ids_in) {
         const int tasks = router_tasks(a.T, a.E);
         const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-        constexpr int RL = RtStage<kRtKCFused>::LDS_PER_WAVE;
-        lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * RL;   // the stage arrays are consecutive
-        static_assert(C::NW * RL <= 4 * 32768, "router staging fits the stage arrays");
-        // Task q runs on workgroup q % G, wave q / G: with at most 4 G tasks every SIMD holds one chain (a
-        // task is a chain of d / 8 dependent MFMAs, so two on one SIMD take about twice as long).
-        for (int q = wave * G + w; q < tasks; q += G * C::NW) router_task<kRtKCFused>(a.ra, q, rlds);
+        // At most four tasks per workgroup: one per SIMD (waves 0..3), staging chunks of kRtKC steps (a
+        // task's time is mostly the load latency of its chunks).  More: every wave, consecutive tasks per
+        // workgroup (they share token rows), chunks of kRtKCFused steps so that eight waves' staging fits.
+        static_assert(4 * RtStage<kRtKC>::LDS_PER_WAVE <= 4 * 32768, "router staging fits the stage arrays");
+        static_assert(C::NW * RtStage<kRtKCFused>::LDS_PER_WAVE <= 4 * 32768, "router staging fits");
+        if (tasks <= 4 * G) {
+            if (wave < 4 && w * 4 + wave < tasks)
+                router_task<kRtKC>(a.ra, w * 4 + wave, (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKC>::LDS_PER_WAVE);
+        } else {
+            lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKCFused>::LDS_PER_WAVE;
+            for (int q = w * C::NW + wave; q < tasks; q += G * C::NW) router_task<kRtKCFused>(a.ra, q, rlds);
+        }
         trace_put(a, kTrRouted, now_ticks());
         if (!fused_barrier(a, barrier_target(call, 1), 0x01000000u)) return;
         trace_put(a, kTrBarA, now_ticks());
@@ -563,8 +614,10 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     trace_put(a, kTrReleaseTicks, release_ticks);
     uint64_t n_done = 0, wait_ticks = 0;
 
-    // ---- compute: per-XCD queues over chunks of CH consecutive tasks
-    const int NB = (g.N + C::BN - 1) / C::BN;
+    // ---- compute: per-XCD queues over chunks of CH consecutive tasks.  A SwiGLU tile covers BN / 2
+    // features (BN / 2 gate rows and the matching up rows of W).
+    constexpr int BNO = SW ? C::BN / 2 : C::BN;
+    const int NB = SW ? (g.F + BNO - 1) / BNO : (g.N + BNO - 1) / BNO;
     const int n_tasks = toff[a.E_local] * NB;
     const int xcd = w % 8;
     const int CH = (G + 7) / 8;
@@ -601,7 +654,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         t.e = __builtin_amdgcn_readfirstlane(lo);
         t.row0 = __builtin_amdgcn_readfirstlane(off[lo] + mt * C::BM);
         t.rows_valid = __builtin_amdgcn_readfirstlane(min(C::BM, off[lo + 1] - off[lo] - mt * C::BM));
-        t.n0 = __builtin_amdgcn_readfirstlane((rem / nt) * C::BN);
+        t.n0 = __builtin_amdgcn_readfirstlane((rem / nt) * BNO);
         return t;
     };
     // Row tile t's arrival counter and the count of moved units that completes it.
@@ -625,7 +678,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     auto claim_job = [&]() { return job_of(claim()); };
     auto done = [&]() { ++n_done; };
     LambdaSched<decltype(claim_job), decltype(wait), decltype(done)> sc{claim_job, wait, done};
-    gemm_run<C::NW>(g, sc, ls);
+    gemm_run<C::NW, SW>(g, sc, ls);
     trace_put(a, kTrDone, now_ticks());
     trace_put(a, kTrTasks, n_done);
     trace_put(a, kTrWaitTicks, wait_ticks);

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm(GemmArgs a)
     gemm_worker<C, SW>(a, blockIdx.x, gridDim.x, ls);
 }
 
-template <class C>
+template <class C, bool SW>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
         ls.p[k] = (lds_char_t *)st[k];
     }
     const uint32_t call = fused_call_epoch(a);
-    fused_kernel_body<C>(a, call, st, ls, off, toff, uoff, basetab);
+    fused_kernel_body<C, SW>(a, call, st, ls, off, toff, uoff, basetab);
     fused_exit(a, call);
 }
 
@@ -318,13 +318,12 @@ int gemm_max_grid(int bm, int bn)
 // guarantee co-residency instead.
 hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s)
 {
-    if (cooperative) {   // the runtime guarantees co-residency (or refuses the launch)
-        void *args[] = {(void *)&a};
-        return hipLaunchCooperativeKernel((const void *)k_fused<FusedTile>, dim3(grid), dim3(FusedTile::THREADS), args,
-                                          0, s);
-    }
-    hipLaunchKernelGGL(k_fused<FusedTile>, dim3(grid), dim3(FusedTile::THREADS), 0, s, a);
-    return hipGetLastError();
+    // a.ga.F > 0: the gate|up weights with the SwiGLU epilogue
+    const void *k = a.ga.F > 0 ? (const void *)k_fused<FusedTile, true> : (const void *)k_fused<FusedTile, false>;
+    void *args[] = {(void *)&a};
+    if (cooperative)   // the runtime guarantees co-residency (or refuses the launch)
+        return hipLaunchCooperativeKernel(k, dim3(grid), dim3(FusedTile::THREADS), args, 0, s);
+    return hipLaunchKernel(k, dim3(grid), dim3(FusedTile::THREADS), args, 0, s);
 }
 
 int fused_max_grid()
@@ -335,9 +334,13 @@ int fused_max_grid()
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev >= 0 && dev < kMaxDevices && cached[dev] > 0) return cached[dev];
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<FusedTile>, FusedTile::THREADS,
-                                                     0) != hipSuccess)
+    int per_cu_sw = 0;   // both variants must fit (they share the workspace layout and the grid)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<FusedTile, false>,
+                                                     FusedTile::THREADS, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_sw, (const void *)k_fused<FusedTile, true>,
+                                                     FusedTile::THREADS, 0) != hipSuccess)
         return 0;
+    per_cu = std::min(per_cu, per_cu_sw);
     if (dev >= 0 && dev < kMaxDevices) cached[dev] = cus * per_cu;
     return cus * per_cu;
 }

@@ -225,6 +225,7 @@ struct TopkArgs {
     int32_t *ids;            // [T, k]  (workspace or user)
     int32_t *ids_user;       // [T, k] or nullptr (second copy)
     float *w_user;           // [T, k] or nullptr
+    float *logits_user;      // [T, E] or nullptr: every logit (ordered partial sum plus bias)
     uint64_t *blkmask;       // [nblk, E_local] token masks to OR into (token-per-wave path), or nullptr
     int32_t T, E, k, e_begin, E_local;
 };
@@ -271,6 +272,7 @@ __device__ __forceinline__ void topk_select(const TopkArgs &a, int t, const Topk
         if (a.bias) x = x + a.bias[min(e, a.E - 1)];
         lv[v] = x;
         key[v] = e < a.E ? topk_key(x, e) : 0ull;
+        if (a.logits_user && e < a.E) a.logits_user[(size_t)t * a.E + e] = x;
     }
     float top_logit = 0.0f, sel_logit = 0.0f;
     int sel_id = 0;

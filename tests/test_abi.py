@@ -82,11 +82,11 @@ def test_status_strings():
 def test_argument_errors_are_synchronous():
     lib = mk.load()
     # k > E, bad d, null pointers: rejected before any HIP call
-    assert lib.mk_route_topk(None, None, None, 4, 128, 8, 9, None, None, None, 0, None) == mk.MK_EINVAL
-    assert lib.mk_route_topk(None, None, None, 4, 100, 8, 2, None, None, None, 0, None) == mk.MK_EINVAL
-    assert lib.mk_route_topk(None, None, None, 4, 136, 8, 2, None, None, None, 0, None) == mk.MK_EUNSUPPORTED
-    assert lib.mk_route_topk(None, None, None, 4, 128, 8, 2, None, None, None, 0, None) == mk.MK_EINVAL
-    assert lib.mk_route_topk(None, None, None, 0, 128, 8, 2, None, None, None, 0, None) == mk.MK_OK
+    assert lib.mk_route_topk(None, None, None, 4, 128, 8, 9, None, None, None, None, 0, None) == mk.MK_EINVAL
+    assert lib.mk_route_topk(None, None, None, 4, 100, 8, 2, None, None, None, None, 0, None) == mk.MK_EINVAL
+    assert lib.mk_route_topk(None, None, None, 4, 136, 8, 2, None, None, None, None, 0, None) == mk.MK_EUNSUPPORTED
+    assert lib.mk_route_topk(None, None, None, 4, 128, 8, 2, None, None, None, None, 0, None) == mk.MK_EINVAL
+    assert lib.mk_route_topk(None, None, None, 0, 128, 8, 2, None, None, None, None, 0, None) == mk.MK_OK
 
 
 def test_workspace_bytes_and_tuning_without_gpu():
@@ -150,3 +150,23 @@ def test_next_steps_argument_errors_are_synchronous():
     assert sw(fake, fake, 4, fake, 128, 64, fake, fake, need - 1, None) == mk.MK_EWORKSPACE
     assert sw(fake, fake, 4, fake, 8192, 131072, fake, fake, need, None) == mk.MK_EUNSUPPORTED
     assert sw(fake, fake, 4, fake, 128, 64, odd, fake, need, None) == mk.MK_EINVAL
+
+
+def test_dispatch_refusals_without_gpu():
+    """mk_dispatch_gemm_swiglu refuses an odd feature count and a gate|up matrix past the 32-bit tile offsets, and
+    the arrival simulator refuses more chunks than it holds, all before touching the device."""
+    lib = mk.load()
+    fake = ctypes.c_void_p(0x1000)
+    xs = (ctypes.c_void_p * 8)(*([0x1000] * 8))
+
+    def call(fn, shape, S=1, chunk_rows=0, sim=False):
+        src = mk.MkSources(S, shape.T // S, ctypes.cast(xs, ctypes.POINTER(ctypes.c_void_p)), chunk_rows,
+                           fake if chunk_rows else None, 1, fake if sim else None, None)
+        return fn(ctypes.byref(shape), ctypes.byref(src), fake, None, None, fake, fake, fake, fake, None, None, None,
+                  fake, 1 << 40, None, None)
+
+    sw = lib.mk_dispatch_gemm_swiglu
+    assert call(sw, mk.MkShape(256, 512, 8, 2, 0, 8, 1032)) == mk.MK_EINVAL           # F = 516, not a multiple of 8
+    assert call(sw, mk.MkShape(256, 8192, 8, 2, 0, 8, 131072)) == mk.MK_EUNSUPPORTED  # (2F + 256) d 2 >= 2^31
+    big = mk.MkShape(32768, 1024, 64, 4, 0, 16, 512)
+    assert call(lib.mk_dispatch_gemm, big, S=8, chunk_rows=1, sim=True) == mk.MK_EUNSUPPORTED   # 32768 chunks

@@ -102,6 +102,29 @@ def test_router_logits_bit_exact(name, changes):
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} logits differ; first at {tuple(np.argwhere(bad)[0])}"
 
 
+@pytest.mark.parametrize("name,changes", [
+    ("tiny", {}), ("skewed", {}), ("decode", {}),
+    ("tiny", dict(T=96, d=384, E=6, k=3, E_local=6)),
+    ("tiny", dict(T=33, d=128, E=1, k=1, E_local=1)),
+])
+def test_router_final_logits_bit_exact(name, changes):
+    """The logits the selection ranks (mk_route_topk's optional logits output: the eight partial sums added
+    left to right, then the bias) equal the oracle's fp32 logits bit for bit, bias included (the skewed
+    workload carries the Zipf bias)."""
+    wl = W.scaled(W.WORKLOADS[name], **changes) if changes else W.WORKLOADS[name]
+    inp = W.make_inputs(wl, 5, with_experts=False)
+    bias = None if inp["bias"] is None else inp["bias"]
+    lg = torch.full((wl.T, wl.E), float("nan"), dtype=torch.float32, device="cuda")
+    ids, _ = mk.mk_route_topk(inp["x"].cuda(), inp["w_router"].cuda(), wl.k,
+                              bias=None if bias is None else bias.cuda(), logits=lg)
+    torch.cuda.synchronize()
+    ref_lg, ref_ids, _ = oracle_route(inp)
+    got = lg.cpu().numpy()
+    bad = got.view(np.uint32) != ref_lg.astype(np.float32).view(np.uint32)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} logits differ; first at {tuple(np.argwhere(bad)[0])}"
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
 # ---------------------------------------------------------------- the five workloads
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -147,6 +170,71 @@ def test_wide_ep_share_with_source_routing():
     y_ref = oracle.expert_rows(inp["x"], inp["w_experts"], offsets, row_token, rows)
     y_gpu = out["y_perm"][torch.from_numpy(rows.astype(np.int64)).cuda()].float().cpu().numpy()
     assert_y_close(y_gpu, y_ref, "wide_ep")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_decode_every_row_other_seeds(seed):
+    """The decode-shaped share at seeds 1 and 2, every routed row against the oracle."""
+    inp = W.make_inputs(W.WORKLOADS["decode"], seed)
+    out = _run(inp, to_dev(inp))
+    full_check(inp, out, what=f"decode seed {seed}")
+
+
+_CANARY_BF16 = 0x7FC1      # a quiet-NaN bf16 pattern no GEMM row produces from finite inputs
+_CANARY_I32 = -7
+
+
+def _canary_outputs(wl, dev):
+    r_cap = wl.T * min(wl.k, wl.E_local)
+    y = torch.empty(r_cap, wl.N, dtype=torch.bfloat16, device=dev)
+    y.view(torch.int16).fill_(_CANARY_BF16)
+    rt = torch.full((r_cap,), _CANARY_I32, dtype=torch.int32, device=dev)
+    return {"y_perm": y, "row_token": rt}
+
+
+def _assert_canaries(out, R, what):
+    tail = out["y_perm"][R:].view(torch.int16)
+    assert bool((tail == _CANARY_BF16).all()), f"{what}: y_perm rows >= R = {R} were written"
+    assert bool((out["row_token"][R:] == _CANARY_I32).all()), f"{what}: row_token entries >= R = {R} were written"
+
+
+@pytest.mark.parametrize("path", ["table", "movers", "staged"])
+def test_decode_rows_beyond_R_untouched(path):
+    """y_perm rows >= R (and row_token entries >= R) keep what the caller left there, on the decode share
+    (R = 127 of R_cap = 1024 at seed 0) in each launch configuration: the table's (rows read in place), a mover role,
+    and the staged launches; the routed rows still match the oracle."""
+    wl = W.WORKLOADS["decode"]
+    inp = W.make_inputs(wl, 0)
+    dev = to_dev(inp)
+    tune = {"table": {}, "movers": {"n_mover_wg": 64}, "staged": {"n_mover_wg": mk.MK_MOVERS_STAGED}}[path]
+    out = _run(inp, dev, out=_canary_outputs(wl, "cuda"), tune=tune)
+    r = full_check(inp, out, what=f"decode {path}")
+    assert r["R"] < wl.T * wl.k
+    _assert_canaries(out, r["R"], f"decode {path}")
+
+
+@pytest.mark.parametrize("path", ["table", "staged"])
+def test_wide_ep_reduced_rows_beyond_R_untouched(path):
+    """The same on a reduced wide-EP share (8 sources x 256 rows, local experts 16..31 of 64, top-4, ids routed
+    by the sources): rows >= R of y_perm and row_token untouched, routed rows against the oracle."""
+    wl = W.scaled(W.WORKLOADS["wide_ep"], T=2048, d=1024, E=64, k=4, N=512, E_local=16, e_begin=16,
+                  chunk_rows=32)
+    inp = W.make_inputs(wl, 7)
+    dev = to_dev(inp)
+    _, ref_ids, _ = oracle_route(inp)
+    tune = {"table": {}, "staged": {"n_mover_wg": mk.MK_MOVERS_STAGED}}[path]
+    out = mk.mk_dispatch_gemm(dev["x"], dev["w_experts"], wl.k, topk_ids_in=torch.from_numpy(ref_ids).cuda(),
+                              E=wl.E, e_begin=wl.e_begin, out=_canary_outputs(wl, "cuda"), tune=tune)
+    torch.cuda.synchronize()
+    assert mk.mk_poll_error(out["workspace"])[0] == mk.MK_OK
+    _, offsets, _, row_token = check_layout(out, ref_ids, wl, f"wide_ep reduced {path}")
+    R = int(offsets[-1])
+    assert R < wl.T * min(wl.k, wl.E_local)
+    rows = sample_rows(offsets, 64)
+    y_ref = oracle.expert_rows(inp["x"], inp["w_experts"], offsets, row_token, rows)
+    assert_y_close(out["y_perm"][torch.from_numpy(rows.astype(np.int64)).cuda()].float().cpu().numpy(), y_ref,
+                   f"wide_ep reduced {path}")
+    _assert_canaries(out, R, f"wide_ep reduced {path}")
 
 
 # ---------------------------------------------------------------- edge cases
