@@ -188,6 +188,8 @@ def library_gemm(wl, steps: int, warmup: int):
 def trace_summary(tr: dict) -> dict:
     """Phase boundaries of the fused kernel (max over workgroups, microseconds from the first start)."""
     live = tr["start"] > 0
+    if not live.any():
+        return {"note": "no trace records written"}
     t0 = tr["start"][live].min()
     us = lambda v: round(float(v - t0) / tr["ticks_per_us"], 2)
     out = {"start_spread_us": us(tr["start"][live].max())}

@@ -230,7 +230,18 @@ mk_status mk_dispatch_gemm_static(const mk_shape *s, const mk_sources *src,
                                   int32_t *topk_ids_out, float *topk_w_out, int32_t *row_token,
                                   int32_t *status, const mk_tuning *tune, void *stream);
 
-/* The tuning the per-shape table picks (what a NULL/zero `tune` means). */
+/* The tuning the per-shape table picks (what a NULL/zero `tune` means), keyed
+ * on the shape and the sources:
+ *   one resident source whose x fits a 4 GiB buffer resource: no mover role
+ *     (MK_MOVERS_NONE), and n_compute_wg = the GEMM tasks a uniform routing
+ *     gives (E_local * ceil(T k / E / 256) * ceil(N / 256)) plus a quarter,
+ *     rounded up to a multiple of 8, at least 32; 0 (every co-resident
+ *     workgroup) once that reaches 256;
+ *   several sources, or rows arriving in chunks: n_mover_wg = 256 (every
+ *     workgroup moves rows first, then computes), n_compute_wg = 0;
+ *   bm = bn = 256, bk = 64, cooperative = 0.
+ * A value the table gives that the device cannot hold at once is clamped to
+ * it; one the caller gives is refused (MK_EUNSUPPORTED). */
 mk_status mk_select_tuning(const mk_shape *s, const mk_sources *src, mk_tuning *out);
 
 /* Where the fused kernel's per-workgroup trace lives inside a dispatch

@@ -112,7 +112,14 @@ def test_workspace_bytes_and_tuning_without_gpu():
         assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, tune=bad) == 0, bad
     t = mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336)
     assert t["bm"] == 256 and t["bn"] == 256 and t["bk"] == 64 and t["n_mover_wg"] == mk.MK_MOVERS_NONE
-    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=8, chunk_rows=128)["n_mover_wg"] > 0
+    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=8, chunk_rows=128)["n_mover_wg"] == 256
+    # compute workgroups keyed on the shape: the expected GEMM tasks plus a quarter, multiple of 8, >= 32;
+    # 0 (all) once that reaches 256
+    assert mk.mk_select_tuning(256, 512, 8, 2, 0, 8, 1024)["n_compute_wg"] == 40        # 32 tasks
+    assert mk.mk_select_tuning(1024, 4096, 8, 2, 0, 8, 4096)["n_compute_wg"] == 160     # 128 tasks
+    assert mk.mk_select_tuning(16, 512, 8, 2, 0, 8, 256)["n_compute_wg"] == 32          # 8 tasks: the floor
+    assert mk.mk_select_tuning(128, 7168, 256, 8, 0, 32, 2048)["n_compute_wg"] == 0     # 256 tasks
+    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=8)["n_compute_wg"] == 0   # rows moved
     assert mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336, S=2)["n_mover_wg"] > 0
     with pytest.raises(mk.MkError):
         mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14335)

@@ -72,6 +72,18 @@ def test_role_split_does_not_change_results(n_mover):
     _same(ref, out)
 
 
+@pytest.mark.parametrize("n_compute", [8, 32, 100, 0])
+def test_grid_size_does_not_change_results(n_compute):
+    """The in-place path on 8, 32 or 100 workgroups, or the table's count (0), gives the staged launches'
+    outputs bit for bit: the grid only changes which workgroup runs a phase's work or a GEMM tile."""
+    wl = W.scaled(W.WORKLOADS["mixtral"], T=1024, N=1024)
+    inp = W.make_inputs(wl, 22)
+    dev = to_dev(inp)
+    ref = _call(inp, dev, tune={"n_mover_wg": -1})
+    out = _call(inp, dev, tune={"n_mover_wg": mk.MK_MOVERS_NONE, "n_compute_wg": n_compute})
+    _same(ref, out, KEYS + ("topk_w",))
+
+
 def test_new_inputs_through_one_workspace():
     """A second call with different inputs through the same workspace must not see the first call's rows."""
     wl = W.scaled(W.WORKLOADS["skewed"], T=2048, N=512)
