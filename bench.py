@@ -120,8 +120,9 @@ def write_traffic(out_dir: str, workload: str, kernel: str, copy_mib: int) -> di
     f_c = _pmc_per_dispatch(os.path.join(out_dir, "pmc_fetch_copy"), "MulFunctor", "FETCH_SIZE")
     w_c = _pmc_per_dispatch(os.path.join(out_dir, "pmc_write_copy"), "MulFunctor", "WRITE_SIZE")
     fetch_scale, write_scale = copy_bytes / f_c, copy_bytes / w_c
-    run = ("python3 bench.py --staged --steps 3 --warmup 1 --no-cpu-baseline" if kernel == "gemm" else
-           f"python3 bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline")
+    run = (f"python3 bench.py --workload {workload} --staged --no-sub --steps 3 --warmup 1 --no-cpu-baseline"
+           if kernel == "gemm" else
+           f"python3 bench.py --workload {workload} --no-sub --steps 3 --warmup 1 --no-cpu-baseline")
     commands = [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} -f csv -d {out_dir}/pmc_{c.split('_')[0].lower()}_{kernel}_{workload} "
                 f"-o run -- {run}" for c in ("FETCH_SIZE", "WRITE_SIZE")]
     commands += [f"export TMPDIR=/tmp; rocprofv3 --pmc {c} -f csv -d {out_dir}/pmc_{c.split('_')[0].lower()}_copy -o run "
@@ -135,6 +136,46 @@ def write_traffic(out_dir: str, workload: str, kernel: str, copy_mib: int) -> di
     with open(_traffic_path(kernel, workload), "w") as f:
         json.dump(rec, f, indent=1)
     return rec
+
+
+def _trace_command(out_dir: str, workload: str, kernel: str) -> str:
+    run = f"python3 bench.py --workload {workload} --no-sub --no-cpu-baseline" + (" --staged" if kernel == "gemm" else "")
+    return f"export TMPDIR=/tmp; rocprofv3 --kernel-trace --stats -f csv -d {out_dir} -o run -- {run}"
+
+
+def summarize_trace(out_dir: str, workload: str, kernel: str, timed: int) -> str:
+    """profiles/<kernel>_<workload>_kernel_trace.md from a rocprofv3 --kernel-trace --stats run of
+    _trace_command: the per-kernel statistics over every dispatch, then the timed window alone (the last
+    `timed` dispatches of the dominant kernel: the bench's timed steps, without its first call and warm-ups)."""
+    import csv
+    import glob
+    substr = {"fused": "k_fused", "gemm": "k_gemm"}[kernel]
+    stats = glob.glob(os.path.join(out_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"no kernel stats / trace csv under {out_dir}")
+    lines = [f"# Kernel trace: {substr}, {workload} workload", "",
+             "Command (run from the repository root on one MI355X):", "", "```",
+             _trace_command(out_dir, workload, kernel), f"python3 bench.py --summarize-trace {out_dir} "
+             f"--workload {workload} --kernel {kernel} --steps {timed}", "```", "",
+             "All dispatches:", "",
+             "| kernel | calls | total us | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(stats[0])):
+        n = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+        f = lambda k: float(r[k]) / 1000.0
+        lines.append(f"| `{n}` | {r['Calls']} | {f('TotalDurationNs'):.1f} | {f('AverageNs'):.1f} | "
+                     f"{f('MinNs'):.1f} | {f('MaxNs'):.1f} | {float(r['Percentage']):.1f} |")
+    d = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in csv.DictReader(open(trace[0]))
+               if substr in r["Kernel_Name"])
+    win = np.array([(e - b) / 1000.0 for b, e in d[-timed:]])
+    lines += ["", f"Timed window (the last {len(win)} of {len(d)} `{substr}` dispatches, the bench's timed steps):", "",
+              "| dispatches | avg us | p10 us | p50 us | p90 us |", "|---|---|---|---|---|",
+              f"| {len(win)} | {win.mean():.1f} | {np.percentile(win, 10):.1f} | {np.percentile(win, 50):.1f} | "
+              f"{np.percentile(win, 90):.1f} |"]
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_kernel_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 def copy_calibration(mib: int, reps: int = 3):
@@ -511,7 +552,11 @@ def main():
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     ap.add_argument("--write-traffic", default="", metavar="DIR",
                     help="only turn the rocprofv3 --pmc outputs under DIR into profiles/<kernel>_<workload>_hbm_traffic.json")
-    ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"), help="kernel for --write-traffic")
+    ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"),
+                    help="kernel for --write-traffic / --summarize-trace")
+    ap.add_argument("--summarize-trace", default="", metavar="DIR",
+                    help="only turn a rocprofv3 --kernel-trace --stats run under DIR into "
+                         "profiles/<kernel>_<workload>_kernel_trace.md (timed window = the last --steps dispatches)")
     ap.add_argument("--evict-mall", action="store_true",
                     help="read 1 GiB before every step (outside the launch events) so no input is left in the "
                          "256 MiB Infinity Cache; value and roofline then come from the launch events")
@@ -529,6 +574,9 @@ def main():
         return
     if args.write_traffic:
         print(json.dumps(write_traffic(args.write_traffic, args.workload, args.kernel, 1024)), flush=True)
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.workload, args.kernel, args.steps), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (asked for --gpus {args.gpus}); run with --gpus 1",
