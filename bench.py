@@ -138,12 +138,14 @@ def write_traffic(out_dir: str, workload: str, kernel: str, copy_mib: int) -> di
     return rec
 
 
-def _trace_command(out_dir: str, workload: str, kernel: str) -> str:
-    run = f"python3 bench.py --workload {workload} --no-sub --no-cpu-baseline" + (" --staged" if kernel == "gemm" else "")
+def _trace_command(out_dir: str, workload: str, kernel: str, extra: str = "") -> str:
+    run = (f"python3 bench.py --workload {workload} --no-sub --no-cpu-baseline" + (" --staged" if kernel == "gemm" else "")
+           + (f" {extra}" if extra else ""))
     return f"export TMPDIR=/tmp; rocprofv3 --kernel-trace --stats -f csv -d {out_dir} -o run -- {run}"
 
 
-def summarize_trace(out_dir: str, workload: str, kernel: str, timed: int) -> str:
+def summarize_trace(out_dir: str, workload: str, kernel: str, timed: int, extra: str = "", name: str = "",
+                    path: str = "") -> str:
     """profiles/<kernel>_<workload>_kernel_trace.md from a rocprofv3 --kernel-trace --stats run of
     _trace_command: the per-kernel statistics over every dispatch, then the timed window alone (the last
     `timed` dispatches of the dominant kernel: the bench's timed steps, without its first call and warm-ups)."""
@@ -154,10 +156,11 @@ def summarize_trace(out_dir: str, workload: str, kernel: str, timed: int) -> str
     trace = glob.glob(os.path.join(out_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not stats or not trace:
         raise SystemExit(f"no kernel stats / trace csv under {out_dir}")
-    lines = [f"# Kernel trace: {substr}, {workload} workload", "",
-             "Command (run from the repository root on one MI355X):", "", "```",
-             _trace_command(out_dir, workload, kernel), f"python3 bench.py --summarize-trace {out_dir} "
-             f"--workload {workload} --kernel {kernel} --steps {timed}", "```", "",
+    tail = (f" --trace-extra '{extra}'" if extra else "") + (f" --trace-name {name}" if name else "")
+    lines = [f"# Kernel trace: {substr}, {workload} workload" + (f" ({extra})" if extra else ""), "",
+             "Commands (run from the repository root on one MI355X):", "", "```",
+             _trace_command(out_dir, workload, kernel, extra), f"python3 bench.py --summarize-trace {out_dir} "
+             f"--workload {workload} --kernel {kernel} --steps {timed}{tail}", "```", "",
              "All dispatches:", "",
              "| kernel | calls | total us | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
     for r in csv.DictReader(open(stats[0])):
@@ -172,7 +175,7 @@ def summarize_trace(out_dir: str, workload: str, kernel: str, timed: int) -> str
               "| dispatches | avg us | p10 us | p50 us | p90 us |", "|---|---|---|---|---|",
               f"| {len(win)} | {win.mean():.1f} | {np.percentile(win, 10):.1f} | {np.percentile(win, 50):.1f} | "
               f"{np.percentile(win, 90):.1f} |"]
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_kernel_trace.md")
+    path = path or os.path.join(ROOT, "profiles", f"{name or kernel + '_' + workload}_kernel_trace.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return path
@@ -394,8 +397,12 @@ class Case:
         self.inp = inp if inp is not None else W.make_inputs(wl, seed)
         dev = self.dev = torch.device("cuda:0")
         x = self.inp["x"]
-        self.xs = ([x[s * wl.rows_per_src:(s + 1) * wl.rows_per_src].contiguous().to(dev) for s in range(wl.S)]
-                   if wl.S > 1 else x.to(dev))
+        if wl.S > 1:   # the peers' rows land in per-peer regions of one receive buffer
+            recv = torch.empty(wl.T, wl.d, dtype=x.dtype, device=dev)
+            recv.copy_(x)
+            self.xs = [recv[s * wl.rows_per_src:(s + 1) * wl.rows_per_src] for s in range(wl.S)]
+        else:
+            self.xs = x.to(dev)
         self.wr = self.inp["w_router"].to(dev)
         self.bias = None if self.inp["bias"] is None else self.inp["bias"].to(dev)
         self.we = self.inp["w_experts"].to(dev)
@@ -405,9 +412,10 @@ class Case:
             self.ids_in = torch.cat(parts).contiguous()
         self.base_tune = dict(base_tune)
         self.arrivals = None
+        xl = self.xs if isinstance(self.xs, list) else [self.xs]
         self.ws = torch.zeros(mk.mk_dispatch_gemm_workspace_bytes(
-            wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, wl.S, tune=self.base_tune), dtype=torch.uint8,
-            device=dev)
+            wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, wl.S, tune=self.base_tune, xs=xl),
+            dtype=torch.uint8, device=dev)
         out = self._call(None, None)
         self.bufs = {k: out[k] for k in ("y_perm", "slot_of", "expert_offsets", "topk_ids", "topk_w", "row_token")}
         self.epoch = 1
@@ -421,8 +429,9 @@ class Case:
         self.arrivals = {"ready": torch.zeros(n, dtype=torch.int32, device=self.dev),
                          "delays": delays_us.to(self.dev)}
         tu = dict(self.base_tune)
+        xl = self.xs if isinstance(self.xs, list) else [self.xs]
         self.ws = torch.zeros(self.mk.mk_dispatch_gemm_workspace_bytes(
-            wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, wl.S, chunk_rows=wl.chunk_rows, tune=tu),
+            wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, wl.S, chunk_rows=wl.chunk_rows, tune=tu, xs=xl),
             dtype=torch.uint8, device=self.dev)
         return self
 
@@ -501,7 +510,8 @@ def decode_record(seed: int, steps: int, warmup: int) -> dict:
 def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
     """One GPU's share of a wide EP layer (8 sources x 2048 rows, d=7168, 32 local of 256 experts, top-8,
     N=2048), ids routed by the sources (untimed), rows arriving in chunks of 128 whose ready flags the
-    kernel's arrival simulator releases at seeded U[0, 100] us delays.  Overlap efficiency = (last arrival
+    kernel's arrival simulator releases at seeded U[0, 100] us delays.  Also timed: the same arrivals with
+    every workgroup first moving rows (the dispatch role), and all rows resident.  Overlap efficiency = (last arrival
     + the grouped GEMM alone on the same layout) / the fused launch: above 1 when the GEMM runs while rows
     are still arriving."""
     import workloads as W
@@ -511,6 +521,9 @@ def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
     fused = Case(wl, seed, {}, inp=inp).with_arrivals(delays)
     mf = fused.run(steps, warmup)
     del fused
+    movers = Case(wl, seed, {"n_mover_wg": 256}, inp=inp).with_arrivals(delays)
+    mm = movers.run(steps, warmup)
+    del movers
     resident = Case(wl, seed, {}, inp=inp)
     mr = resident.run(steps, warmup)
     del resident
@@ -527,6 +540,8 @@ def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
             "arrivals": f"{delays.numel()} chunks of {wl.chunk_rows} rows, flags released at seeded U[0,100] us "
                         f"(last at {float(delays.max()):.0f} us), rows already resident",
             "roofline": roof,
+            "path": "the per-shape table's (tiles read their rows in place, each waiting for its rows' chunks)",
+            "fused_movers_arrivals_launch_ms": round(float(np.mean(mm["launch_all"])), 4),
             "fused_all_resident_launch_ms": round(float(np.mean(mr["launch_all"])), 4),
             "gemm_alone_launch_ms": round(gemm_ms, 4),
             "last_arrival_ms": round(arrival_ms, 4),
@@ -548,12 +563,15 @@ def main():
     ap.add_argument("--staged", action="store_true", help="one launch per step instead of the fused kernel")
     ap.add_argument("--movers", type=int, default=0, help="override the per-shape mover count")
     ap.add_argument("--compute-wg", type=int, default=0, help="override the per-shape compute workgroup count")
+    ap.add_argument("--tile-order", type=int, default=0, help="override the per-shape GEMM task order (1 or 2)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain MIB-MiB device copy (counter calibration) and exit")
     ap.add_argument("--write-traffic", default="", metavar="DIR",
                     help="only turn the rocprofv3 --pmc outputs under DIR into profiles/<kernel>_<workload>_hbm_traffic.json")
     ap.add_argument("--kernel", default="fused", choices=("fused", "gemm"),
                     help="kernel for --write-traffic / --summarize-trace")
+    ap.add_argument("--trace-extra", default="", help="bench arguments the traced run added (--summarize-trace)")
+    ap.add_argument("--trace-name", default="", help="profile name instead of <kernel>_<workload> (--summarize-trace)")
     ap.add_argument("--summarize-trace", default="", metavar="DIR",
                     help="only turn a rocprofv3 --kernel-trace --stats run under DIR into "
                          "profiles/<kernel>_<workload>_kernel_trace.md (timed window = the last --steps dispatches)")
@@ -576,7 +594,8 @@ def main():
         print(json.dumps(write_traffic(args.write_traffic, args.workload, args.kernel, 1024)), flush=True)
         return
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.workload, args.kernel, args.steps), flush=True)
+        print(summarize_trace(args.summarize_trace, args.workload, args.kernel, args.steps, args.trace_extra,
+                              args.trace_name), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (asked for --gpus {args.gpus}); run with --gpus 1",
@@ -598,6 +617,8 @@ def main():
         base_tune["n_mover_wg"] = args.movers
     if args.compute_wg:
         base_tune["n_compute_wg"] = args.compute_wg
+    if args.tile_order:
+        base_tune["tile_order"] = args.tile_order
     case = Case(wl, args.seed, base_tune)
     if wl.chunk_rows > 0 and not args.staged:   # rows arriving in chunks, flags released at seeded delays
         case.with_arrivals(case.inp["delays_us"])
@@ -605,7 +626,7 @@ def main():
     ms_step, R, flops = m["ms_step"], m["R"], m["flops"]
     tflops = flops / (ms_step * 1e-3) / 1e12
     kernel = "gemm" if args.staged else "fused"
-    traffic = _traffic(kernel, args.workload) if not (args.movers or args.compute_wg) else None
+    traffic = _traffic(kernel, args.workload) if not (args.movers or args.compute_wg or args.tile_order) else None
     roof = _roofline(flops, m["alg_bytes"], m["launch_all"],
                      "grouped expert GEMM (k_gemm)" if args.staged else "fused dispatch+GEMM (k_fused)", traffic)
     rec = {
@@ -623,10 +644,11 @@ def main():
         "roofline": roof,
         "torch": torch.__version__,
     }
-    if args.staged or args.movers or args.compute_wg:
+    if args.staged or args.movers or args.compute_wg or args.tile_order:
         rec["config"]["path"] = ("staged" if args.staged else "fused") + (
             f", {args.movers} movers" if args.movers else "") + (
-            f", {args.compute_wg} compute workgroups" if args.compute_wg else "")
+            f", {args.compute_wg} compute workgroups" if args.compute_wg else "") + (
+            f", tile order {args.tile_order}" if args.tile_order else "")
     if args.evict_mall:
         rec["config"]["mall"] = "1 GiB read before every step; step time = launch time"
     if args.trace and not args.staged:
@@ -640,7 +662,8 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(case.inp, R)
         rec["cpu_baseline"]["value"] = round(rec["cpu_baseline"]["value"], 6)
     del case
-    if not args.no_sub and not (args.staged or args.movers or args.compute_wg) and args.workload == "mixtral":
+    if not args.no_sub and not (args.staged or args.movers or args.compute_wg or args.tile_order) and \
+            args.workload == "mixtral":
         torch.cuda.empty_cache()
         rec["decode"] = decode_record(args.seed, args.steps, args.warmup)
         torch.cuda.empty_cache()

@@ -85,8 +85,10 @@ typedef struct {
  *                 tile (waiting for the source chunks' ready flags when rows
  *                 arrive from peers) and then join the GEMM role;
  *                 MK_MOVERS_NONE: no mover role: the GEMM reads each tile's
- *                 token rows in place through the slot -> token map (one
- *                 resident source only, T * d * 2 < 4 GiB; else
+ *                 token rows in place through the slot -> token map, and
+ *                 when rows arrive from peers each tile first waits for the
+ *                 ready flags of its rows' chunks (at most 8 sources, all
+ *                 inside 4 GiB - 256 bytes from the lowest one; else
  *                 MK_EUNSUPPORTED);
  *                 MK_MOVERS_STAGED: one kernel launch per step instead of the
  *                 persistent kernel (no overlap; for comparison).
@@ -101,13 +103,21 @@ typedef struct {
  *                 (for callers that share the device with other streams); about
  *                 15 us more per call.  0: an ordinary launch (see
  *                 mk_dispatch_gemm).
+ *   tile_order    order of the GEMM tasks (the fused path): MK_ORDER_EXPERT,
+ *                 every expert's row tiles together (its short last tile
+ *                 beside the full tiles that share its weights), or
+ *                 MK_ORDER_TAILS_LAST, the full 256-row tiles of all experts
+ *                 first and the experts' short last tiles after them (the last
+ *                 round is then made of short tasks).  0: the table's.
  *   ev_gemm_begin / ev_gemm_end: NULL, or hipEvent_t handles the library
  *                 records on `stream` immediately before and after the launch
  *                 that runs the expert GEMM, so a caller can time that kernel. */
 #define MK_MOVERS_STAGED (-1)
 #define MK_MOVERS_NONE (-2)
+#define MK_ORDER_EXPERT 1
+#define MK_ORDER_TAILS_LAST 2
 typedef struct {
-    int32_t n_mover_wg, n_compute_wg, bm, bn, bk, cooperative;
+    int32_t n_mover_wg, n_compute_wg, bm, bn, bk, cooperative, tile_order;
     void *ev_gemm_begin;
     void *ev_gemm_end;
 } mk_tuning;
@@ -218,7 +228,7 @@ mk_status mk_dispatch_gemm_swiglu(const mk_shape *s, const mk_sources *src,
  * A shape, sources and tuning whose workspace (mk_dispatch_gemm_workspace_bytes)
  * exceeds MK_STATIC_SCRATCH_BYTES is refused with MK_EWORKSPACE before any
  * device work; paths that copy rows into the expert-contiguous buffer need it
- * for the rows, so in practice this is the in-place path (one resident source).
+ * for the rows, so in practice this is the in-place path.
  * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
  * (two streams, two threads) race and give undefined results. */
 #define MK_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
@@ -232,13 +242,14 @@ mk_status mk_dispatch_gemm_static(const mk_shape *s, const mk_sources *src,
 
 /* The tuning the per-shape table picks (what a NULL/zero `tune` means), keyed
  * on the shape and the sources:
- *   one resident source whose x fits a 4 GiB buffer resource: no mover role
- *     (MK_MOVERS_NONE), and n_compute_wg = the GEMM tasks a uniform routing
- *     gives (E_local * ceil(T k / E / 256) * ceil(N / 256)) plus a quarter,
+ *   rows readable in place (at most 8 sources inside one 4 GiB window,
+ *     resident or arriving in chunks): no mover role (MK_MOVERS_NONE), and
+ *     n_compute_wg = the GEMM tasks a uniform routing gives
+ *     (E_local * ceil(T k / E / 256) * ceil(N / 256)) plus a quarter,
  *     rounded up to a multiple of 8, at least 32; 0 (every co-resident
  *     workgroup) once that reaches 256;
- *   several sources, or rows arriving in chunks: n_mover_wg = 256 (every
- *     workgroup moves rows first, then computes), n_compute_wg = 0;
+ *   otherwise: n_mover_wg = 256 (every workgroup moves rows first, then
+ *     computes), n_compute_wg = 0;
  *   bm = bn = 256, bk = 64, cooperative = 0.
  * A value the table gives that the device cannot hold at once is clamped to
  * it; one the caller gives is refused (MK_EUNSUPPORTED). */

@@ -39,10 +39,12 @@ class MkSources(ctypes.Structure):
 
 class MkTuning(ctypes.Structure):
     _fields_ = [("n_mover_wg", _c_i32), ("n_compute_wg", _c_i32), ("bm", _c_i32), ("bn", _c_i32),
-                ("bk", _c_i32), ("cooperative", _c_i32), ("ev_gemm_begin", _vp), ("ev_gemm_end", _vp)]
+                ("bk", _c_i32), ("cooperative", _c_i32), ("tile_order", _c_i32), ("ev_gemm_begin", _vp),
+                ("ev_gemm_end", _vp)]
 
-TUNING_INTS = ("n_mover_wg", "n_compute_wg", "bm", "bn", "bk", "cooperative")
+TUNING_INTS = ("n_mover_wg", "n_compute_wg", "bm", "bn", "bk", "cooperative", "tile_order")
 MK_MOVERS_STAGED, MK_MOVERS_NONE = -1, -2   # n_mover_wg: one launch per step; no mover role (rows read in place)
+MK_ORDER_EXPERT, MK_ORDER_TAILS_LAST = 1, 2   # tile_order: row tiles expert by expert; full tiles first
 
 
 def _tuning(tune: Optional[dict]):
@@ -177,24 +179,36 @@ def mk_route_topk(x: torch.Tensor, w_router: torch.Tensor, k: int, bias: Optiona
     return topk_ids, topk_w
 
 
-def mk_dispatch_gemm_workspace_bytes(T, d, E, k, e_begin, E_local, N, S=1, chunk_rows=0,
-                                     tune: Optional[dict] = None) -> int:
-    """Workspace bytes for this shape, number of sources, arrival chunking and tuning (None = the table)."""
-    shape = _shape(T, d, E, k, e_begin, E_local, N)
-    ptrs = (_vp * max(S, 1))(*([0x1000] * max(S, 1)))   # placeholders: only the count is inspected
-    src = MkSources(S, T // max(S, 1), ctypes.cast(ptrs, ctypes.POINTER(_vp)), int(chunk_rows),
+def _placeholder_sources(T, d, S, chunk_rows, xs):
+    """mk_sources for the size and table queries: the given source tensors' addresses (the table reads rows
+    in place only from sources inside one 4 GiB window), else S contiguous placeholder buffers."""
+    S = len(xs) if xs is not None else max(S, 1)
+    rows = T // S
+    addrs = ([t.data_ptr() for t in xs] if xs is not None else
+             [0x1000 + i * rows * d * 2 for i in range(S)])   # never dereferenced
+    ptrs = (_vp * S)(*addrs)
+    src = MkSources(S, rows, ctypes.cast(ptrs, ctypes.POINTER(_vp)), int(chunk_rows),
                     ctypes.c_void_p(0x1000) if chunk_rows else None, 0, None, None)
+    return src, ptrs
+
+
+def mk_dispatch_gemm_workspace_bytes(T, d, E, k, e_begin, E_local, N, S=1, chunk_rows=0,
+                                     tune: Optional[dict] = None, xs: Optional[Sequence[torch.Tensor]] = None) -> int:
+    """Workspace bytes for this shape, sources (xs: the source tensors, else S placeholders), arrival chunking and
+    tuning (None = the table)."""
+    shape = _shape(T, d, E, k, e_begin, E_local, N)
+    src, _ptrs = _placeholder_sources(T, d, S, chunk_rows, xs)
     tu = _tuning(tune)
     return int(load().mk_dispatch_gemm_workspace_bytes(ctypes.byref(shape), ctypes.byref(src),
                                                        None if tu is None else ctypes.byref(tu)))
 
 
-def mk_select_tuning(T, d, E, k, e_begin, E_local, N, S=1, chunk_rows=0) -> dict:
-    """The per-shape table's tuning for this shape, number of sources and arrival chunking."""
+def mk_select_tuning(T, d, E, k, e_begin, E_local, N, S=1, chunk_rows=0,
+                     xs: Optional[Sequence[torch.Tensor]] = None) -> dict:
+    """The per-shape table's tuning for this shape, sources (as for mk_dispatch_gemm_workspace_bytes) and arrival
+    chunking."""
     shape = _shape(T, d, E, k, e_begin, E_local, N)
-    ptrs = (_vp * max(S, 1))(*([0x1000] * max(S, 1)))
-    src = MkSources(S, T // max(S, 1), ctypes.cast(ptrs, ctypes.POINTER(_vp)), int(chunk_rows),
-                    ctypes.c_void_p(0x1000) if chunk_rows else None, 0, None, None)
+    src, _ptrs = _placeholder_sources(T, d, S, chunk_rows, xs)
     out = MkTuning()
     _check(load().mk_select_tuning(ctypes.byref(shape), ctypes.byref(src), ctypes.byref(out)), "mk_select_tuning")
     return {f: getattr(out, f) for f in TUNING_INTS}

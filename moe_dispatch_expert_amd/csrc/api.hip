@@ -93,18 +93,30 @@ int ticks_per_us()
     return v;
 }
 
-// The per-shape table.  One resident source (S = 1, no arrival flags): no mover role, the GEMM gathers
-// token rows straight from x through row_token (n_mover_wg = 0 in the table's answer); the x
-// matrix must fit one buffer resource (< 4 GiB).  Several sources, resident or arriving from peers:
-// every co-resident workgroup starts as a mover, then computes (on the one-GPU share of a wide EP
-// layer, 8 sources x 2048 rows, d = 7168, 32 local experts, rows arriving in 128-row chunks at
-// U[0, 100] us, the launch took 0.78 / 0.77 / 0.76 / 0.75 ms with 32 / 64 / 128 / 256 movers: every
-// expert tile holds rows of most chunks, so no tile is complete much before the last arrival, and
-// more movers finish the copy sooner).
-bool gather_possible(const mk_shape *s, const mk_sources *src)
+// Where the GEMM can read token rows in place (no mover role): at most kGatherSources sources, all
+// inside one buffer resource (< 4 GiB from the lowest one).  *lo and *span receive that window.
+bool gather_window(const mk_shape *s, const mk_sources *src, uintptr_t *lo = nullptr, uint64_t *span = nullptr)
 {
-    return src && src->S == 1 && src->chunk_rows == 0 && (size_t)s->T * s->d * 2 <= 0xFFFFFFF0ull;
+    if (!src || src->S < 1 || src->S > kGatherSources) return false;
+    const uint64_t bytes = (uint64_t)src->rows_per_src * s->d * 2;
+    uintptr_t l = (uintptr_t)src->x[0], h = l + bytes;
+    for (int i = 1; i < src->S; ++i) {
+        l = std::min(l, (uintptr_t)src->x[i]);
+        h = std::max(h, (uintptr_t)src->x[i] + (uintptr_t)bytes);
+    }
+    if (lo) *lo = l;
+    if (span) *span = (uint64_t)(h - l);
+    return (uint64_t)(h - l) <= kPastResource;
 }
+
+// The per-shape table.  Rows readable in place (gather_window): no mover role, the GEMM reads each
+// tile's token rows straight from the sources through the slot -> token map (MK_MOVERS_NONE), and
+// when rows arrive from peers each tile first waits for its rows' chunk flags.  (On the one-GPU share
+// of a wide EP layer, 8 sources x 2048 rows, d = 7168, 32 local experts, rows arriving in 128-row
+// chunks at U[0, 100] us, moving the rows first took 0.78 / 0.77 / 0.76 / 0.75 ms with 32 / 64 / 128 /
+// 256 movers: every expert tile holds rows of most chunks, so no tile is complete much before the
+// last arrival.)  Otherwise every co-resident workgroup starts as a mover, then computes.
+bool gather_possible(const mk_shape *s, const mk_sources *src) { return gather_window(s, src); }
 
 // Compute workgroups of the in-place path: as many as the GEMM tasks a uniform routing gives (each
 // local expert ~ T k / E rows, in 256-row tiles, times the 256-column blocks of N), with a quarter
@@ -129,6 +141,7 @@ mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
     t.bm = 256;
     t.bn = 256;
     t.bk = Tiles<4>::M256::BK;
+    t.tile_order = MK_ORDER_EXPERT;
     if (gather_possible(s, src)) {
         t.n_mover_wg = MK_MOVERS_NONE;
         t.n_compute_wg = table_compute_wg(s);
@@ -157,11 +170,12 @@ mk_status plan_call(const mk_shape *s, const mk_sources *src, const mk_tuning *t
             (tune->bk && tune->bk != Tiles<4>::M256::BK))
             return MK_EUNSUPPORTED;
         if (tune->n_mover_wg < MK_MOVERS_NONE || tune->n_compute_wg < 0 || tune->cooperative < 0 ||
-            tune->cooperative > 1)
+            tune->cooperative > 1 || tune->tile_order < 0 || tune->tile_order > MK_ORDER_TAILS_LAST)
             return MK_EINVAL;
         if (tune->n_mover_wg) p.tu.n_mover_wg = tune->n_mover_wg;
         if (tune->n_compute_wg) p.tu.n_compute_wg = tune->n_compute_wg;
         p.tu.cooperative = tune->cooperative;
+        if (tune->tile_order) p.tu.tile_order = tune->tile_order;
     }
     // Phase 3 of the fused kernel keeps nblk * E_local block counts in LDS.
     const WsLayout L0 = ws_layout(s->T, s->d, s->E, s->k, s->E_local, false);
@@ -267,7 +281,14 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
         fa.ca.E_local = s->E_local;
         fa.ga.x_perm = x_perm;
         if (gather) {
-            fa.ga.x_tok = rows.p[0];
+            uintptr_t lo = 0;
+            uint64_t span = 0;
+            gather_window(s, src, &lo, &span);
+            fa.ga.x_tok = (const uint16_t *)lo;
+            fa.ga.x_bytes = span;
+            fa.ga.x_nsrc = src->S;
+            fa.ga.x_rows_per_src = rows.rows_per_src;
+            for (int i = 0; i < src->S; ++i) fa.ga.x_src_off[i] = (uint32_t)((uintptr_t)src->x[i] - lo);
             fa.ga.row_token = row_token_ws;
             fa.ga.T = s->T;
         }
@@ -326,6 +347,7 @@ mk_status dispatch_impl(const mk_shape *s, const mk_sources *src, const float *w
         if (G > kBarrierWGs) return MK_EUNSUPPORTED;
         const int grid = G + fa.has_sim;
         fa.gather = gather ? 1 : 0;
+        fa.tails_last = tu.tile_order == MK_ORDER_TAILS_LAST ? 1 : 0;
         fa.n_mover = gather ? 0 : (tu.n_mover_wg > G ? G : tu.n_mover_wg);
         fa.max_tiles = L.max_tiles;
         fa.ticks_per_us = (uint32_t)ticks_per_us();

@@ -60,8 +60,10 @@ struct FusedArgs {
     uint64_t spin_limit;
     int32_t T, d, E, k, e_begin, E_local, nblk, bm;
     int32_t n_mover;             // workgroups that start as movers (0: gather mode)
-    int32_t gather;              // 1: no mover role; the GEMM reads token rows through row_token (one resident
-                                 // source), after a third grid barrier that publishes row_token
+    int32_t tails_last;          // 1: GEMM tasks of full row tiles first, the experts' short last tiles after
+    int32_t gather;              // 1: no mover role; the GEMM reads token rows in place (sources inside one
+                                 // buffer resource), each tile waiting for its rows' chunk flags if rows
+                                 // arrive from peers
     int32_t has_sim;             // last workgroup is the arrival simulator
     int32_t max_tiles;
     uint32_t ticks_per_us;       // wall-clock ticks per microsecond
@@ -418,6 +420,24 @@ __device__ __forceinline__ void fused_arrival_sim(const FusedArgs &a, char *lds)
     }
 }
 
+// The simulator's way into the GEMM role (in-place path): wait until barrier C of this call has passed
+// (the expert and tile offsets and row_token are then in memory), then load the offsets into LDS.
+__device__ __forceinline__ bool fused_join_layout(const FusedArgs &a, uint32_t call, int32_t *off, int32_t *toff)
+{
+    __shared__ int ok_sh;
+    if (threadIdx.x == 0)
+        ok_sh = wait_flag_eq(&a.hdr->bar_gen, barrier_target(call, 3), &a.hdr->err, 2 * a.spin_limit,
+                             0x08000000u) ? 1 : 0;
+    __syncthreads();
+    if (!ok_sh) return false;
+    for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
+        off[e] = a.offsets[e];
+        toff[e] = a.tile_off[e];
+    }
+    __syncthreads();
+    return true;
+}
+
 // st / ls: the four GEMM stage arrays (32 KiB each; ls holds their LDS-space
 // addresses for the GEMM), also used by the earlier phases; off, toff, uoff:
 // LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
@@ -431,13 +451,20 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     __syncthreads();
     trace_put(a, kTrStart, now_ticks());
     trace_put(a, kTrXcc, (uint64_t)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & 0xF));
+    const int G = fused_participants(a);
+    GemmArgs g = a.ga;
+    bool run_phases = true;
     if (a.has_sim && w == (int)gridDim.x - 1) {
         fused_arrival_sim(a, st[0]);   // the stage arrays are consecutive: 128 KiB
-        trace_put(a, kTrDone, now_ticks());
-        return;
+        // In the in-place path the simulator then joins the GEMM role, once barrier C has published the
+        // layout and the slot -> token map (taken whenever rows are simulated).
+        if (!a.gather || !fused_join_layout(a, call, off, toff)) {
+            trace_put(a, kTrDone, now_ticks());
+            return;
+        }
+        run_phases = false;
     }
-    const int G = fused_participants(a);
-
+    if (run_phases) {
     if (w == 0 && threadIdx.x < 8) a.xcd_next[threadIdx.x] = 0u;
     for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x) a.tile_cnt[i] = 0u;
 
@@ -460,6 +487,11 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         if (tasks <= 4 * G) {
             if (wave < 4 && w * 4 + wave < tasks)
                 router_task<kRtKC>(a.ra, w * 4 + wave, (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKC>::LDS_PER_WAVE);
+        } else if (a.E >= 2 * kRtExp) {   // two expert groups per task: two chains per lane
+            static_assert(C::NW * RtStage<kRtKCPair, 2>::LDS_PER_WAVE <= 4 * 32768, "router staging fits");
+            const int tasks2 = router_tasks(a.T, a.E, 2);
+            lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKCPair, 2>::LDS_PER_WAVE;
+            for (int q = w * C::NW + wave; q < tasks2; q += G * C::NW) router_task<kRtKCPair, 2>(a.ra, q, rlds);
         } else {
             lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKCFused>::LDS_PER_WAVE;
             for (int q = w * C::NW + wave; q < tasks; q += G * C::NW) router_task<kRtKCFused>(a.ra, q, rlds);
@@ -546,10 +578,9 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     // scanned (the stage arrays that hold them now are reused by the GEMM) and finds the tokens of its
     // tiles from them and the block masks; otherwise it reads row_token after a barrier that publishes
     // every workgroup's slots.
-    GemmArgs g = a.ga;
     if (a.gather) {
         const int nb = a.nblk * a.E_local;
-        if (nb <= kBaseTab) {
+        if (nb <= kBaseTab && !a.has_sim) {
             for (int i = threadIdx.x; i < nb; i += blockDim.x) basetab[i] = cnt[i];
             __syncthreads();
             g.tok_mask = a.ca.blkmask;
@@ -612,6 +643,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     trace_put(a, kTrUnits, n_units);
     trace_put(a, kTrCopyTicks, copy_ticks);
     trace_put(a, kTrReleaseTicks, release_ticks);
+    }   // run_phases
     uint64_t n_done = 0, wait_ticks = 0;
 
     // ---- compute: per-XCD queues over chunks of CH consecutive tasks.  A SwiGLU tile covers BN / 2
@@ -640,38 +672,101 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         return -1;
     };
     // Task q -> expert, column block, row tile (consecutive tasks share a W tile).
+    // With tails_last the full row tiles of every expert come first and the experts' short last tiles
+    // after them: fpre[e] = full tiles of the experts before e (in uoff, which the movers are done with);
+    // the tails before e are then toff[e] - fpre[e].
+    int32_t *fpre = uoff;
+    if (a.tails_last) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int acc = 0;
+            for (int e = 0; e < a.E_local; ++e) {
+                fpre[e] = acc;
+                acc += (off[e + 1] - off[e]) / C::BM;
+            }
+            fpre[a.E_local] = acc;
+        }
+        __syncthreads();
+    }
     auto job_of = [&](int q) -> TileJob {
         TileJob t{0, 0, 0, 0};
         if (q < 0) return t;
-        int lo = 0, hi = a.E_local;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (toff[mid] * NB <= q) lo = mid; else hi = mid;
+        int e, row0, rows, nb;
+        if (!a.tails_last) {
+            int lo = 0, hi = a.E_local;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (toff[mid] * NB <= q) lo = mid; else hi = mid;
+            }
+            const int nt = toff[lo + 1] - toff[lo];
+            const int rem = q - toff[lo] * NB;
+            const int mt = rem % nt;
+            e = lo;
+            row0 = off[lo] + mt * C::BM;
+            rows = min(C::BM, off[lo + 1] - off[lo] - mt * C::BM);
+            nb = rem / nt;
+        } else if (q < fpre[a.E_local] * NB) {   // a full tile
+            int lo = 0, hi = a.E_local;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (fpre[mid] * NB <= q) lo = mid; else hi = mid;
+            }
+            const int nf = fpre[lo + 1] - fpre[lo];
+            const int rem = q - fpre[lo] * NB;
+            e = lo;
+            row0 = off[lo] + (rem % nf) * C::BM;
+            rows = C::BM;
+            nb = rem / nf;
+        } else {                                  // a tail: one per expert that has one
+            const int q2 = q - fpre[a.E_local] * NB;
+            int lo = 0, hi = a.E_local;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if ((toff[mid] - fpre[mid]) * NB <= q2) lo = mid; else hi = mid;
+            }
+            const int nf = fpre[lo + 1] - fpre[lo];
+            e = lo;
+            row0 = off[lo] + nf * C::BM;
+            rows = off[lo + 1] - row0;
+            nb = q2 - (toff[lo] - fpre[lo]) * NB;
         }
-        const int nt = toff[lo + 1] - toff[lo];
-        const int rem = q - toff[lo] * NB;
-        const int mt = rem % nt;
-        t.e = __builtin_amdgcn_readfirstlane(lo);
-        t.row0 = __builtin_amdgcn_readfirstlane(off[lo] + mt * C::BM);
-        t.rows_valid = __builtin_amdgcn_readfirstlane(min(C::BM, off[lo + 1] - off[lo] - mt * C::BM));
-        t.n0 = __builtin_amdgcn_readfirstlane((rem / nt) * BNO);
+        t.e = __builtin_amdgcn_readfirstlane(e);
+        t.row0 = __builtin_amdgcn_readfirstlane(row0);
+        t.rows_valid = __builtin_amdgcn_readfirstlane(rows);
+        t.n0 = __builtin_amdgcn_readfirstlane(nb * BNO);
         return t;
     };
     // Row tile t's arrival counter and the count of moved units that completes it.
     auto tile_counter = [&](const TileJob &t) { return a.tile_cnt + toff[t.e] + (t.row0 - off[t.e]) / C::BM; };
     auto tile_units = [&](const TileJob &t) { return (uint32_t)((t.rows_valid + kMoveRows - 1) / kMoveRows); };
-    // Blocking: wait until all rows of t are moved (false: give up, the error word is set).
+    // Blocking: wait until all rows of t are moved, or, rows read in place from peers, until their
+    // chunks have arrived (false: give up, the error word is set).
     auto wait = [&](const TileJob &t) -> bool {
         if (n_done == 0) trace_put(a, kTrFirstTask, now_ticks());
-        if (a.gather) return true;   // rows are read in place; row_token was published by barrier 3
+        if (a.gather && a.fl.chunk_rows == 0) return true;   // rows read in place, all resident
         const uint64_t tw0 = now_ticks();
-        if (threadIdx.x == 0)
-            // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
-            q_sh = wait_flag_geq(tile_counter(t), tile_units(t), &a.hdr->err, 2 * a.spin_limit,
-                                 0x10000000u | (uint32_t)(tile_counter(t) - a.tile_cnt)) ? 1 : 0;
-        __syncthreads();
-        const int ok = __builtin_amdgcn_readfirstlane(q_sh);
-        __syncthreads();
+        int ok;
+        if (a.gather) {
+            // thread i waits for the ready flag of the source chunk of the tile's row i
+            int fail = 0;
+            const int i = threadIdx.x;
+            if (i < t.rows_valid) {
+                const int tok = g.tok_base ? token_of_rank(g, t.e, t.row0 - off[t.e] + i) : g.row_token[t.row0 + i];
+                const int sh = tok / a.src.rows_per_src;
+                const int c = sh * a.fl.chunks_per_src + (tok - sh * a.src.rows_per_src) / a.fl.chunk_rows;
+                fail = wait_flag_eq(a.fl.ready + c, a.fl.epoch, &a.hdr->err, a.spin_limit,
+                                    0x20000000u | (uint32_t)c) ? 0 : 1;
+            }
+            ok = __syncthreads_or(fail) ? 0 : 1;
+        } else {
+            if (threadIdx.x == 0)
+                // twice the movers' bound: a withheld arrival is reported as itself, not as this wait
+                q_sh = wait_flag_geq(tile_counter(t), tile_units(t), &a.hdr->err, 2 * a.spin_limit,
+                                     0x10000000u | (uint32_t)(tile_counter(t) - a.tile_cnt)) ? 1 : 0;
+            __syncthreads();
+            ok = __builtin_amdgcn_readfirstlane(q_sh);
+            __syncthreads();
+        }
         wait_ticks += now_ticks() - tw0;
         return ok != 0;
     };

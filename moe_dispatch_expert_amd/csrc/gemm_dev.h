@@ -55,9 +55,14 @@ __device__ __forceinline__ lds_char_t *stage_at(const LdsStages &ls, int k)
 
 struct GemmArgs {
     const uint16_t *x_perm;      // [x_perm_rows, d] expert-contiguous rows (row mode)
-    const uint16_t *x_tok;       // [T, d] token matrix (gather mode: row r is token row_token[r]), or nullptr
+    const uint16_t *x_tok;       // gather mode: the lowest source buffer (row r is token row_token[r]), or nullptr
     const int32_t *row_token;    // [R_cap] slot -> token (gather mode)
-    int32_t T;                   // rows of x_tok
+    int32_t T;                   // tokens
+    // Gather mode: token t = s * x_rows_per_src + r is row r of source s, at byte x_src_off[s] + r * d * 2
+    // from x_tok; the sources lie in the x_bytes (< 4 GiB) from x_tok.
+    int32_t x_nsrc, x_rows_per_src;
+    uint32_t x_src_off[kGatherSources];
+    uint64_t x_bytes;
     // Gather mode with the tokens derived in place of row_token (nullptr: read row_token): the
     // per-64-token-block expert masks [nblk, E_local], the per-block exclusive bases of every expert
     // (LDS, same layout) and the expert offsets (LDS).
@@ -430,10 +435,18 @@ __device__ __forceinline__ XOffsets<NW> x_offsets(const GemmArgs &a, const TileJ
         if (a.x_tok) {
             // Gather: row m of the tile is token row_token[row0 + m] of the token matrix; rows past the
             // tile's valid rows point past the end of the resource and read 0 without a memory access.
-            int tok = a.T;
-            if (t.rows_valid > 0 && m < t.rows_valid)
-                tok = a.tok_base ? token_of_rank(a, t.e, t.row0 - a.tok_off[t.e] + m) : a.row_token[t.row0 + m];
-            o.v[i] = (uint32_t)tok * row_bytes + ch;
+            uint32_t off = kPastResource;
+            if (t.rows_valid > 0 && m < t.rows_valid) {
+                const int tok = a.tok_base ? token_of_rank(a, t.e, t.row0 - a.tok_off[t.e] + m)
+                                           : a.row_token[t.row0 + m];
+                const int sh = a.x_nsrc > 1 ? tok / a.x_rows_per_src : 0;
+                uint32_t base = a.x_src_off[0];
+#pragma unroll
+                for (int k = 1; k < kGatherSources; ++k)
+                    if (sh == k) base = a.x_src_off[k];
+                off = base + (uint32_t)(tok - sh * a.x_rows_per_src) * row_bytes;
+            }
+            o.v[i] = off + ch;
         } else {
             o.v[i] = (uint32_t)m * row_bytes + ch;
         }
@@ -451,7 +464,7 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs &a, const TileJob &t)
     TileSrc s;
     const size_t w_first = (size_t)t.e * a.N + t.n0;
     s.w = make_rsrc4(a.w + w_first * a.d, ((size_t)a.E_local * a.N - w_first) * a.d * 2);
-    if (a.x_tok) s.x = make_rsrc4(a.x_tok, (size_t)a.T * a.d * 2);
+    if (a.x_tok) s.x = make_rsrc4(a.x_tok, a.x_bytes);
     // Row mode: only the tile's valid rows are readable: rows past a ragged end return 0 without a
     // memory access (they may belong to a tile that is not yet moved).
     else s.x = make_rsrc4(a.x_perm + (size_t)t.row0 * a.d, (size_t)t.rows_valid * a.d * 2);

@@ -8,6 +8,10 @@
 namespace mk {
 
 constexpr int kMaxSources = 64;     // source shards a call may name
+constexpr int kGatherSources = 8;   // sources the GEMM can read rows from in place
+// A buffer offset past every resource the kernels build (their sizes stay below it): loads read 0
+// without a memory access.
+constexpr uint32_t kPastResource = 0xFFFFFF00u;
 constexpr int kRouterSegments = 8;  // contiguous K segments of the router dot product
 constexpr int kMaxK = 32;           // experts per token this build handles
 constexpr int kTokBlock = 64;       // tokens per counting block (one wave, lane = token)

@@ -140,6 +140,13 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t code, uint32
         __hip_atomic_store(err + 1, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A store written through the XCD's L2 to memory (sc0 sc1), for data that workgroups on other XCDs
+// read after the next grid barrier: the barrier's release then has no dirty lines of it to write back.
+__device__ __forceinline__ void store_through(float *p, float v)
+{
+    asm volatile("global_store_dword %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void fence_acquire_agent()
 {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");

@@ -81,35 +81,39 @@ constexpr int kRtExp = 8;                     // experts per wave task
 
 // Staging geometry for KC K steps per chunk (128 in the router's own launch, 64 in the fused kernel,
 // whose eight waves share the GEMM's 128 KiB of stage arrays).
-template <int KC>
+template <int KC, int NG = 1>
 struct RtStage {
     static constexpr int WS = KC + 4;                 // LDS row stride of the staged weights (floats)
     static constexpr int XS = KC + 8;                 // LDS row stride of the staged x rows (bf16)
-    static constexpr int WBUF = kRtExp * WS * 4;      // bytes of one weight buffer
+    static constexpr int WBUF = kRtExp * WS * 4;      // bytes of one expert group's weight buffer
     static constexpr int XBUF = kRtTok * XS * 2;      // bytes of one x buffer
-    static constexpr int LDS_PER_WAVE = 2 * (WBUF + XBUF);
+    static constexpr int LDS_PER_WAVE = 2 * (NG * WBUF + XBUF);
 };
 constexpr int kRtKC = 128;                    // K steps per staged chunk of the router launch
 constexpr int kRtKCFused = 64;                // ... of the fused kernel
+constexpr int kRtKCPair = 32;                 // ... of the fused kernel, two expert groups per task
 constexpr int kRtLdsPerWave = RtStage<kRtKC>::LDS_PER_WAVE;
 
-__host__ __device__ inline int router_tasks(int T, int E)
+// NG expert groups per task: NG independent chains per lane (the matrix core issues the next
+// group's op while the previous one's result is pending: one dependent 4x4x1 chain waits ~48 cycles
+// per step, two interleaved chains ~22 per op, four ~13, measured on the part).
+__host__ __device__ inline int router_tasks(int T, int E, int NG = 1)
 {
-    return ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp) * kRouterSegments;
+    return ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp * NG - 1) / (kRtExp * NG)) * kRouterSegments;
 }
 
 typedef __attribute__((address_space(3))) float lds_float_t;
 typedef __attribute__((address_space(3))) char lds_byte_t;
 
-// FULL: the 8 columns exist and E % 4 == 0 (16-byte weight loads); otherwise
+// FULL: the 8 NG columns exist and E % 4 == 0 (16-byte weight loads); otherwise
 // one load per column, columns past E repeating the last (never stored).
-// lds: this wave's RtStage<KC>::LDS_PER_WAVE bytes.
-template <bool FULL, int KC>
+// lds: this wave's RtStage<KC, NG>::LDS_PER_WAVE bytes.
+template <bool FULL, int KC, int NG>
 __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int tb, int e0, lds_byte_t *lds)
 {
     constexpr int kRtKC = KC;
-    constexpr int kRtWS = RtStage<KC>::WS, kRtXS = RtStage<KC>::XS;
-    constexpr int kRtWBuf = RtStage<KC>::WBUF, kRtXBuf = RtStage<KC>::XBUF;
+    constexpr int kRtWS = RtStage<KC, NG>::WS, kRtXS = RtStage<KC, NG>::XS;
+    constexpr int kRtWBuf = RtStage<KC, NG>::WBUF, kRtXBuf = RtStage<KC, NG>::XBUF;
     typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
     typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
     const int lane = threadIdx.x % kWave;
@@ -124,14 +128,14 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
     for (int i = 0; i < XI; ++i)
         xrow[i] = token_row(a.src, min(tb * kRtTok + XR * i + lane / XP, a.T - 1), a.d) + (size_t)s * seg +
                   8 * (lane % XP);
-    // Weight staging: lane l loads rows (l / 2) + 32 i (i < KC / 32) of a chunk, columns 4 (l % 2) .. + 3.
-    const int c0 = min(4 * (lane & 1), a.E - 1 - e0);
-    const int clast = a.E - 1 - e0 - c0;
-    const float *wsrc = a.wr + (size_t)s * seg * a.E + e0 + c0;
+    // Weight staging: lane l loads rows (l / 2) + 32 i (i < KC / 32) of a chunk, columns 8 g + 4 (l % 2)
+    // .. + 3 of group g (columns past E: the last one again).
+    const int cl = 4 * (lane & 1);
+    const float *wseg = a.wr + (size_t)s * seg * a.E;
     constexpr int WI = kRtKC / 32;
     struct Regs {
         u32x4_t x[XI];
-        f32x4_t w[WI];
+        f32x4_t w[NG][WI];
     };
     // Chunk c into registers (past the end: the last chunk again; steps past the segment: clamped).
     auto fetch = [&](int c, Regs &r) {
@@ -139,26 +143,33 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
 #pragma unroll
         for (int i = 0; i < WI; ++i) {
             const int row = min(cc * kRtKC + (lane >> 1) + 32 * i, seg - 1);
-            const float *q = wsrc + (size_t)row * a.E;
-            if (FULL) {
-                r.w[i] = *(const f32x4_t *)q;
-            } else {
+            const float *q = wseg + (size_t)row * a.E;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) r.w[i][j] = q[min(j, clast)];
+            for (int g = 0; g < NG; ++g) {
+                const int col = e0 + 8 * g + cl;
+                if (FULL) {
+                    r.w[g][i] = *(const f32x4_t *)(q + col);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) r.w[g][i][j] = q[min(col + j, a.E - 1)];
+                }
             }
         }
         const int k0 = min(cc * kRtKC + 8 * (lane % XP), seg - 8) - 8 * (lane % XP);
 #pragma unroll
         for (int i = 0; i < XI; ++i) r.x[i] = *(const u32x4_t *)(xrow[i] + k0);
     };
-    auto wbuf = [&](int c) { return (lds_float_t *)(lds + (c & 1) * kRtWBuf); };
-    auto xbuf = [&](int c) { return lds + 2 * kRtWBuf + (c & 1) * kRtXBuf; };
+    auto wbuf = [&](int c, int g) { return (lds_float_t *)(lds + ((c & 1) * NG + g) * kRtWBuf); };
+    auto xbuf = [&](int c) { return lds + 2 * NG * kRtWBuf + (c & 1) * kRtXBuf; };
     auto stash = [&](const Regs &r, int c) {
-        lds_float_t *wb = wbuf(c);
 #pragma unroll
-        for (int i = 0; i < WI; ++i)
+        for (int g = 0; g < NG; ++g) {
+            lds_float_t *wb = wbuf(c, g);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wb[(4 * (lane & 1) + j) * kRtWS + (lane >> 1) + 32 * i] = r.w[i][j];
+            for (int i = 0; i < WI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wb[(4 * (lane & 1) + j) * kRtWS + (lane >> 1) + 32 * i] = r.w[g][i][j];
+        }
         lds_byte_t *xb = xbuf(c);
 #pragma unroll
         for (int i = 0; i < XI; ++i)
@@ -168,9 +179,10 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
     fetch(0, r);
     stash(r, 0);
     fetch(1, r);
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int c = 0; c < nch; ++c) {
-        const lds_float_t *wb = wbuf(c) + eb * kRtWS;
         const lds_byte_t *xb = xbuf(c) + (lane & 31) * kRtXS * 2;
         const int len = min(kRtKC, seg - c * kRtKC);   // a multiple of 16
 #pragma unroll
@@ -180,13 +192,18 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
                 const u32x4_t x1 = *(const lds_u32x4_t *)(xb + 32 * b + 16);
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    const f32x4_t w4 = *(const lds_f32x4_t *)(wb + 16 * b + 4 * h);
+                    f32x4_t w4[NG];
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        w4[g] = *(const lds_f32x4_t *)(wbuf(c, g) + eb * kRtWS + 16 * b + 4 * h);
                     const u32x4_t xw = h < 2 ? x0 : x1;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t word = xw[2 * (h & 1) + j / 2];
                         const float xf = __uint_as_float((j & 1) ? (word & 0xFFFF0000u) : (word << 16));
-                        acc = __builtin_amdgcn_mfma_f32_4x4x1f32(xf, w4[j], acc, 0, 0, 0);
+#pragma unroll
+                        for (int g = 0; g < NG; ++g)
+                            acc[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(xf, w4[g][j], acc[g], 0, 0, 0);
                     }
                 }
             }
@@ -197,26 +214,30 @@ __device__ __forceinline__ void router_task_body(const RouterArgs &a, int s, int
         stash(r, c + 1);
         fetch(c + 2, r);
     }
-    const int e = e0 + eb;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int t = tb * kRtTok + 4 * ((lane & 31) >> 2) + q;
-        if (t < a.T && e < a.E) a.part[((size_t)s * a.T + t) * a.E + e] = acc[q];
+    for (int g = 0; g < NG; ++g) {
+        const int e = e0 + 8 * g + eb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = tb * kRtTok + 4 * ((lane & 31) >> 2) + q;
+            if (t < a.T && e < a.E) store_through(a.part + ((size_t)s * a.T + t) * a.E + e, acc[g][q]);
+        }
     }
 }
 
 // Wave task q (< router_tasks(T, E)); q uniform over the wave.  Task numbers
 // run expert group fastest, so the waves of a workgroup share token rows.
-template <int KC = kRtKC>
+template <int KC = kRtKC, int NG = 1>
 __device__ __forceinline__ void router_task(const RouterArgs &a, int q, lds_byte_t *lds)
 {
-    const int neg = (a.E + kRtExp - 1) / kRtExp;
+    constexpr int GE = kRtExp * NG;   // experts per task
+    const int neg = (a.E + GE - 1) / GE;
     const int ntb = (a.T + kRtTok - 1) / kRtTok;
     const int eg = __builtin_amdgcn_readfirstlane(q % neg);
     const int tb = __builtin_amdgcn_readfirstlane((q / neg) % ntb);
     const int s = __builtin_amdgcn_readfirstlane(q / (neg * ntb));
-    if (a.E % 4 == 0 && eg * kRtExp + kRtExp <= a.E) router_task_body<true, KC>(a, s, tb, eg * kRtExp, lds);
-    else router_task_body<false, KC>(a, s, tb, eg * kRtExp, lds);
+    if (a.E % 4 == 0 && eg * GE + GE <= a.E) router_task_body<true, KC, NG>(a, s, tb, eg * GE, lds);
+    else router_task_body<false, KC, NG>(a, s, tb, eg * GE, lds);
 }
 
 struct TopkArgs {

@@ -20,12 +20,31 @@ def say(*a):
     print(*a, flush=True)
 
 
-def to_dev(inp: dict) -> dict:
+def source_views(x: torch.Tensor, S: int, reverse: bool = True) -> list:
+    """The S row shards of x as regions of one device receive buffer (one region per peer, a spare row
+    between regions; with reverse, source s sits in region S - 1 - s), so the sources are separate buffers
+    whose offsets differ from their token order."""
+    rows, d = x.shape[0] // S, x.shape[1]
+    recv = torch.empty(S * (rows + 1), d, dtype=x.dtype, device="cuda")
+    out = []
+    for s in range(S):
+        r = (S - 1 - s) if reverse else s
+        v = recv[r * (rows + 1):r * (rows + 1) + rows]
+        v.copy_(x[s * rows:(s + 1) * rows])
+        out.append(v)
+    return out
+
+
+def to_dev(inp: dict, separate: bool = False) -> dict:
+    """Device copies of the inputs; several sources as regions of one receive buffer (separate: one
+    allocation each)."""
     wl = inp["wl"]
     dev = {}
     x = inp["x"]
-    if wl.S > 1:
+    if wl.S > 1 and separate:
         dev["x"] = [x[s * wl.rows_per_src:(s + 1) * wl.rows_per_src].contiguous().cuda() for s in range(wl.S)]
+    elif wl.S > 1:
+        dev["x"] = source_views(x, wl.S)
     else:
         dev["x"] = x.cuda()
     dev["w_router"] = inp["w_router"].cuda()

@@ -46,8 +46,8 @@ int main(void) {
   printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", offsetof(mk_sources, S), offsetof(mk_sources, rows_per_src),
          offsetof(mk_sources, x), offsetof(mk_sources, chunk_rows), offsetof(mk_sources, chunk_ready),
          offsetof(mk_sources, epoch), offsetof(mk_sources, sim_delay_us), offsetof(mk_sources, sim_payload));
-  printf("%zu %zu %zu %zu\n", offsetof(mk_shape, N), offsetof(mk_tuning, bk), offsetof(mk_tuning, cooperative),
-         offsetof(mk_tuning, ev_gemm_end));
+  printf("%zu %zu %zu %zu %zu\n", offsetof(mk_shape, N), offsetof(mk_tuning, bk), offsetof(mk_tuning, cooperative),
+         offsetof(mk_tuning, tile_order), offsetof(mk_tuning, ev_gemm_end));
   return 0;
 }
 ''')
@@ -63,7 +63,7 @@ int main(void) {
     assert offs == [S.S.offset, S.rows_per_src.offset, S.x.offset, S.chunk_rows.offset, S.chunk_ready.offset,
                     S.epoch.offset, S.sim_delay_us.offset, S.sim_payload.offset]
     assert last == [mk.MkShape.N.offset, mk.MkTuning.bk.offset, mk.MkTuning.cooperative.offset,
-                    mk.MkTuning.ev_gemm_end.offset]
+                    mk.MkTuning.tile_order.offset, mk.MkTuning.ev_gemm_end.offset]
 
 
 def test_header_compiles_as_cxx(tmp_path):
@@ -97,30 +97,35 @@ def test_workspace_bytes_and_tuning_without_gpu():
                                                  tune={"n_mover_wg": mk.MK_MOVERS_STAGED})
     assert 0 < in_place < row_buffer                     # rows read in place: no row buffer
     assert moved == staged and moved - in_place >= row_buffer
-    # several sources or arrival flags: the table moves rows, so the row buffer is part of the default
-    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=2) >= moved
-    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=2, chunk_rows=128) >= moved
+    # up to 8 sources in one 4 GiB window, resident or arriving: rows read in place, no row buffer; more
+    # sources: the table moves rows, so the row buffer is part of the default
+    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=2) < row_buffer
+    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=8, chunk_rows=128) < row_buffer
+    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=16) >= moved
     assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 9, 0, 8, 14336) == 0   # k > E
     assert mk.mk_dispatch_gemm_workspace_bytes(16, 128, 8, 2, 4, 8, 64) == 0         # local range past E
-    # in place needs one resident source; staged launches cannot wait for arrival flags
-    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=2,
+    # in place needs at most 8 sources; staged launches cannot wait for arrival flags
+    assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=16,
                                                tune={"n_mover_wg": mk.MK_MOVERS_NONE}) == 0
     assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, S=2, chunk_rows=128,
                                                tune={"n_mover_wg": mk.MK_MOVERS_STAGED}) == 0
     # tile sizes other than the one built, negative counts and a bad cooperative flag are refused
-    for bad in ({"bm": 128}, {"bk": 32}, {"n_compute_wg": -1}, {"n_mover_wg": -3}, {"cooperative": 2}):
+    for bad in ({"bm": 128}, {"bk": 32}, {"n_compute_wg": -1}, {"n_mover_wg": -3}, {"cooperative": 2},
+                {"tile_order": 3}, {"tile_order": -1}):
         assert mk.mk_dispatch_gemm_workspace_bytes(4096, 4096, 8, 2, 0, 8, 14336, tune=bad) == 0, bad
     t = mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336)
     assert t["bm"] == 256 and t["bn"] == 256 and t["bk"] == 64 and t["n_mover_wg"] == mk.MK_MOVERS_NONE
-    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=8, chunk_rows=128)["n_mover_wg"] == 256
+    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=8, chunk_rows=128)["n_mover_wg"] == \
+        mk.MK_MOVERS_NONE
+    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=16, chunk_rows=128)["n_mover_wg"] == 256
     # compute workgroups keyed on the shape: the expected GEMM tasks plus a quarter, multiple of 8, >= 32;
     # 0 (all) once that reaches 256
     assert mk.mk_select_tuning(256, 512, 8, 2, 0, 8, 1024)["n_compute_wg"] == 40        # 32 tasks
     assert mk.mk_select_tuning(1024, 4096, 8, 2, 0, 8, 4096)["n_compute_wg"] == 160     # 128 tasks
     assert mk.mk_select_tuning(16, 512, 8, 2, 0, 8, 256)["n_compute_wg"] == 32          # 8 tasks: the floor
     assert mk.mk_select_tuning(128, 7168, 256, 8, 0, 32, 2048)["n_compute_wg"] == 0     # 256 tasks
-    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=8)["n_compute_wg"] == 0   # rows moved
-    assert mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336, S=2)["n_mover_wg"] > 0
+    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=16)["n_compute_wg"] == 0   # rows moved
+    assert mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336, S=16)["n_mover_wg"] > 0
     with pytest.raises(mk.MkError):
         mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14335)
 

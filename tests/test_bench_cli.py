@@ -30,3 +30,29 @@ def test_traffic_summaries_are_complete():
         # bytes = counters x calibration of a plain copy of known size
         want = d["fetch_kib_per_dispatch"] * d["fetch_scale"] + d["write_kib_per_dispatch"] * d["write_scale"]
         assert abs(d["bytes_per_launch"] - want) <= 1e-6 * want
+
+
+def test_trace_summary_reports_the_timed_window(tmp_path):
+    """--summarize-trace: every dispatch in the statistics table, and the average over the last K dispatches of
+    the dominant kernel (the timed steps) beside it, from rocprofv3's kernel-trace CSV columns."""
+    sys.path.insert(0, ROOT)
+    import bench
+    d = tmp_path / "kt"
+    d.mkdir()
+    (d / "run_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void mk::k_fused<X>(mk::FusedArgs)",5,5000,1000,99.0,500,1500,0\n')
+    durs = [1500, 1200, 900, 800, 600]   # the first call and a warm-up, then three timed steps
+    rows = ['"Kernel_Name","Start_Timestamp","End_Timestamp"']
+    t = 1000
+    for du in durs:
+        rows.append(f'"void mk::k_fused<X>(mk::FusedArgs)",{t},{t + du}')
+        rows.append(f'"other_kernel",{t + du + 10},{t + du + 20}')
+        t += 10000
+    (d / "run_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    out = tmp_path / "summary.md"
+    bench.summarize_trace(str(d), "tiny", "fused", 3, path=str(out))
+    text = out.read_text()
+    assert "| `void mk::k_fused<X>(mk::FusedArgs)` | 5 |" in text
+    assert "| 3 | 0.8 | " in text      # (900 + 800 + 600) / 3 ns = 0.77 us, printed to one decimal
+    assert "rocprofv3 --kernel-trace --stats" in text

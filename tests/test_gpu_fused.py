@@ -84,6 +84,33 @@ def test_grid_size_does_not_change_results(n_compute):
     _same(ref, out, KEYS + ("topk_w",))
 
 
+@pytest.mark.parametrize("name,changes,arrivals", [
+    ("mixtral", dict(T=1024, N=1024), False),
+    ("skewed", dict(T=2048, N=512), False),
+    ("wide_ep", dict(T=2048, d=1024, E=64, k=4, N=512, E_local=16, e_begin=16, chunk_rows=32), True),
+])
+def test_tile_order_does_not_change_results(name, changes, arrivals):
+    """The GEMM tasks in expert order or with the short last tiles after every full tile (rows read in place,
+    with arrivals for the wide-EP share, and moved by 64 movers) give the same bits."""
+    wl = W.scaled(W.WORKLOADS[name], **changes)
+    inp = W.make_inputs(wl, 23)
+    dev = to_dev(inp)
+    for movers in (0, 64):
+        outs = []
+        for order in (mk.MK_ORDER_EXPERT, mk.MK_ORDER_TAILS_LAST):
+            tune = {"tile_order": order, "n_mover_wg": movers}
+            if arrivals:
+                _, ref_ids, _ = oracle_route(inp)
+                delays = torch.randint(0, 50, (wl.S * (wl.rows_per_src // wl.chunk_rows),),
+                                       generator=torch.Generator().manual_seed(6)).to(torch.int32)
+                out, st, detail, _ = _ep_run(wl, inp, dev, torch.from_numpy(ref_ids).cuda(), delays=delays, tune=tune)
+                assert st == mk.MK_OK, (mk.mk_status_str(st), detail)
+            else:
+                out = _call(inp, dev, tune=tune)
+            outs.append(out)
+        _same(outs[0], outs[1], KEYS + ("topk_w",) if not arrivals else KEYS)
+
+
 def test_new_inputs_through_one_workspace():
     """A second call with different inputs through the same workspace must not see the first call's rows."""
     wl = W.scaled(W.WORKLOADS["skewed"], T=2048, N=512)
@@ -144,14 +171,33 @@ def test_arrival_flags_schedules_are_bit_identical():
                                         dtype=torch.int32),
     }
     for name, delays in schedules.items():
-        for n_mover in (8, 64):
+        for n_mover in (8, 64, mk.MK_MOVERS_NONE):   # movers, or tiles reading their rows in place
             out, st, detail, ready = _ep_run(wl, inp, dev, ids_in, delays=delays, tune={"n_mover_wg": n_mover})
             assert st == mk.MK_OK, (name, mk.mk_status_str(st), detail)
             assert (ready.cpu() == 1).all(), name
             _same(base, out)
 
 
-def test_poison_mode_reads_only_released_rows():
+def test_in_place_sources_equal_moved_rows():
+    """Sources as regions of one receive buffer (in reverse order): the table reads their rows in place; the
+    same inputs through separately allocated sources with every workgroup moving rows give the same bits."""
+    wl = _ep_small()
+    inp, dev, ids_in = _ep_inputs(wl, 44)
+    t = mk.mk_select_tuning(wl.T, wl.d, wl.E, wl.k, wl.e_begin, wl.E_local, wl.N, chunk_rows=wl.chunk_rows,
+                            xs=dev["x"])
+    assert t["n_mover_wg"] == mk.MK_MOVERS_NONE
+    in_place, st, _, _ = _ep_run(wl, inp, dev, ids_in, pre_release=True)
+    assert st == mk.MK_OK
+    moved, st, _, _ = _ep_run(wl, inp, to_dev(inp, separate=True), ids_in, pre_release=True,
+                              tune={"n_mover_wg": 256})
+    assert st == mk.MK_OK
+    _same(in_place, moved)
+
+
+@pytest.mark.parametrize("n_mover", [16, mk.MK_MOVERS_NONE])
+def test_poison_mode_reads_only_released_rows(n_mover):
+    """Every source row holds NaN until the simulator copies its chunk in and releases the flag: movers, or
+    GEMM tiles reading rows in place, must read only released rows."""
     wl = _ep_small()
     inp, dev, ids_in = _ep_inputs(wl, 41)
     base, st, _, _ = _ep_run(wl, inp, dev, ids_in, pre_release=True)
@@ -162,7 +208,7 @@ def test_poison_mode_reads_only_released_rows():
     g = torch.Generator().manual_seed(5)
     delays = torch.randint(0, 60, (wl.S * (wl.rows_per_src // wl.chunk_rows),), generator=g,
                            dtype=torch.int64).to(torch.int32)
-    out, st, detail, _ = _ep_run(wl, inp, dev, ids_in, delays=delays, payload=payload, tune={"n_mover_wg": 16})
+    out, st, detail, _ = _ep_run(wl, inp, dev, ids_in, delays=delays, payload=payload, tune={"n_mover_wg": n_mover})
     assert st == mk.MK_OK, (mk.mk_status_str(st), detail)
     R = int(out["expert_offsets"][-1])
     assert not torch.isnan(out["y_perm"][:R].float()).any()
@@ -184,9 +230,10 @@ def test_full_size_wide_ep_with_arrivals():
                    "wide_ep arrivals")
 
 
-def test_withheld_arrival_flag_times_out():
-    """One chunk is never released (no simulator, flag left at 0): the movers' bounded wait gives up,
-    the call reports MK_ETIMEOUT and the kernel exits."""
+@pytest.mark.parametrize("n_mover", [64, 0])
+def test_withheld_arrival_flag_times_out(n_mover):
+    """One chunk is never released (no simulator, flag left at 0): the movers' bounded wait (64 movers), or
+    the tiles' (the table: rows read in place), gives up, the call reports MK_ETIMEOUT and the kernel exits."""
     wl = _ep_small()
     inp, dev, ids_in = _ep_inputs(wl, 42)
     n_chunks = wl.S * (wl.rows_per_src // wl.chunk_rows)
@@ -196,7 +243,8 @@ def test_withheld_arrival_flag_times_out():
     os.environ["MK_TIMEOUT_US"] = "20000"
     try:
         out = mk.mk_dispatch_gemm(dev["x"], dev["w_experts"], wl.k, topk_ids_in=ids_in, E=wl.E,
-                                  e_begin=wl.e_begin, chunk_rows=wl.chunk_rows, chunk_ready=ready, epoch=1)
+                                  e_begin=wl.e_begin, chunk_rows=wl.chunk_rows, chunk_ready=ready, epoch=1,
+                                  tune={"n_mover_wg": n_mover})
         st, detail = mk.mk_poll_error(out["workspace"])
     finally:
         if old is None:

@@ -64,15 +64,15 @@ def test_static_scratch_matches_workspace_entry_point():
 
 
 def test_static_scratch_refuses_a_workspace_beyond_it():
-    """The wide expert-parallel share (8 sources, arrival flags) moves its rows into the expert-contiguous
-    buffer, about 1.9 GB: refused with MK_EWORKSPACE before any device work (no GPU needed)."""
+    """The wide expert-parallel share (8 sources, arrival flags) needs a workspace of about 134 MB (the router's
+    partial sums of 16384 tokens x 256 experts): refused with MK_EWORKSPACE before any device work (no GPU needed)."""
     lib = mk.load()
     wl = W.WORKLOADS["wide_ep"]
     assert mk.mk_dispatch_gemm_workspace_bytes(wl.T, wl.d, wl.E, wl.k, 0, wl.E_local, wl.N, S=wl.S,
                                                chunk_rows=wl.chunk_rows) > (32 << 20)
     fake = ctypes.c_void_p(0x100000)
     shape = mk.MkShape(wl.T, wl.d, wl.E, wl.k, 0, wl.E_local, wl.N)
-    xs = (ctypes.c_void_p * wl.S)(*([0x100000] * wl.S))
+    xs = (ctypes.c_void_p * wl.S)(*[0x100000 + i * wl.rows_per_src * wl.d * 2 for i in range(wl.S)])
     src = mk.MkSources(wl.S, wl.rows_per_src, ctypes.cast(xs, ctypes.POINTER(ctypes.c_void_p)), wl.chunk_rows,
                        fake, 1, None, None)
     rc = lib.mk_dispatch_gemm_static(ctypes.byref(shape), ctypes.byref(src), None, None, fake, fake, fake, fake,
