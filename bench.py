@@ -494,6 +494,13 @@ class Case:
                 "alg_bytes": alg_bytes}
 
 
+def _device_record(torch) -> dict:
+    """What the runtime reports about the GPU (the peaks above are the vendor's figures for MI355X)."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2 ** 30, 1)}
+
+
 def decode_record(seed: int, steps: int, warmup: int) -> dict:
     """Decode-shaped share (T=128, d=7168, 32 local of 256 experts, top-8, N=2048), routing inside the step:
     weight-streaming bound, so its roofline is HBM bytes (weights of the hit experts, x, router weights,
@@ -514,6 +521,7 @@ def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
     every workgroup first moving rows (the dispatch role), and all rows resident.  Overlap efficiency = (last arrival
     + the grouped GEMM alone on the same layout) / the fused launch: above 1 when the GEMM runs while rows
     are still arriving."""
+    import torch
     import workloads as W
     wl = W.WORKLOADS["wide_ep"]
     inp = W.make_inputs(wl, seed)
@@ -524,6 +532,9 @@ def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
     movers = Case(wl, seed, {"n_mover_wg": 256}, inp=inp).with_arrivals(delays)
     mm = movers.run(steps, warmup)
     del movers
+    at_zero = Case(wl, seed, {}, inp=inp).with_arrivals(torch.zeros_like(delays))
+    mz = at_zero.run(steps, warmup)
+    del at_zero
     resident = Case(wl, seed, {}, inp=inp)
     mr = resident.run(steps, warmup)
     del resident
@@ -542,6 +553,7 @@ def wide_ep_record(seed: int, steps: int, warmup: int) -> dict:
             "roofline": roof,
             "path": "the per-shape table's (tiles read their rows in place, each waiting for its rows' chunks)",
             "fused_movers_arrivals_launch_ms": round(float(np.mean(mm["launch_all"])), 4),
+            "fused_arrivals_all_at_0us_launch_ms": round(float(np.mean(mz["launch_all"])), 4),
             "fused_all_resident_launch_ms": round(float(np.mean(mr["launch_all"])), 4),
             "gemm_alone_launch_ms": round(gemm_ms, 4),
             "last_arrival_ms": round(arrival_ms, 4),
@@ -643,6 +655,7 @@ def main():
         "hbm_GBs_step_alg": m["alg_bytes"] / (ms_step * 1e-3) / 1e9,
         "roofline": roof,
         "torch": torch.__version__,
+        "device": _device_record(torch),
     }
     if args.staged or args.movers or args.compute_wg or args.tile_order:
         rec["config"]["path"] = ("staged" if args.staged else "fused") + (
