@@ -35,7 +35,8 @@ namespace mk {
 constexpr int kMoveRows = 32;          // rows per mover work unit
 constexpr int kScanHalf = 8192;       // ints per LDS array in phase 3
 constexpr int kMaxScanEntries = 2 * kScanHalf; // nblk * E_local held in LDS by phase 3
-constexpr int kBaseTab = 4096;        // nblk * E_local bases kept through the GEMM (in-place path, no 3rd barrier)
+constexpr int kBaseTab = 8192;        // nblk * E_local bases kept through the GEMM (in-place path, no 3rd barrier),
+                                      // as 16-bit ranks within an expert (T < 65536)
 
 struct FusedArgs {
     RouterArgs ra;
@@ -444,7 +445,7 @@ __device__ __forceinline__ bool fused_join_layout(const FusedArgs &a, uint32_t c
 template <class C, bool SW>
 __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t call, char *const (&st)[4],
                                                   const LdsStages &ls, int32_t *off, int32_t *toff, int32_t *uoff,
-                                                  int32_t *basetab)
+                                                  uint16_t *basetab)
 {
     const int w = blockIdx.x;
     if (w < kTraceWGs && (int)threadIdx.x < kTraceWords) a.trace[w * kTraceWords + threadIdx.x] = 0;   // this call's record only
@@ -580,8 +581,8 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     // every workgroup's slots.
     if (a.gather) {
         const int nb = a.nblk * a.E_local;
-        if (nb <= kBaseTab && !a.has_sim) {
-            for (int i = threadIdx.x; i < nb; i += blockDim.x) basetab[i] = cnt[i];
+        if (nb <= kBaseTab && a.T < 65536 && !a.has_sim) {
+            for (int i = threadIdx.x; i < nb; i += blockDim.x) basetab[i] = (uint16_t)cnt[i];
             __syncthreads();
             g.tok_mask = a.ca.blkmask;
             g.tok_base = basetab;

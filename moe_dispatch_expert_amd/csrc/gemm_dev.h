@@ -65,9 +65,9 @@ struct GemmArgs {
     uint64_t x_bytes;
     // Gather mode with the tokens derived in place of row_token (nullptr: read row_token): the
     // per-64-token-block expert masks [nblk, E_local], the per-block exclusive bases of every expert
-    // (LDS, same layout) and the expert offsets (LDS).
+    // (16-bit ranks within the expert, LDS, same layout) and the expert offsets (LDS).
     const uint64_t *tok_mask;
-    const int32_t *tok_base;
+    const uint16_t *tok_base;
     const int32_t *tok_off;
     int32_t tok_nblk;
     const uint16_t *w;           // [E_local, N, d]

@@ -78,7 +78,8 @@ template <class C, bool SW>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
-    __shared__ int32_t off[1025], toff[1025], uoff[1025], basetab[kBaseTab];
+    __shared__ int32_t off[1025], toff[1025], uoff[1025];
+    __shared__ uint16_t basetab[kBaseTab];
     LdsStages ls;
     char *st[4];   // filled one by one: a constant initializer would become a static one
     for (int k = 0; k < 4; ++k) {
