@@ -8,20 +8,24 @@
 // (compute, communication) with the count per role set per tensor shape.
 // Here, on one MI355X, a co-resident grid of workgroups runs:
 //   phase 1  router logits                                  (all workgroups)
-//   -- grid barrier --
+//   -- grid barrier A --
 //   phase 2  top-k, gate, per-64-token histogram + ranks    (all)
-//   -- grid barrier --
+//   -- grid barrier B --
 //   phase 3  offsets / per-block bases by an LDS scan in every workgroup,
 //            slot map and row map for the workgroup's own token blocks
-//   -- grid barrier --
-//   roles    movers: copy row chunks of each tile into the expert-contiguous
-//            buffer (waiting on source-chunk arrival flags when the rows come
-//            from peers), then bump the tile's arrival count (release);
-//            compute: take GEMM tasks from per-XCD queues, wait (acquire)
-//            until the tile's count is complete, run the tile;
-//            movers join the compute role when the dispatch work is done.
-//   arrival simulator (optional, one workgroup outside the barriers): stands
-//            in for the peers and releases source-chunk flags at given delays.
+//   (-- grid barrier C, only when the GEMM must read row_token: a block-base
+//            table too large for LDS, or rows from the arrival simulator --)
+//   rows     in place: the GEMM tiles read their token rows straight from the
+//            sources, each tile first waiting (acquire) for the ready flags of
+//            its rows' source chunks when rows arrive from peers; or movers
+//            copy row chunks of each tile into the expert-contiguous buffer
+//            (waiting on the chunk flags) and bump the tile's arrival count
+//            (release), then join the compute role;
+//   compute  take GEMM tasks from per-XCD queues, wait until the tile's rows are
+//            there, run the tile.
+//   arrival simulator (optional, the last workgroup, outside the barriers):
+//            stands in for the peers and releases source-chunk flags at given
+//            delays, then (in place) joins the compute role after barrier C.
 #pragma once
 
 #include "gemm_dev.h"

@@ -194,6 +194,28 @@ def test_in_place_sources_equal_moved_rows():
     _same(in_place, moved)
 
 
+def test_in_place_ragged_chunks_and_sources():
+    """Sources of 250 rows (not a multiple of the 64-token blocks) in 32-row chunks (the last chunk of each
+    source ragged), seeded arrivals: rows read in place give the bits of 64 movers and of all rows pre-released."""
+    wl = W.scaled(_ep_small(), T=2000)
+    inp, dev, ids_in = _ep_inputs(wl, 45)
+    assert wl.rows_per_src == 250
+    n_chunks = wl.S * (-(-wl.rows_per_src // wl.chunk_rows))
+    delays = torch.randint(0, 40, (n_chunks,), generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    ref, st, _, _ = _ep_run(wl, inp, dev, ids_in, pre_release=True)
+    assert st == mk.MK_OK
+    for movers in (mk.MK_MOVERS_NONE, 64):
+        out, st, detail, ready = _ep_run(wl, inp, dev, ids_in, delays=delays, tune={"n_mover_wg": movers})
+        assert st == mk.MK_OK, (movers, mk.mk_status_str(st), detail)
+        assert (ready.cpu() == 1).all()
+        _same(ref, out)
+    _, offsets, _, row_token = check_layout(ref, ids_in.cpu().numpy(), wl, "ragged ep")
+    rows = sample_rows(offsets, 32)
+    y_ref = oracle.expert_rows(inp["x"], inp["w_experts"], offsets, row_token, rows)
+    assert_y_close(ref["y_perm"][torch.from_numpy(rows.astype(np.int64)).cuda()].float().cpu().numpy(), y_ref,
+                   "ragged ep")
+
+
 @pytest.mark.parametrize("n_mover", [16, mk.MK_MOVERS_NONE])
 def test_poison_mode_reads_only_released_rows(n_mover):
     """Every source row holds NaN until the simulator copies its chunk in and releases the flag: movers, or
