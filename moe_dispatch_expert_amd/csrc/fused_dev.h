@@ -694,7 +694,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         __syncthreads();
     }
     auto job_of = [&](int q) -> TileJob {
-        TileJob t{0, 0, 0, 0};
+        TileJob t{0, 0, 0, 0, 0};
         if (q < 0) return t;
         int e, row0, rows, nb;
         if (!a.tails_last) {
@@ -739,6 +739,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         t.row0 = __builtin_amdgcn_readfirstlane(row0);
         t.rows_valid = __builtin_amdgcn_readfirstlane(rows);
         t.n0 = __builtin_amdgcn_readfirstlane(nb * BNO);
+        t.w_once = __builtin_amdgcn_readfirstlane(off[e + 1] - off[e] <= 64 ? 1 : 0);
         return t;
     };
     // Row tile t's arrival counter and the count of moved units that completes it.
