@@ -492,6 +492,12 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         if (tasks <= 4 * G) {
             if (wave < 4 && w * 4 + wave < tasks)
                 router_task<kRtKC>(a.ra, w * 4 + wave, (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKC>::LDS_PER_WAVE);
+        } else if (a.E >= 4 * kRtExp) {   // four expert groups per task: four chains per lane
+            // (skewed-shaped, 64 experts: routing 43 -> 36 us against two groups per task)
+            static_assert(C::NW * RtStage<kRtKCPair, 4>::LDS_PER_WAVE <= 4 * 32768, "router staging fits");
+            const int tasks4 = router_tasks(a.T, a.E, 4);
+            lds_byte_t *rlds = (lds_byte_t *)ls.p[0] + wave * RtStage<kRtKCPair, 4>::LDS_PER_WAVE;
+            for (int q = w * C::NW + wave; q < tasks4; q += G * C::NW) router_task<kRtKCPair, 4>(a.ra, q, rlds);
         } else if (a.E >= 2 * kRtExp) {   // two expert groups per task: two chains per lane
             static_assert(C::NW * RtStage<kRtKCPair, 2>::LDS_PER_WAVE <= 4 * 32768, "router staging fits");
             const int tasks2 = router_tasks(a.T, a.E, 2);

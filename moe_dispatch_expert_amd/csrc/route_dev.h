@@ -91,7 +91,7 @@ struct RtStage {
 };
 constexpr int kRtKC = 128;                    // K steps per staged chunk of the router launch
 constexpr int kRtKCFused = 64;                // ... of the fused kernel
-constexpr int kRtKCPair = 32;                 // ... of the fused kernel, two expert groups per task
+constexpr int kRtKCPair = 32;                 // ... of the fused kernel, two or four expert groups per task
 constexpr int kRtLdsPerWave = RtStage<kRtKC>::LDS_PER_WAVE;
 
 // NG expert groups per task: NG independent chains per lane (the matrix core issues the next

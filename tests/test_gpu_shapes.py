@@ -101,8 +101,10 @@ def test_k_depths(d):
 
 
 @pytest.mark.parametrize("E,E_local,e_begin,k,T", [(65, 65, 0, 1, 37), (100, 40, 30, 8, 130), (300, 16, 284, 5, 200),
-                                                  (1000, 24, 500, 8, 70)])
+                                                  (1000, 24, 500, 8, 70), (65, 65, 0, 2, 1500), (40, 40, 0, 3, 2100)])
 def test_wide_expert_counts(E, E_local, e_begin, k, T):
+    """Routing with E past one wave, groups of experts that end past E (router tasks of one, two or four
+    groups of 8 experts, by the task count), local ranges inside E; against the oracle, fused and staged."""
     wl = W.scaled(W.WORKLOADS["decode"], T=T, d=512, E=E, k=k, E_local=E_local, e_begin=e_begin, N=256)
     inp = W.make_inputs(wl, 14)
     out = _run(inp, to_dev(inp))
