@@ -106,7 +106,9 @@ __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t want,
     wait_vmem_all();   // every wave's stores of the phase have reached L2
     __syncthreads();
     __shared__ int ok_shared;
-    if (threadIdx.x == 0) st_release(a.bar_flag + blockIdx.x, want);
+    // (every value that crosses the barrier is written through to memory or by an atomic, and every
+    // wave has waited for its stores above, so the arrival needs no release write-back)
+    if (threadIdx.x == 0) st_relaxed(a.bar_flag + blockIdx.x, want);
     bool ok = true;
     if (blockIdx.x == 0) {
         const int G = fused_participants(a);
@@ -132,7 +134,7 @@ __device__ __forceinline__ bool fused_barrier(const FusedArgs &a, uint32_t want,
         }
         if (ok && threadIdx.x == 0) {
             fence_acquire_agent();
-            st_release(&a.hdr->bar_gen, want);
+            st_relaxed(&a.hdr->bar_gen, want);
         }
         __syncthreads();
         return ok;
@@ -470,15 +472,17 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         run_phases = false;
     }
     if (run_phases) {
-    if (w == 0 && threadIdx.x < 8) a.xcd_next[threadIdx.x] = 0u;
-    for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x) a.tile_cnt[i] = 0u;
+    // Counters and masks that other workgroups update with atomics: cleared through to memory.
+    if (w == 0 && threadIdx.x < 8) store_through(a.xcd_next + threadIdx.x, 0u);
+    for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x)
+        store_through(a.tile_cnt + i, 0u);
 
     // The token-per-wave selection builds the block masks with atomic ORs:
     // clear them before barrier A.
     const bool wave_topk = !a.ids_in;
     if (wave_topk)
         for (int i = w * (int)blockDim.x + threadIdx.x; i < a.nblk * a.E_local; i += G * (int)blockDim.x)
-            a.ca.blkmask[i] = 0ull;
+            store_through(a.ca.blkmask + i, 0ull);
 
     // ---- phase 1: router logits
     if (!a.ids_in) {
@@ -533,7 +537,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
                 const size_t o = (size_t)base_t * a.k + i;
                 const int32_t id = a.ids_in[o];
                 ids_lds[i] = id;
-                a.ta.ids[o] = id;
+                store_through(a.ta.ids + o, id);
                 if (a.ids_user) a.ids_user[o] = id;
             }
             __syncthreads();
@@ -552,12 +556,12 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     fused_scan(a, cnt, part, off, toff, uoff, wave_topk);
     if (w == 0) {
         for (int e = threadIdx.x; e <= a.E_local; e += blockDim.x) {
-            a.offsets[e] = off[e];
-            a.tile_off[e] = toff[e];
+            store_through(a.offsets + e, off[e]);
+            store_through(a.tile_off + e, toff[e]);
         }
         if (threadIdx.x == 0) {
-            a.hdr->R = (uint32_t)off[a.E_local];
-            a.hdr->n_tiles = (uint32_t)toff[a.E_local];
+            store_through(&a.hdr->R, (uint32_t)off[a.E_local]);
+            store_through(&a.hdr->n_tiles, (uint32_t)toff[a.E_local]);
         }
     }
     for (int blk = w; blk < a.nblk; blk += G) {
@@ -575,7 +579,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
             if (local && rank >= 0) {
                 slot = off[le] + cnt[blk * a.E_local + le] + rank;
                 if (slot < off[le + 1]) {
-                    a.row_token_ws[slot] = t;
+                    store_through(a.row_token_ws + slot, t);
                     if (a.row_token_user) a.row_token_user[slot] = t;
                 } else {
                     slot = -1;

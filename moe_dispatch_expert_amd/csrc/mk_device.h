@@ -119,9 +119,9 @@ __device__ __forceinline__ uint32_t ld_acquire(const uint32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_release(uint32_t *p, uint32_t v)
+__device__ __forceinline__ void st_relaxed(uint32_t *p, uint32_t v)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p)
 {
@@ -140,11 +140,23 @@ __device__ __forceinline__ void raise_error(uint32_t *err, uint32_t code, uint32
         __hip_atomic_store(err + 1, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A store written through the XCD's L2 to memory (sc0 sc1), for data that workgroups on other XCDs
-// read after the next grid barrier: the barrier's release then has no dirty lines of it to write back.
+// Stores written through the XCD's L2 to memory (sc0 sc1), for data that workgroups on other XCDs
+// read after the next grid barrier.  The fused kernel's grid barriers publish their arrivals without a
+// release fence (whose L2 write-back costs microseconds and slows every other workgroup's loads): every
+// value that crosses such a barrier is written this way or by an atomic, so it is in memory once the
+// writing wave's stores have completed (s_waitcnt vmcnt(0)).
 __device__ __forceinline__ void store_through(float *p, float v)
 {
     asm volatile("global_store_dword %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_through(uint32_t *p, uint32_t v)
+{
+    asm volatile("global_store_dword %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_through(int32_t *p, int32_t v) { store_through((uint32_t *)p, (uint32_t)v); }
+__device__ __forceinline__ void store_through(uint64_t *p, uint64_t v)
+{
+    asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ void fence_acquire_agent()

@@ -321,7 +321,7 @@ __device__ __forceinline__ void topk_select(const TopkArgs &a, int t, const Topk
     zsum = wave_sum_f32(zsum);
     if (l < a.k) {
         const size_t o = (size_t)t * a.k + l;
-        a.ids[o] = sel_id;
+        store_through(a.ids + o, sel_id);   // read by other workgroups after the next grid barrier
         if (a.ids_user) a.ids_user[o] = sel_id;
         if (a.w_user) a.w_user[o] = expf(sel_logit - top_logit) / zsum;
         // the token's bit in its block's mask of every local expert it chose
@@ -416,7 +416,7 @@ __device__ __forceinline__ void count_block(const CountArgs &a, int blk, const i
         }
         if (bad) {   // report the token, give none of its choices a slot
             raise_error(a.err, kErrInval, (uint32_t)t);
-            for (int j = 0; j < a.k; ++j) a.lrank[(size_t)t * a.k + j] = -1;
+            for (int j = 0; j < a.k; ++j) store_through(a.lrank + (size_t)t * a.k + j, -1);
             pend = 0;
         }
         for (;;) {
@@ -430,7 +430,7 @@ __device__ __forceinline__ void count_block(const CountArgs &a, int blk, const i
                 if (((pend >> j) & 1u) && ids_lds[l * a.k + j] == e) jj = j;
             const uint64_t m = __ballot(jj >= 0);
             if (jj >= 0) {
-                a.lrank[(size_t)t * a.k + jj] = __popcll(m & lanemask_lt());
+                store_through(a.lrank + (size_t)t * a.k + jj, (int32_t)__popcll(m & lanemask_lt()));
                 pend &= ~(1u << jj);
             }
             if (l == 0) {
@@ -441,8 +441,8 @@ __device__ __forceinline__ void count_block(const CountArgs &a, int blk, const i
     }
     __syncthreads();
     for (int e = threadIdx.x; e < a.E_local; e += blockDim.x) {
-        a.blkcnt[(size_t)blk * a.E_local + e] = cnt_lds[e];
-        a.blkmask[(size_t)blk * a.E_local + e] = mask_lds[e];
+        store_through(a.blkcnt + (size_t)blk * a.E_local + e, cnt_lds[e]);
+        store_through(a.blkmask + (size_t)blk * a.E_local + e, mask_lds[e]);
     }
     __syncthreads();
 }
