@@ -106,9 +106,11 @@ typedef struct {
  *   tile_order    order of the GEMM tasks (the fused path): MK_ORDER_EXPERT,
  *                 every expert's row tiles together (its short last tile
  *                 beside the full tiles that share its weights), or
- *                 MK_ORDER_TAILS_LAST, the full 256-row tiles of all experts
- *                 first and the experts' short last tiles after them (the last
- *                 round is then made of short tasks).  0: the table's.
+ *                 MK_ORDER_TAILS_LAST, every other row tile of all experts
+ *                 first and the experts' short last tiles (at most 64 rows)
+ *                 after them (the last round is then made of short tasks).
+ *                 0: the table's (tails last where a uniform routing gives
+ *                 at most three rounds of tasks on 256 workgroups).
  *   ev_gemm_begin / ev_gemm_end: NULL, or hipEvent_t handles the library
  *                 records on `stream` immediately before and after the launch
  *                 that runs the expert GEMM, so a caller can time that kernel. */

@@ -118,17 +118,23 @@ bool gather_window(const mk_shape *s, const mk_sources *src, uintptr_t *lo = nul
 // last arrival.)  Otherwise every co-resident workgroup starts as a mover, then computes.
 bool gather_possible(const mk_shape *s, const mk_sources *src) { return gather_window(s, src); }
 
-// Compute workgroups of the in-place path: as many as the GEMM tasks a uniform routing gives (each
-// local expert ~ T k / E rows, in 256-row tiles, times the 256-column blocks of N), with a quarter
+// GEMM tasks a uniform routing gives: each local expert ~ T k / E rows, in 256-row tiles, times the
+// 256-column blocks of N.
+// Compute workgroups of the in-place path: as many as those tasks, with a quarter
 // more for skew, at least 32, in multiples of 8 (one per XCD); 0 (every co-resident workgroup)
 // when that reaches 256.  Fewer workgroups make the grid barriers and the phases before the GEMM
 // cheaper when the GEMM cannot use the whole device: T = 256, d = 512, 8 experts, top-2, N = 1024
 // (32 tasks) took 0.034 ms on 32 or 64 workgroups, 0.040 on 128 and 0.060 on 256.
-int table_compute_wg(const mk_shape *s)
+long uniform_tasks(const mk_shape *s)
 {
     const double rows_e = (double)s->T * s->k / s->E;
     const long tiles_e = (long)((rows_e + 255.0) / 256.0);
-    const long tasks = (long)s->E_local * (tiles_e > 0 ? tiles_e : 1) * ((s->N + 255) / 256);
+    return (long)s->E_local * (tiles_e > 0 ? tiles_e : 1) * ((s->N + 255) / 256);
+}
+
+int table_compute_wg(const mk_shape *s)
+{
+    const long tasks = uniform_tasks(s);
     long g = (tasks * 5 + 3) / 4;
     g = (g + 7) / 8 * 8;
     if (g < 32) g = 32;
@@ -141,7 +147,12 @@ mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
     t.bm = 256;
     t.bn = 256;
     t.bk = Tiles<4>::M256::BK;
-    t.tile_order = MK_ORDER_EXPERT;
+    // Task order: with at most three rounds of tasks on the device's 256 workgroups, the experts' short
+    // last tiles go after every other tile, so that the longer tasks are spread evenly first (one GPU's
+    // share of a wide EP layer, 16384 x 8 of 256 experts, 32 local, d = 7168, N = 2048: two rounds plus
+    // 112 short tasks, 0.673 -> 0.645 ms).  Otherwise every expert's tiles together, each short tile
+    // beside the tiles that share its W tile (Mixtral-shaped, 7 rounds, and skewed, 4.5: 1-2% faster).
+    t.tile_order = uniform_tasks(s) <= 3 * 256 ? MK_ORDER_TAILS_LAST : MK_ORDER_EXPERT;
     if (gather_possible(s, src)) {
         t.n_mover_wg = MK_MOVERS_NONE;
         t.n_compute_wg = table_compute_wg(s);

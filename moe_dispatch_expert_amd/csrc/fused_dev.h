@@ -37,6 +37,7 @@
 namespace mk {
 
 constexpr int kMoveRows = 32;          // rows per mover work unit
+constexpr int kShortTile = 64;         // a last row tile of at most this many rows is short (tile order)
 constexpr int kScanHalf = 8192;       // ints per LDS array in phase 3
 constexpr int kMaxScanEntries = 2 * kScanHalf; // nblk * E_local held in LDS by phase 3
 constexpr int kBaseTab = 8192;        // nblk * E_local bases kept through the GEMM (in-place path, no 3rd barrier),
@@ -687,9 +688,9 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
         return -1;
     };
     // Task q -> expert, column block, row tile (consecutive tasks share a W tile).
-    // With tails_last the full row tiles of every expert come first and the experts' short last tiles
-    // after them: fpre[e] = full tiles of the experts before e (in uoff, which the movers are done with);
-    // the tails before e are then toff[e] - fpre[e].
+    // With tails_last every expert's row tiles but a short last one (at most kShortTile rows) come
+    // first, the short last tiles after them: fpre[e] = the other tiles of the experts before e (in
+    // uoff, which the movers are done with); the short tiles before e are then toff[e] - fpre[e].
     int32_t *fpre = uoff;
     if (a.tails_last) {
         __syncthreads();
@@ -697,7 +698,8 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
             int acc = 0;
             for (int e = 0; e < a.E_local; ++e) {
                 fpre[e] = acc;
-                acc += (off[e + 1] - off[e]) / C::BM;
+                const int c = off[e + 1] - off[e];
+                acc += c / C::BM + (c % C::BM > kShortTile ? 1 : 0);
             }
             fpre[a.E_local] = acc;
         }
@@ -730,7 +732,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
             const int rem = q - fpre[lo] * NB;
             e = lo;
             row0 = off[lo] + (rem % nf) * C::BM;
-            rows = C::BM;
+            rows = min(C::BM, off[lo + 1] - row0);
             nb = rem / nf;
         } else {                                  // a tail: one per expert that has one
             const int q2 = q - fpre[a.E_local] * NB;
