@@ -147,15 +147,17 @@ mk_tuning table_tuning(const mk_shape *s, const mk_sources *src)
     t.bm = 256;
     t.bn = 256;
     t.bk = Tiles<4>::M256::BK;
-    // Task order: with at most three rounds of tasks on the device's 256 workgroups, the experts' short
-    // last tiles go after every other tile, so that the longer tasks are spread evenly first (one GPU's
-    // share of a wide EP layer, 16384 x 8 of 256 experts, 32 local, d = 7168, N = 2048: two rounds plus
-    // 112 short tasks, 0.673 -> 0.645 ms).  Otherwise every expert's tiles together, each short tile
-    // beside the tiles that share its W tile (Mixtral-shaped, 7 rounds, and skewed, 4.5: 1-2% faster).
-    t.tile_order = uniform_tasks(s) <= 3 * 256 ? MK_ORDER_TAILS_LAST : MK_ORDER_EXPERT;
+    // Task order: rows read in place and at most three rounds of tasks on the device's 256 workgroups:
+    // the experts' short last tiles go after every other tile, so that the longer tasks are spread evenly
+    // first (one GPU's share of a wide EP layer, 16384 x 8 of 256 experts, 32 local, d = 7168, N = 2048:
+    // two rounds plus 112 short tasks, 0.673 -> 0.645 ms).  Otherwise every expert's tiles together, each
+    // short tile beside the tiles that share its W tile (Mixtral-shaped, 7 rounds, and skewed, 4.5: 1-2%
+    // faster; the same share with moved rows and arrivals: 0.742 against 0.785 ms with the short tiles last).
+    t.tile_order = MK_ORDER_EXPERT;
     if (gather_possible(s, src)) {
         t.n_mover_wg = MK_MOVERS_NONE;
         t.n_compute_wg = table_compute_wg(s);
+        if (uniform_tasks(s) <= 3 * 256) t.tile_order = MK_ORDER_TAILS_LAST;
     } else {
         t.n_mover_wg = 256;
         t.n_compute_wg = 0;   // 0: every co-resident workgroup
@@ -203,6 +205,8 @@ mk_status plan_call(const mk_shape *s, const mk_sources *src, const mk_tuning *t
     // the table's compute count is for the in-place path; on another path it means every workgroup
     p.table_compute = !(tune && tune->n_compute_wg);
     if (p.path != Path::kGather && p.table_compute) p.tu.n_compute_wg = 0;
+    // likewise the table's task order (tails last only where rows are read in place)
+    if (p.path != Path::kGather && !(tune && tune->tile_order)) p.tu.tile_order = MK_ORDER_EXPERT;
     p.L = ws_layout(s->T, s->d, s->E, s->k, s->E_local, p.path != Path::kGather);
     return MK_OK;
 }

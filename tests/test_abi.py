@@ -133,6 +133,8 @@ def test_workspace_bytes_and_tuning_without_gpu():
         mk.MK_ORDER_TAILS_LAST                                                              # 512 tasks
     assert mk.mk_select_tuning(4096, 4096, 8, 2, 0, 8, 14336)["tile_order"] == mk.MK_ORDER_EXPERT   # 1792
     assert mk.mk_select_tuning(8192, 2048, 64, 6, 0, 64, 1408)["tile_order"] == mk.MK_ORDER_EXPERT  # 1152
+    assert mk.mk_select_tuning(16384, 7168, 256, 8, 0, 32, 2048, S=16, chunk_rows=128)["tile_order"] == \
+        mk.MK_ORDER_EXPERT                                                                  # rows moved
 
 
 def test_next_steps_argument_errors_are_synchronous():
