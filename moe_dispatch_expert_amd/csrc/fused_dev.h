@@ -474,7 +474,8 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     }
     if (run_phases) {
     // Counters and masks that other workgroups update with atomics: cleared through to memory.
-    if (w == 0 && threadIdx.x < 8) store_through(a.xcd_next + threadIdx.x, 0u);
+    // (each XCD's counter starts past the tasks its own workgroups take first, without an atomic)
+    if (w == 0 && threadIdx.x < 8) store_through(a.xcd_next + threadIdx.x, (uint32_t)((G - (int)threadIdx.x + 7) / 8));
     for (int i = w * (int)blockDim.x + threadIdx.x; i < a.max_tiles; i += G * (int)blockDim.x)
         store_through(a.tile_cnt + i, 0u);
 
@@ -670,16 +671,22 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     const int xcd = w % 8;
     const int CH = (G + 7) / 8;
     __shared__ int q_sh;
-    // The next task index, walking this XCD's queue, then the others' (-1: none left).
+    // The next task index, walking this XCD's queue, then the others' (-1: none left).  A participating
+    // workgroup's first task is entry w / 8 of its own queue (the queue's w / 8-th workgroup); the queue
+    // counters start at the number of workgroups per XCD (the arrival simulator, not among them, claims
+    // through the counter).
     int o = 0;
+    bool first = w < G;
     auto claim = [&]() -> int {
         for (; o < 8; ++o) {
             const int x = (xcd + o) % 8;
             if (threadIdx.x == 0) {
-                const int i = (int)__hip_atomic_fetch_add(a.xcd_next + x, 1u, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
+                const int i = first ? w / 8
+                                    : (int)__hip_atomic_fetch_add(a.xcd_next + x, 1u, __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT);
                 q_sh = (i / CH) * 8 * CH + x * CH + (i % CH);
             }
+            first = false;
             __syncthreads();
             const int q = __builtin_amdgcn_readfirstlane(q_sh);   // uniform: keeps the tile loop scalar
             __syncthreads();
