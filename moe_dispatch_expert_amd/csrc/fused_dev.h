@@ -192,46 +192,111 @@ __device__ __forceinline__ void fused_scan(const FusedArgs &a, const ScanLds &cn
                            int32_t *uoff, bool from_masks)
 {
     const int n = a.nblk * a.E_local;
-    if (from_masks)
-        for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = __popcll(a.ca.blkmask[i]);
-    else
-        for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = a.ca.blkcnt[i];
+    // kScanBatch loads in flight per thread before the first LDS write (through the generic LDS
+    // pointers the compiler would otherwise wait for each load before the next one).
+    constexpr int kScanBatch = 16;
+    const int nt = (int)blockDim.x;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kScanBatch * nt) {
+        int32_t v[kScanBatch];
+        if (from_masks) {
+            uint64_t m[kScanBatch];
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) m[j] = i0 + j * nt < n ? a.ca.blkmask[i0 + j * nt] : 0ull;
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) v[j] = __popcll(m[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kScanBatch; ++j) v[j] = i0 + j * nt < n ? a.ca.blkcnt[i0 + j * nt] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j)
+            if (i0 + j * nt < n) cnt[i0 + j * nt] = v[j];
+    }
     __syncthreads();
-    // thread (e, p): blocks [p*L, (p+1)*L) of expert column e
+    // Thread (e, p): blocks [p*L, (p+1)*L) of expert column e (EC columns per pass).  The sums of the
+    // P chunks of a column are prefixed by Hillis-Steele rounds in LDS (log2 P barriers, not P - 1
+    // reads in a row).
     const int P = a.E_local >= (int)blockDim.x ? 1 : (int)blockDim.x / a.E_local;
     const int L = (a.nblk + P - 1) / P;
-    for (int base_e = 0; base_e < a.E_local; base_e += (int)blockDim.x / P) {
-        const int e = base_e + (int)threadIdx.x % ((int)blockDim.x / P);
-        const int p = (int)threadIdx.x / ((int)blockDim.x / P);
+    const int EC = (int)blockDim.x / P;
+    for (int base_e = 0; base_e < a.E_local; base_e += EC) {
+        const int col = (int)threadIdx.x % EC;
+        const int e = base_e + col;
+        const int p = (int)threadIdx.x / EC;
+        const bool mine = e < a.E_local && p < P;
         int32_t s = 0;
-        if (e < a.E_local && p < P)
+        if (mine)
             for (int b = p * L; b < min(a.nblk, (p + 1) * L); ++b) s += cnt[b * a.E_local + e];
+        __syncthreads();   // the previous pass is done with part
+        if (mine) part[p * EC + col] = s;
         __syncthreads();
-        if (e < a.E_local && p < P) part[p * ((int)blockDim.x / P) + ((int)threadIdx.x % ((int)blockDim.x / P))] = s;
-        __syncthreads();
-        if (e < a.E_local && p < P) {
-            int32_t run = 0;
-            const int col = (int)threadIdx.x % ((int)blockDim.x / P);
-            for (int q = 0; q < p; ++q) run += part[q * ((int)blockDim.x / P) + col];
+        int32_t incl = s;   // sum of chunks 0 .. p of the column
+        for (int dl = 1; dl < P; dl <<= 1) {
+            const int32_t add = mine && p >= dl ? part[(p - dl) * EC + col] : 0;
+            __syncthreads();
+            incl += add;
+            if (mine) part[p * EC + col] = incl;
+            __syncthreads();
+        }
+        if (mine) {
+            int32_t run = incl - s;
             for (int b = p * L; b < min(a.nblk, (p + 1) * L); ++b) {
                 const int32_t c = cnt[b * a.E_local + e];
                 cnt[b * a.E_local + e] = run;   // now the exclusive base of block b
                 run += c;
             }
-            if (p == P - 1) off[e + 1] = run;   // expert total (inclusive scan below)
+            if (p == P - 1) off[e + 1] = run;   // expert total (prefixed below)
         }
         __syncthreads();
+    }
+    // Expert offsets and the prefixes of row tiles and mover units (kMoveRows rows each) from the totals
+    // in off[1 .. E_local]: wave scans, then the waves' totals, a pass per blockDim experts.
+    int32_t *wsum = part;   // 3 ints per wave (the column partials are done with)
+    const int lane = (int)threadIdx.x % kWave, wv = (int)threadIdx.x / kWave, nwv = (int)blockDim.x / kWave;
+    int32_t carry_c = 0, carry_t = 0, carry_u = 0;
+    for (int e0 = 0; e0 < a.E_local; e0 += blockDim.x) {
+        const int e = e0 + (int)threadIdx.x;
+        const int32_t c = e < a.E_local ? off[e + 1] : 0;
+        int32_t sc = c, st = (c + a.bm - 1) / a.bm, su = (c + kMoveRows - 1) / kMoveRows;
+        for (int dl = 1; dl < kWave; dl <<= 1) {
+            const int32_t c2 = __shfl_up(sc, dl), t2 = __shfl_up(st, dl), u2 = __shfl_up(su, dl);
+            if (lane >= dl) {
+                sc += c2;
+                st += t2;
+                su += u2;
+            }
+        }
+        if (lane == kWave - 1) {
+            wsum[3 * wv] = sc;
+            wsum[3 * wv + 1] = st;
+            wsum[3 * wv + 2] = su;
+        }
+        __syncthreads();
+        int32_t pc = carry_c, pt = carry_t, pu = carry_u;
+        for (int v = 0; v < nwv; ++v) {
+            if (v == wv) {
+                sc += pc;
+                st += pt;
+                su += pu;
+            }
+            pc += wsum[3 * v];
+            pt += wsum[3 * v + 1];
+            pu += wsum[3 * v + 2];
+        }
+        if (e < a.E_local) {
+            off[e + 1] = sc;
+            toff[e + 1] = st;
+            uoff[e + 1] = su;
+        }
+        carry_c = pc;
+        carry_t = pt;
+        carry_u = pu;
+        __syncthreads();   // wsum is rewritten by the next pass
     }
     if (threadIdx.x == 0) {
         off[0] = 0;
         toff[0] = 0;
         uoff[0] = 0;
-        for (int e = 0; e < a.E_local; ++e) {
-            const int32_t c = off[e + 1];
-            off[e + 1] = off[e] + c;
-            toff[e + 1] = toff[e] + (c + a.bm - 1) / a.bm;
-            uoff[e + 1] = uoff[e] + (c + kMoveRows - 1) / kMoveRows;   // mover units of kMoveRows rows
-        }
     }
     __syncthreads();
 }
@@ -674,23 +739,43 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     // The next task index, walking this XCD's queue, then the others' (-1: none left).  A participating
     // workgroup's first task is entry w / 8 of its own queue (the queue's w / 8-th workgroup); the queue
     // counters start at the number of workgroups per XCD (the arrival simulator, not among them, claims
-    // through the counter).
+    // through the counter).  Once a queue comes up empty the workgroup reads all eight counters at once
+    // and takes entries only from queues that still hold tasks (a counter only grows, so a queue seen
+    // empty stays empty): one round trip instead of an atomic on every queue in turn.
+    auto entry_task = [&](int i, int x) { return (i / CH) * 8 * CH + x * CH + (i % CH); };
     int o = 0;
     bool first = w < G;
+    bool polled = false;
+    uint32_t live = 0xFFu;   // queues that may still hold tasks (uniform)
+    __shared__ uint32_t live_sh;
     auto claim = [&]() -> int {
         for (; o < 8; ++o) {
             const int x = (xcd + o) % 8;
+            if (!((live >> x) & 1u)) continue;
             if (threadIdx.x == 0) {
                 const int i = first ? w / 8
                                     : (int)__hip_atomic_fetch_add(a.xcd_next + x, 1u, __ATOMIC_RELAXED,
                                                                   __HIP_MEMORY_SCOPE_AGENT);
-                q_sh = (i / CH) * 8 * CH + x * CH + (i % CH);
+                q_sh = entry_task(i, x);
             }
             first = false;
             __syncthreads();
             const int q = __builtin_amdgcn_readfirstlane(q_sh);   // uniform: keeps the tile loop scalar
             __syncthreads();
             if (q < n_tasks) return q;
+            if (!polled) {
+                polled = true;
+                if (threadIdx.x < kWave) {   // wave 0: lane y reads queue y's counter
+                    bool has = false;
+                    if (threadIdx.x < 8)
+                        has = entry_task((int)ld_relaxed(a.xcd_next + threadIdx.x), (int)threadIdx.x) < n_tasks;
+                    const uint64_t b = __ballot(has);
+                    if (threadIdx.x == 0) live_sh = (uint32_t)b;
+                }
+                __syncthreads();
+                live = __builtin_amdgcn_readfirstlane(live_sh);
+                __syncthreads();
+            }
         }
         return -1;
     };

@@ -403,29 +403,24 @@ struct TileJob {
 
 // The lane's byte offsets of a tile's x rows: slot i covers tile row
 // (wave + NW i) * 8 + lane / 8 (the same rows for every tile height; a
-// shorter tile uses the first slots), plus its chunk.  Computed for the next task while the current one stores its
-// outputs, so the slot -> token reads of the gather mode are off the critical path.
+// shorter tile uses the first slots), plus its chunk.  Computed for the next task in the current one's
+// epilogue, between staging its outputs and storing them.
 template <int NW>
 struct XOffsets {
     uint32_t v[Tiles<NW>::M256::XS];
 };
 
-// The token of rank q among expert e's rows: the last block b whose base is <= q holds it (bases grow
-// by the block's count, so that block has more than q - base bits), at the (q - base)-th set bit of the
-// block's mask.
-__device__ __forceinline__ int token_of_rank(const GemmArgs &a, int e, int q)
+// The token tables of the in-place path (tok_base, tok_off) live in LDS: read them as LDS, not through
+// generic pointers (a generic load waits on both the LDS and the vector-memory counters).
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16_t;
+typedef __attribute__((address_space(3))) const int32_t lds_ci32_t;
+
+// Position of the j-th set bit of m (j < popcount(m)): halve the window each step.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int j)
 {
-    const int E = a.E_local;
-    int lo = 0, hi = a.tok_nblk;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (a.tok_base[mid * E + e] <= q) lo = mid; else hi = mid;
-    }
-    uint64_t m = a.tok_mask[(size_t)lo * E + e];
-    int j = q - a.tok_base[lo * E + e];
     int pos = 0;
 #pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) {   // select the j-th set bit: halve the window each step
+    for (int w = 32; w >= 1; w >>= 1) {
         const int c = __popcll(m & ((1ull << w) - 1ull));
         if (j >= c) {
             j -= c;
@@ -433,36 +428,98 @@ __device__ __forceinline__ int token_of_rank(const GemmArgs &a, int e, int q)
             pos += w;
         }
     }
-    return lo * 64 + pos;
+    return pos;
+}
+
+// The tokens of ranks q[0..n) among expert e's rows: the last block b whose base is <= q holds it (bases
+// grow by the block's count, so that block has more than q - base bits), at the (q - base)-th set bit of
+// the block's mask.  The n searches run side by side without branches (one LDS latency per halving step
+// for all of them) and the n mask loads are in flight together.  Lanes with valid[i] false get 0.
+template <int NQ>
+__device__ __forceinline__ void tokens_of_ranks(const GemmArgs &a, int e, const int (&q)[NQ], const bool (&valid)[NQ],
+                                                int (&tok)[NQ])
+{
+    const int E = a.E_local;
+    lds_cu16_t *base = (lds_cu16_t *)a.tok_base;
+    int lo[NQ], hi[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        lo[i] = 0;
+        hi[i] = a.tok_nblk;
+    }
+    for (int span = a.tok_nblk; span > 1; span = (span + 1) >> 1) {   // ceil(log2 nblk) halvings
+        int v[NQ], mid[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            mid[i] = (lo[i] + hi[i]) >> 1;   // lo when the window is down to one block
+            v[i] = base[mid[i] * E + e];
+        }
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const bool live = hi[i] - lo[i] > 1;
+            lo[i] = live && v[i] <= q[i] ? mid[i] : lo[i];
+            hi[i] = live && v[i] > q[i] ? mid[i] : hi[i];
+        }
+    }
+    uint64_t m[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) m[i] = valid[i] ? a.tok_mask[(size_t)lo[i] * E + e] : 0ull;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) tok[i] = valid[i] ? lo[i] * 64 + nth_set_bit(m[i], q[i] - base[lo[i] * E + e]) : 0;
+}
+
+__device__ __forceinline__ int token_of_rank(const GemmArgs &a, int e, int q)
+{
+    const int qs[1] = {q};
+    const bool valid[1] = {true};
+    int tok[1];
+    tokens_of_ranks<1>(a, e, qs, valid, tok);
+    return tok[0];
 }
 
 template <int NW>
 __device__ __forceinline__ XOffsets<NW> x_offsets(const GemmArgs &a, const TileJob &t, int wave, int lane)
 {
+    constexpr int XS = Tiles<NW>::M256::XS;
     XOffsets<NW> o;
     const uint32_t row_bytes = (uint32_t)a.d * 2;
     const uint32_t ch = dma_chunk_bytes(wave, lane);
+    int m[XS];
 #pragma unroll
-    for (int i = 0; i < Tiles<NW>::M256::XS; ++i) {
-        const int m = (wave + NW * i) * 8 + (lane >> 3);
-        if (a.x_tok) {
-            // Gather: row m of the tile is token row_token[row0 + m] of the token matrix; rows past the
-            // tile's valid rows point past the end of the resource and read 0 without a memory access.
-            uint32_t off = kPastResource;
-            if (t.rows_valid > 0 && m < t.rows_valid) {
-                const int tok = a.tok_base ? token_of_rank(a, t.e, t.row0 - a.tok_off[t.e] + m)
-                                           : a.row_token[t.row0 + m];
-                const int sh = a.x_nsrc > 1 ? tok / a.x_rows_per_src : 0;
-                uint32_t base = a.x_src_off[0];
+    for (int i = 0; i < XS; ++i) m[i] = (wave + NW * i) * 8 + (lane >> 3);
+    if (!a.x_tok) {
 #pragma unroll
-                for (int k = 1; k < kGatherSources; ++k)
-                    if (sh == k) base = a.x_src_off[k];
-                off = base + (uint32_t)(tok - sh * a.x_rows_per_src) * row_bytes;
-            }
-            o.v[i] = off + ch;
-        } else {
-            o.v[i] = (uint32_t)m * row_bytes + ch;
+        for (int i = 0; i < XS; ++i) o.v[i] = (uint32_t)m[i] * row_bytes + ch;
+        return o;
+    }
+    // Gather: row m of the tile is token row_token[row0 + m] of the token matrix; rows past the tile's
+    // valid rows point past the end of the resource and read 0 without a memory access.
+    bool valid[XS];
+    int tok[XS];
+#pragma unroll
+    for (int i = 0; i < XS; ++i) valid[i] = t.rows_valid > 0 && m[i] < t.rows_valid;
+    if (a.tok_base) {
+        const int r0 = t.row0 - ((lds_ci32_t *)a.tok_off)[t.e];   // rank of the tile's first row
+        int q[XS];
+#pragma unroll
+        for (int i = 0; i < XS; ++i) q[i] = r0 + m[i];
+        tokens_of_ranks<XS>(a, t.e, q, valid, tok);
+    } else {
+#pragma unroll
+        for (int i = 0; i < XS; ++i) tok[i] = valid[i] ? a.row_token[t.row0 + m[i]] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < XS; ++i) {
+        uint32_t off = kPastResource;
+        if (valid[i]) {
+            const int sh = a.x_nsrc > 1 ? tok[i] / a.x_rows_per_src : 0;
+            uint32_t base = a.x_src_off[0];
+#pragma unroll
+            for (int k = 1; k < kGatherSources; ++k)
+                if (sh == k) base = a.x_src_off[k];
+            off = base + (uint32_t)(tok[i] - sh * a.x_rows_per_src) * row_bytes;
         }
+        o.v[i] = off + ch;
     }
     return o;
 }

@@ -33,10 +33,16 @@ __device__ __forceinline__ void scan_block(const ScanArgs &a, int32_t *s_cnt, in
     const int e = threadIdx.x;
     int32_t cnt = 0;
     if (e < a.E_local) {
-        for (int b = 0; b < a.nblk; ++b) {
-            const size_t o = (size_t)b * a.E_local + e;
-            a.blkbase[o] = cnt;
-            cnt += a.blkcnt[o];
+        constexpr int kB = 16;   // loads in flight before the stores (which might alias them)
+        for (int b0 = 0; b0 < a.nblk; b0 += kB) {
+            int32_t c[kB];
+#pragma unroll
+            for (int j = 0; j < kB; ++j) c[j] = b0 + j < a.nblk ? a.blkcnt[(size_t)(b0 + j) * a.E_local + e] : 0;
+#pragma unroll
+            for (int j = 0; j < kB; ++j) {
+                if (b0 + j < a.nblk) a.blkbase[(size_t)(b0 + j) * a.E_local + e] = cnt;
+                cnt += c[j];
+            }
         }
     }
     const int32_t til = e < a.E_local ? (cnt + a.bm - 1) / a.bm : 0;
