@@ -180,6 +180,37 @@ __device__ __forceinline__ void fused_exit(const FusedArgs &a, uint32_t call)
 // expert offsets and tile prefix (LDS).  The nblk*E_local counts live in two
 // LDS arrays of kScanHalf ints (entry i in cnt0[i] or cnt1[i - kScanHalf]);
 // part: blockDim.x ints; off/toff/uoff: E_local+1 ints each.
+// Inclusive scan of NV values per thread over the workgroup's threads, in thread order: wave scans, then
+// the waves' totals (NV ints per wave in wsum, LDS).  tot gets the workgroup's totals.  Every thread of
+// the workgroup calls it (it holds two barriers).
+template <int NV>
+__device__ __forceinline__ void block_incl_scan(int32_t (&v)[NV], int32_t (&tot)[NV], int32_t *wsum)
+{
+    const int lane = (int)threadIdx.x % kWave, wv = (int)threadIdx.x / kWave, nwv = (int)blockDim.x / kWave;
+    for (int dl = 1; dl < kWave; dl <<= 1) {
+        int32_t u[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) u[j] = __shfl_up(v[j], dl);
+        if (lane >= dl)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) v[j] += u[j];
+    }
+    if (lane == kWave - 1)
+#pragma unroll
+        for (int j = 0; j < NV; ++j) wsum[NV * wv + j] = v[j];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) tot[j] = 0;
+    for (int u = 0; u < nwv; ++u) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            if (u == wv) v[j] += tot[j];
+            tot[j] += wsum[NV * u + j];
+        }
+    }
+    __syncthreads();   // wsum may be rewritten after this
+}
+
 struct ScanLds {
     int32_t *cnt0, *cnt1;
     __device__ __forceinline__ int32_t &operator[](int i) const
@@ -250,48 +281,20 @@ __device__ __forceinline__ void fused_scan(const FusedArgs &a, const ScanLds &cn
         __syncthreads();
     }
     // Expert offsets and the prefixes of row tiles and mover units (kMoveRows rows each) from the totals
-    // in off[1 .. E_local]: wave scans, then the waves' totals, a pass per blockDim experts.
-    int32_t *wsum = part;   // 3 ints per wave (the column partials are done with)
-    const int lane = (int)threadIdx.x % kWave, wv = (int)threadIdx.x / kWave, nwv = (int)blockDim.x / kWave;
-    int32_t carry_c = 0, carry_t = 0, carry_u = 0;
+    // in off[1 .. E_local], a pass per blockDim experts (part, done with, holds the waves' totals).
+    int32_t carry[3] = {0, 0, 0};
     for (int e0 = 0; e0 < a.E_local; e0 += blockDim.x) {
         const int e = e0 + (int)threadIdx.x;
         const int32_t c = e < a.E_local ? off[e + 1] : 0;
-        int32_t sc = c, st = (c + a.bm - 1) / a.bm, su = (c + kMoveRows - 1) / kMoveRows;
-        for (int dl = 1; dl < kWave; dl <<= 1) {
-            const int32_t c2 = __shfl_up(sc, dl), t2 = __shfl_up(st, dl), u2 = __shfl_up(su, dl);
-            if (lane >= dl) {
-                sc += c2;
-                st += t2;
-                su += u2;
-            }
-        }
-        if (lane == kWave - 1) {
-            wsum[3 * wv] = sc;
-            wsum[3 * wv + 1] = st;
-            wsum[3 * wv + 2] = su;
-        }
-        __syncthreads();
-        int32_t pc = carry_c, pt = carry_t, pu = carry_u;
-        for (int v = 0; v < nwv; ++v) {
-            if (v == wv) {
-                sc += pc;
-                st += pt;
-                su += pu;
-            }
-            pc += wsum[3 * v];
-            pt += wsum[3 * v + 1];
-            pu += wsum[3 * v + 2];
-        }
+        int32_t v[3] = {c, (c + a.bm - 1) / a.bm, (c + kMoveRows - 1) / kMoveRows}, tot[3];
+        block_incl_scan<3>(v, tot, part);
         if (e < a.E_local) {
-            off[e + 1] = sc;
-            toff[e + 1] = st;
-            uoff[e + 1] = su;
+            off[e + 1] = carry[0] + v[0];
+            toff[e + 1] = carry[1] + v[1];
+            uoff[e + 1] = carry[2] + v[2];
         }
-        carry_c = pc;
-        carry_t = pt;
-        carry_u = pu;
-        __syncthreads();   // wsum is rewritten by the next pass
+#pragma unroll
+        for (int j = 0; j < 3; ++j) carry[j] += tot[j];
     }
     if (threadIdx.x == 0) {
         off[0] = 0;
@@ -785,16 +788,19 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     // uoff, which the movers are done with); the short tiles before e are then toff[e] - fpre[e].
     int32_t *fpre = uoff;
     if (a.tails_last) {
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int acc = 0;
-            for (int e = 0; e < a.E_local; ++e) {
-                fpre[e] = acc;
-                const int c = off[e + 1] - off[e];
-                acc += c / C::BM + (c % C::BM > kShortTile ? 1 : 0);
-            }
-            fpre[a.E_local] = acc;
+        int32_t *wsum = (int32_t *)st[2];   // the scan's partials, done with
+        int32_t carry = 0;
+        __syncthreads();   // this workgroup is done with uoff (the movers' unit prefix)
+        for (int e0 = 0; e0 < a.E_local; e0 += blockDim.x) {
+            const int e = e0 + (int)threadIdx.x;
+            const int c = e < a.E_local ? off[e + 1] - off[e] : 0;
+            int32_t v[1] = {c / C::BM + (c % C::BM > kShortTile ? 1 : 0)}, tot[1];
+            const int32_t mine = v[0];
+            block_incl_scan<1>(v, tot, wsum);
+            if (e < a.E_local) fpre[e] = carry + v[0] - mine;
+            carry += tot[0];
         }
+        if (threadIdx.x == 0) fpre[a.E_local] = carry;
         __syncthreads();
     }
     auto job_of = [&](int q) -> TileJob {

@@ -371,7 +371,8 @@ __device__ __forceinline__ void topk_wave_units_nv(const TopkArgs &a, int u0, in
 
 __device__ __forceinline__ void topk_wave_loop(const TopkArgs &a, int u0, int stride)
 {
-    if (a.E <= 128) topk_wave_units_nv<2>(a, u0, stride);
+    if (a.E <= 64) topk_wave_units_nv<1>(a, u0, stride);
+    else if (a.E <= 128) topk_wave_units_nv<2>(a, u0, stride);
     else if (a.E <= 256) topk_wave_units_nv<4>(a, u0, stride);
     else if (a.E <= 512) topk_wave_units_nv<8>(a, u0, stride);
     else topk_wave_units_nv<16>(a, u0, stride);
