@@ -175,11 +175,6 @@ __device__ __forceinline__ void fused_exit(const FusedArgs &a, uint32_t call)
     }
 }
 
-// Phase 3 in one workgroup: per-block exclusive bases for every local expert
-// (into LDS and, for the blocks this workgroup owns, into the workspace),
-// expert offsets and tile prefix (LDS).  The nblk*E_local counts live in two
-// LDS arrays of kScanHalf ints (entry i in cnt0[i] or cnt1[i - kScanHalf]);
-// part: blockDim.x ints; off/toff/uoff: E_local+1 ints each.
 // Inclusive scan of NV values per thread over the workgroup's threads, in thread order: wave scans, then
 // the waves' totals (NV ints per wave in wsum, LDS).  tot gets the workgroup's totals.  Every thread of
 // the workgroup calls it (it holds two barriers).
@@ -211,6 +206,11 @@ __device__ __forceinline__ void block_incl_scan(int32_t (&v)[NV], int32_t (&tot)
     __syncthreads();   // wsum may be rewritten after this
 }
 
+// Phase 3 in one workgroup: per-block exclusive bases for every local expert
+// (into LDS and, for the blocks this workgroup owns, into the workspace),
+// expert offsets and tile prefix (LDS).  The nblk*E_local counts live in two
+// LDS arrays of kScanHalf ints (entry i in cnt0[i] or cnt1[i - kScanHalf]);
+// part: blockDim.x ints; off/toff/uoff: E_local+1 ints each.
 struct ScanLds {
     int32_t *cnt0, *cnt1;
     __device__ __forceinline__ int32_t &operator[](int i) const
@@ -517,7 +517,7 @@ __device__ __forceinline__ bool fused_join_layout(const FusedArgs &a, uint32_t c
 // st / ls: the four GEMM stage arrays (32 KiB each; ls holds their LDS-space
 // addresses for the GEMM), also used by the earlier phases; off, toff, uoff:
 // LDS arrays of at least E_local + 1 ints that outlive the GEMM tiles.
-template <class C, bool SW>
+template <class C, bool SW, bool HALF_N = false>
 __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t call, char *const (&st)[4],
                                                   const LdsStages &ls, int32_t *off, int32_t *toff, int32_t *uoff,
                                                   uint16_t *basetab)
@@ -889,7 +889,7 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     auto claim_job = [&]() { return job_of(claim()); };
     auto done = [&]() { ++n_done; };
     LambdaSched<decltype(claim_job), decltype(wait), decltype(done)> sc{claim_job, wait, done};
-    gemm_run<C::NW, SW>(g, sc, ls);
+    gemm_run<C::NW, SW, HALF_N>(g, sc, ls);
     trace_put(a, kTrDone, now_ticks());
     trace_put(a, kTrTasks, n_done);
     trace_put(a, kTrWaitTicks, wait_ticks);

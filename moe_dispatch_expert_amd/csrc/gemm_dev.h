@@ -277,7 +277,7 @@ template <class C>
 __device__ __forceinline__ void stage_tile(const f32x16_t (&acc)[C::NI][C::MI], const LdsStages &ls, int wave,
                                            int lane)
 {
-    static_assert(C::BN == 256 && C::BM <= 256, "an output row segment is 512 bytes; at most 4 x 64 rows");
+    static_assert(C::BN <= 256 && C::BM <= 256, "an output row segment is at most 512 bytes; at most 4 x 64 rows");
     const int wn = wave % C::WN, wm = wave / C::WN;
     // The swizzled offsets depend only on the lane; computed from an opaque copy of it here, so that the
     // compiler does not hoist dozens of them out of the tile loop and keep them live (spilled) throughout.
@@ -318,7 +318,7 @@ __device__ __forceinline__ void store_staged_tile(const GemmArgs &a, int row0, i
     constexpr int NS = RPW / 2, BATCH = NS < 8 ? NS : 8;
     static_assert(RPW % 2 == 0 && NS % BATCH == 0, "rows per wave");
     const int c = lane & 31;
-    const bool col_ok = n0 + c * 8 < a.N;   // N % 8 == 0: a chunk is wholly inside or outside
+    const bool col_ok = c * 8 < C::BN && n0 + c * 8 < a.N;   // N % 8 == 0: a chunk is wholly inside or outside
     // Rows past rows_valid fall outside the resource: those stores are dropped.  The stores are
     // non-temporal (no tile reads y back; skewed and wide-EP launches 1.5-2% shorter).
     const __amdgpu_buffer_rsrc_t ysrc = make_rsrc(a.y + (size_t)row0 * a.N + n0, (size_t)rows_valid * a.N * 2);
@@ -388,6 +388,7 @@ __device__ __forceinline__ void store_staged_swiglu(const GemmArgs &a, int row0,
 template <int NW>
 struct Tiles {
     typedef BigTile<256, 256, 2, NW> M256;
+    typedef BigTile<256, 128, 2, NW> M256H;   // a full row tile over the last 128 or fewer columns
     typedef BigTile<128, 256, 2, NW> M128;
     typedef BigTile<64, 256, 4, NW> M64;
     typedef BigTile<32, 256, NW == 8 ? 8 : 4, NW> M32;
@@ -796,8 +797,10 @@ struct LambdaSched {
 // The persistent tile loop.  Sched provides: claim() -> the next TileJob of
 // this workgroup (rows_valid <= 0: none left); wait(job) -> false if the
 // workgroup must stop (a failed wait for the job's rows); done() after each
-// tile.
-template <int NW, bool SW = false, class Sched>
+// tile.  HALF_N: the build with the half-width tile for a ragged last column
+// block (a kernel of its own, so that shapes with N % 256 == 0 keep the code
+// and register allocation of the build without it).
+template <int NW, bool SW = false, bool HALF_N = false, class Sched>
 __device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const LdsStages &ls)
 {
     typedef Tiles<NW> T;
@@ -809,7 +812,10 @@ __device__ __forceinline__ void gemm_run(const GemmArgs &a, Sched &sc, const Lds
         if (!sc.wait(job)) return;
         TileJob next;
         XOffsets<NW> xo_next;
-        if (job.rows_valid > 128) gemm_tile_big<typename T::M256, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        // The last column block of a ragged N (128 columns or fewer) runs half as many MFMAs.
+        if (HALF_N && !SW && job.rows_valid > 128 && a.N - job.n0 <= 128)
+            gemm_tile_big<typename T::M256H, SW>(a, job, xo, next, xo_next, sc, ls, so);
+        else if (job.rows_valid > 128) gemm_tile_big<typename T::M256, SW>(a, job, xo, next, xo_next, sc, ls, so);
         else if (job.rows_valid > 64) gemm_tile_big<typename T::M128, SW>(a, job, xo, next, xo_next, sc, ls, so);
         // A W tile that only this task reads streams non-temporally, so that it does not push the
         // token rows and the other tiles' W out of the L2 (decode: 0.221 -> 0.205 ms; with W tiles

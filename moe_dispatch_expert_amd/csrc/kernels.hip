@@ -74,7 +74,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm(GemmArgs a)
     gemm_worker<C, SW>(a, blockIdx.x, gridDim.x, ls);
 }
 
-template <class C, bool SW>
+template <class C, bool SW, bool HALF_N = false>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
 {
     __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
         ls.p[k] = (lds_char_t *)st[k];
     }
     const uint32_t call = fused_call_epoch(a);
-    fused_kernel_body<C, SW>(a, call, st, ls, off, toff, uoff, basetab);
+    fused_kernel_body<C, SW, HALF_N>(a, call, st, ls, off, toff, uoff, basetab);
     fused_exit(a, call);
 }
 
@@ -319,8 +319,11 @@ int gemm_max_grid(int bm, int bn)
 // guarantee co-residency instead.
 hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s)
 {
-    // a.ga.F > 0: the gate|up weights with the SwiGLU epilogue
-    const void *k = a.ga.F > 0 ? (const void *)k_fused<FusedTile, true> : (const void *)k_fused<FusedTile, false>;
+    // a.ga.F > 0: the gate|up weights with the SwiGLU epilogue; a ragged N (N % 256 != 0): the build whose
+    // last column block runs the half-width tile
+    const void *k = a.ga.F > 0          ? (const void *)k_fused<FusedTile, true>
+                    : a.ga.N % 256 != 0 ? (const void *)k_fused<FusedTile, false, true>
+                                        : (const void *)k_fused<FusedTile, false>;
     void *args[] = {(void *)&a};
     if (cooperative)   // the runtime guarantees co-residency (or refuses the launch)
         return hipLaunchCooperativeKernel(k, dim3(grid), dim3(FusedTile::THREADS), args, 0, s);
@@ -335,13 +338,15 @@ int fused_max_grid()
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev >= 0 && dev < kMaxDevices && cached[dev] > 0) return cached[dev];
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    int per_cu_sw = 0;   // both variants must fit (they share the workspace layout and the grid)
+    int per_cu_sw = 0, per_cu_half = 0;   // every variant must fit (they share the workspace layout and the grid)
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<FusedTile, false>,
                                                      FusedTile::THREADS, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_sw, (const void *)k_fused<FusedTile, true>,
+                                                     FusedTile::THREADS, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_half, (const void *)k_fused<FusedTile, false, true>,
                                                      FusedTile::THREADS, 0) != hipSuccess)
         return 0;
-    per_cu = std::min(per_cu, per_cu_sw);
+    per_cu = std::min(per_cu, std::min(per_cu_sw, per_cu_half));
     if (dev >= 0 && dev < kMaxDevices) cached[dev] = cus * per_cu;
     return cus * per_cu;
 }
