@@ -17,7 +17,7 @@ import moe_dispatch_expert_amd as mk
 import oracle
 import workloads as W
 from gpu_cases import (assert_w_close, assert_y_close, check_layout, full_check, oracle_route, sample_rows, say,
-                       to_dev)
+                       to_dev, Y_FLOOR, Y_REL)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,20 +137,45 @@ def test_tiny_every_row(seed):
 
 @pytest.mark.parametrize("name,n_random", [("mixtral", 24), ("skewed", 48), ("decode", 0)])
 def test_workload_sampled_rows(name, n_random):
+    """Full-size workloads: routing and layout bit-exact and sampled rows (decode: every row) against the oracle;
+    then every row against an fp32 GEMM of the same bf16 operands on the GPU (the rows' tokens are the ones whose
+    layout just matched the oracle), to the same bound."""
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, 0)
-    out = _run(inp, to_dev(inp))
+    dev = to_dev(inp)
+    out = _run(inp, dev)
     _, ids, _ = oracle_route(inp)
     _, offsets, _, _ = oracle.layout(ids, wl.e_begin, wl.E_local)
     rows = None if name == "decode" else sample_rows(offsets, n_random)
     r = full_check(inp, out, rows=rows, what=name)
     if name == "skewed":
         assert (r["count"] == 0).sum() >= 4
+    if name != "decode":
+        _every_row_vs_fp32_gemm(out, dev["x"], dev["w_experts"], offsets, wl, name)
+
+
+def _every_row_vs_fp32_gemm(out, x, w_experts, offsets, wl, what):
+    """Every routed row against an fp32 GEMM of the same bf16 operands on the GPU, to the oracle's bound (the
+    rows' tokens are row_token's, whose layout the caller has matched with the oracle)."""
+    torch.backends.cuda.matmul.allow_tf32 = False
+    rt = out["row_token"].long()
+    n_bad = 0
+    for e in range(wl.E_local):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b == a:
+            continue
+        ref = torch.matmul(x[rt[a:b]].float(), w_experts[e].float().t().contiguous())
+        got = out["y_perm"][a:b].float()
+        tol = torch.clamp(Y_REL * ref.abs(), min=Y_FLOOR)
+        n_bad += int(((got - ref).abs() > tol).sum())
+    say(f"{what}: every one of {int(offsets[-1])} rows x {wl.N} columns against the fp32 GEMM, {n_bad} out of bound")
+    assert n_bad == 0
 
 
 def test_wide_ep_share_with_source_routing():
     """One GPU's share: 8 source shards, routing done per shard by the sources (mk_route_topk),
-    ids handed to the dispatch call; local experts 0..31 of 256."""
+    ids handed to the dispatch call; local experts 0..31 of 256.  Sampled rows against the oracle, every row
+    against an fp32 GEMM."""
     wl = W.WORKLOADS["wide_ep"]
     inp = W.make_inputs(wl, 0)
     dev = to_dev(inp)
@@ -170,6 +195,7 @@ def test_wide_ep_share_with_source_routing():
     y_ref = oracle.expert_rows(inp["x"], inp["w_experts"], offsets, row_token, rows)
     y_gpu = out["y_perm"][torch.from_numpy(rows.astype(np.int64)).cuda()].float().cpu().numpy()
     assert_y_close(y_gpu, y_ref, "wide_ep")
+    _every_row_vs_fp32_gemm(out, torch.cat(dev["x"]), dev["w_experts"], offsets, wl, "wide_ep")
 
 
 @pytest.mark.parametrize("seed", [1, 2])
