@@ -181,7 +181,9 @@ size_t mk_dispatch_gemm_workspace_bytes(const mk_shape *s, const mk_sources *src
  * every call through it before that stops early (outputs undefined).  After
  * that it needs no re-zeroing: a failed call still ends its epoch, so barrier
  * state it left behind cannot satisfy a later call's barriers.
- * The fused kernel runs one workgroup per resident slot of the device and
+ * The fused kernel runs one workgroup per resident slot of the device (eight
+ * waves; four, one per SIMD, where T * k <= 32 * E, i.e. a uniform routing
+ * gives every expert at most 32 rows, N % 256 == 0 and no SwiGLU epilogue) and
  * synchronises them with grid barriers: they must all become resident, so
  * work of other streams on the device only delays it, and a wait longer than
  * the bound (MK_TIMEOUT_US microseconds, default 2000000) ends the call with

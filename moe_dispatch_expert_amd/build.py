@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build", "mk")
 LIB = os.path.join(HERE, "libmk.so")
-SOURCES = ["kernels.hip", "api.hip"]
+SOURCES = ["kernels.hip", "kernels_w4.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -6,6 +6,7 @@
 #include <algorithm>
 
 #include "fused_dev.h"
+#include "fused_kernel.h"
 #include "gemm_dev.h"
 #include "layout_dev.h"
 #include "mk_launch.h"
@@ -72,23 +73,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm(GemmArgs a)
     LdsStages ls;
     for (int k = 0; k < 4; ++k) ls.p[k] = (lds_char_t *)(stg + k * C::STAGE);
     gemm_worker<C, SW>(a, blockIdx.x, gridDim.x, ls);
-}
-
-template <class C, bool SW, bool HALF_N = false>
-__global__ __launch_bounds__(C::THREADS, 1) void k_fused(FusedArgs a)
-{
-    __shared__ __attribute__((aligned(1024))) char stg[4 * C::STAGE];   // the four stage arrays, consecutive
-    __shared__ int32_t off[1025], toff[1025], uoff[1025];
-    __shared__ uint16_t basetab[kBaseTab];
-    LdsStages ls;
-    char *st[4];   // filled one by one: a constant initializer would become a static one
-    for (int k = 0; k < 4; ++k) {
-        st[k] = stg + k * C::STAGE;
-        ls.p[k] = (lds_char_t *)st[k];
-    }
-    const uint32_t call = fused_call_epoch(a);
-    fused_kernel_body<C, SW, HALF_N>(a, call, st, ls, off, toff, uoff, basetab);
-    fused_exit(a, call);
 }
 
 // Combine: wave task q = (token q / nc, 512-column chunk q % nc); the lane owns
@@ -317,8 +301,10 @@ int gemm_max_grid(int bm, int bn)
 // other streams only delays the late ones, and a wait that outlasts the bound
 // ends the call with MK_ETIMEOUT.  A cooperative launch has the runtime
 // guarantee co-residency instead.
-hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s)
+hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, bool four_waves, hipStream_t s)
 {
+    // four_waves, with neither of the builds below: the four-wave build (kernels_w4.hip)
+    if (four_waves && a.ga.F == 0 && a.ga.N % 256 == 0) return launch_fused4(a, grid, cooperative, s);
     // a.ga.F > 0: the gate|up weights with the SwiGLU epilogue; a ragged N (N % 256 != 0): the build whose
     // last column block runs the half-width tile
     const void *k = a.ga.F > 0          ? (const void *)k_fused<FusedTile, true>
@@ -338,7 +324,7 @@ int fused_max_grid()
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev >= 0 && dev < kMaxDevices && cached[dev] > 0) return cached[dev];
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    int per_cu_sw = 0, per_cu_half = 0;   // every variant must fit (they share the workspace layout and the grid)
+    int per_cu_sw = 0, per_cu_half = 0;   // every build must fit (one workspace layout, one grid)
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_fused<FusedTile, false>,
                                                      FusedTile::THREADS, 0) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_sw, (const void *)k_fused<FusedTile, true>,
@@ -346,7 +332,8 @@ int fused_max_grid()
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_half, (const void *)k_fused<FusedTile, false, true>,
                                                      FusedTile::THREADS, 0) != hipSuccess)
         return 0;
-    per_cu = std::min(per_cu, std::min(per_cu_sw, per_cu_half));
+    const int per_cu_4 = fused4_per_cu();
+    per_cu = std::min(std::min(per_cu, per_cu_4), std::min(per_cu_sw, per_cu_half));
     if (dev >= 0 && dev < kMaxDevices) cached[dev] = cus * per_cu;
     return cus * per_cu;
 }

@@ -42,8 +42,11 @@ hipError_t launch_gemm_swiglu(const GemmArgs &a, int grid, hipStream_t s);
 int gemm_max_grid(int bm, int bn);
 // The persistent fused kernel: one workgroup per resident slot of the device (its grid barriers need them all
 // resident together).
-hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, hipStream_t s);
+hipError_t launch_fused(const FusedArgs &a, int grid, bool cooperative, bool four_waves, hipStream_t s);
 int fused_max_grid();
+// The four-wave build (kernels_w4.hip): its launch, and how many of its workgroups a CU holds.
+hipError_t launch_fused4(const FusedArgs &a, int grid, bool cooperative, hipStream_t s);
+int fused4_per_cu();
 // A staged call's status into status[2], then the error words cleared; a zero fill of bytes (% 16 == 0).
 hipError_t launch_status(WsHeader *hdr, int32_t *status, hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
