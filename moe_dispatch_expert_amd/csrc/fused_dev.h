@@ -752,6 +752,8 @@ __device__ __forceinline__ void fused_kernel_body(const FusedArgs &a, uint32_t c
     uint32_t live = 0xFFu;   // queues that may still hold tasks (uniform)
     __shared__ uint32_t live_sh;
     auto claim = [&]() -> int {
+        // At most one task per workgroup: every task is some workgroup's first, nothing is left to take.
+        if (!first && n_tasks <= G && !a.has_sim) return -1;
         for (; o < 8; ++o) {
             const int x = (xcd + o) % 8;
             if (!((live >> x) & 1u)) continue;
