@@ -9,6 +9,8 @@
 - Global expert counts above 64 that are not multiples of 64 (the
   token-per-wave selection with 2, 4, 8 and 16 keys per lane), k = 1 and the
   largest k.
+- The layout's LDS capacities: the block-base table and the scan arrays full,
+  and one block past each.
 """
 import numpy as np
 import pytest
@@ -118,3 +120,14 @@ def test_largest_k():
     inp = W.make_inputs(wl, 15)
     r = full_check(inp, _run(inp, to_dev(inp)), what="k=32")
     assert r["R"] == 70 * 32
+
+
+@pytest.mark.parametrize("T", [8192, 8256, 16384, 16448])
+def test_layout_capacity_boundaries(T):
+    """The fused kernel's layout at its LDS capacities (64 local experts, 64-token blocks): 8192 block bases,
+    the most the GEMM keeps in LDS (no third barrier); 8256, one block more (row_token after a third barrier);
+    16384, the most the scan holds; 16448, past it (the staged path takes over).  Every row against the oracle."""
+    wl = W.scaled(W.WORKLOADS["tiny"], T=T, d=128, E=64, k=2, E_local=64, N=64)
+    inp = W.make_inputs(wl, 16)
+    r = full_check(inp, _run(inp, to_dev(inp)), what=f"T={T}")
+    assert r["R"] == 2 * T
