@@ -35,7 +35,7 @@ typedef int32_t mk_status;
 enum {
     MK_OK = 0,
     MK_EINVAL = 1,        /* bad shape, null pointer, misalignment, k out of range */
-    MK_EUNSUPPORTED = 2,  /* legal shape this build does not handle (see each call) */
+    MK_EUNSUPPORTED = 2,  /* legal shape this library does not handle (see each call) */
     MK_EWORKSPACE = 3,    /* workspace missing or smaller than required */
     MK_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
     MK_ETIMEOUT = 5       /* a device-side wait exceeded its bound (mk_poll_error) */
@@ -95,7 +95,7 @@ typedef struct {
  *   n_compute_wg  > 0: workgroups that start in the GEMM role; the grid is then
  *                 n_compute_wg (+ n_mover_wg), and must fit the device at once
  *                 (else MK_EUNSUPPORTED).  0: every workgroup the device holds.
- *   bm, bn, bk    0 or the one tile this build has: 256 token rows, 256 output
+ *   bm, bn, bk    0 or the one tile this library has: 256 token rows, 256 output
  *                 columns, K slabs of 64 (the last row tile of each expert
  *                 shrinks to 128, 64 or 32 rows by itself); else MK_EUNSUPPORTED.
  *   cooperative   1: launch the persistent kernel cooperatively, so the runtime
